@@ -1,0 +1,454 @@
+"""Plain, slow float64 CPU oracle of the sparse MoE layer.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code
+with the HIP path (no kernels, headers, helpers or constants) and never imports
+the ``top_routing_expert_amd`` package.
+
+Every step is written out in NumPy float64 from its definition on the pages:
+
+  [MoE-Explained]  "Mixture of Experts Explained" (Hugging Face blog; the copy
+                   read is a Chinese translation).  Sections used: "What is
+                   sparsity?" (the weighted expert sum, softmax gating,
+                   KeepTopK, softmax over the kept logits), "Load balancing
+                   tokens for MoEs" (auxiliary loss), "MoEs and Transformers"
+                   (expert capacity, overflow through the residual), "Switch
+                   Transformers" (top-1 routing, the expert-capacity equation,
+                   capacity factor, full-precision router), "Stabilizing
+                   training with router Z-loss".
+  [Handbook-digest] digest of "The Ultimate MoE Training Handbook": section
+                   "what MoE saves" (64 experts / top-8 / width 1024 example)
+                   and "the three hard parts" (FP32 router because close
+                   scores flip; aux loss vs loss-free bias).
+  [Handbook-news]  news digest "Hugging Face releases a 30k-word free MoE
+                   training handbook", "confirmed" bullets: sigmoid and
+                   sqrt(softplus) scoring, routing scale near sqrt(k), the
+                   fixed-step bias update, shared experts.
+
+Where the pages leave a step open, the reading taken is stated at the function
+and listed in the design notes:
+  * expert capacity counts routed slots: C = ceil(CF * T * k / E); CF is an
+    fp32 value; CF <= 0 means no limit;
+  * within an expert, tokens are kept in ascending token order; a slot beyond
+    capacity is dropped on its own (the token keeps its other slots) and the
+    surviving gates are not renormalised; a dropped slot adds 0 to y (the
+    caller's residual carries the token);
+  * ties in the selection score go to the lower expert index; NaN ranks lowest;
+  * top-1 without renormalisation uses the raw softmax probability as gate;
+  * aux loss  L_aux = aux_coef * E * sum_e f_e * P_e with f_e = count_e/(T*k)
+    (pre-drop counts) and P_e = mean_t of the scores normalised over E;
+    z-loss    L_z = z_coef * mean_t (logsumexp_e z_te)^2 on the router logits
+    (including any logit offset);
+  * GELU is the exact erf form; expert linears have no biases;
+  * the loss-free bias update is b_e += gamma * sign(T*k/E - count_e).
+
+Array conventions (row-major): x [T,d]; Wg [d,E] (z = x Wg); W13 [E, n_up, d]
+(rows 0..F-1 gate, F..2F-1 up for SwiGLU; [E,F,d] for GELU); W2 [E,d,F];
+shared Ws13 [2Fs,d], Ws2 [d,Fs].
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+F64 = np.float64
+SCORES = ("softmax", "sigmoid", "sqrt_softplus")
+NEAR_TIE_REL = 1e-5
+
+__all__ = [
+    "capacity", "router_logits", "score", "select_topk", "near_tie_flags", "gates",
+    "logsumexp_rows", "router_losses", "route", "dispatch", "permute", "silu", "gelu",
+    "expert_ffn", "shared_expert", "combine", "bias_update", "layer_fwd", "layer_bwd",
+    "NEAR_TIE_REL",
+]
+
+
+# ---------------------------------------------------------------------------
+# Capacity
+# ---------------------------------------------------------------------------
+def capacity(T: int, E: int, k: int, capacity_factor: float):
+    """Expert capacity [MoE-Explained, "Switch Transformers", capacity equation].
+
+    The equation divides the tokens of a batch evenly over the experts and
+    scales by the capacity factor.  "Tokens" is read as the T*k routed slots
+    (equal to the printed form at k=1, where the equation is stated) and
+    rounded up.  The factor is an fp32 value.  Returns None for no limit.
+    """
+    cf = float(np.float32(capacity_factor))
+    if cf <= 0.0:
+        return None
+    return int(math.ceil(cf * T * k / E))
+
+
+# ---------------------------------------------------------------------------
+# Router
+# ---------------------------------------------------------------------------
+def router_logits(x, Wg, offset=None):
+    """z = x . W_g (+ per-expert offset) [MoE-Explained, "What is sparsity?",
+    softmax gating equation], in float64."""
+    z = np.asarray(x, F64) @ np.asarray(Wg, F64)
+    if offset is not None:
+        z = z + np.asarray(offset, F64)[None, :]
+    return z
+
+
+def score(z, kind: str):
+    """Router scoring function over the E logits of each token.
+
+    softmax: [MoE-Explained, "What is sparsity?"]; sigmoid and sqrt(softplus):
+    [Handbook-news, "confirmed" bullets on router scoring].
+    """
+    z = np.asarray(z, F64)
+    if kind == "softmax":
+        m = z.max(axis=1, keepdims=True)
+        e = np.exp(z - m)
+        return e / e.sum(axis=1, keepdims=True)
+    if kind == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-z))
+    if kind == "sqrt_softplus":
+        softplus = np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+        return np.sqrt(softplus)
+    raise ValueError(kind)
+
+
+def select_topk(sel, k: int):
+    """KeepTopK [MoE-Explained, "What is sparsity?", KeepTopK equation].
+
+    Returns idx [T,k]: the k largest selection scores per token in descending
+    order, ties to the lower expert index (a stable sort), NaN last.
+    """
+    sel = np.asarray(sel, F64)
+    order = np.argsort(-sel, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def near_tie_flags(sel, k: int, rel: float = NEAR_TIE_REL):
+    """Tokens whose selection could flip under sub-1e-5 relative rounding.
+
+    ``boundary``: the k-th and (k+1)-th largest selection scores differ by less
+    than ``rel`` * max(|a|,|b|) (the kept set is ambiguous).  ``order``: two
+    adjacent kept scores are that close (the slot order is ambiguous).
+    """
+    sel = np.asarray(sel, F64)
+    T, E = sel.shape
+    srt = -np.sort(-sel, axis=1)
+    def close(a, b):
+        return np.abs(a - b) < rel * np.maximum(np.abs(a), np.abs(b))
+    boundary = close(srt[:, k - 1], srt[:, k]) if k < E else np.zeros(T, bool)
+    order = np.zeros(T, bool)
+    for j in range(k - 1):
+        order |= close(srt[:, j], srt[:, j + 1])
+    return boundary, order
+
+
+def gates(s, idx, renorm: bool, gate_scale: float):
+    """Gates of the kept experts.
+
+    g_j = s[idx_j] (the selection bias is not part of the gate); renormalising
+    over the kept experts reproduces Softmax(KeepTopK(z)) for softmax scoring
+    [MoE-Explained, "What is sparsity?", last gating equation]; top-1 without
+    renormalisation keeps the raw probability [MoE-Explained, "Switch
+    Transformers"]; the result is multiplied by the routing scale
+    [Handbook-news, routing scale near sqrt(k)].
+    """
+    g = np.take_along_axis(np.asarray(s, F64), idx, axis=1)
+    if renorm:
+        g = g / g.sum(axis=1, keepdims=True)
+    return g * float(np.float32(gate_scale))
+
+
+def logsumexp_rows(z):
+    z = np.asarray(z, F64)
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
+def router_losses(z, s, counts, k: int, aux_coef: float, z_coef: float):
+    """Auxiliary load-balance loss and router z-loss.
+
+    [MoE-Explained, "Load balancing tokens for MoEs" and "Switch
+    Transformers"] name the load-balance loss that pushes experts toward equal
+    importance and equal token counts; [MoE-Explained, "Stabilizing training
+    with router Z-loss"] names the penalty on large logits.  Formulas (the
+    pages give none): L_aux = aux_coef * E * sum_e f_e P_e with f_e the
+    fraction of routed slots sent to e (pre-drop) and P_e the mean over tokens
+    of the scores normalised over E; L_z = z_coef * mean_t logsumexp(z_t)^2.
+    """
+    s = np.asarray(s, F64)
+    T, E = s.shape
+    p_hat = s / s.sum(axis=1, keepdims=True)
+    P = p_hat.mean(axis=0)
+    f = np.asarray(counts, F64) / (T * k)
+    aux = float(np.float32(aux_coef)) * E * float(np.sum(f * P))
+    lse = logsumexp_rows(z)
+    zl = float(np.float32(z_coef)) * float(np.mean(lse * lse))
+    return aux, zl
+
+
+def route(x, Wg, k, score_kind, renorm, gate_scale, offset=None, sel_bias=None,
+          aux_coef=0.0, z_coef=0.0):
+    """The FP32-router step of the layer in float64 [Handbook-digest, "the three
+    hard parts", 1: routing in full precision].  Returns a dict with z, s, sel,
+    idx [T,k], g [T,k], counts [E] (pre-drop), losses and near-tie flags."""
+    z = router_logits(x, Wg, offset)
+    s = score(z, score_kind)
+    sel = s + (np.asarray(sel_bias, F64)[None, :] if sel_bias is not None else 0.0)
+    idx = select_topk(sel, k)
+    g = gates(s, idx, renorm, gate_scale)
+    E = z.shape[1]
+    counts = np.bincount(idx.reshape(-1), minlength=E).astype(np.int64)
+    aux, zl = router_losses(z, s, counts, k, aux_coef, z_coef)
+    boundary, order = near_tie_flags(sel, k)
+    return dict(z=z, s=s, sel=sel, idx=idx, g=g, counts=counts, aux=aux, zloss=zl,
+                near_tie=boundary, near_tie_order=order)
+
+
+# ---------------------------------------------------------------------------
+# Dispatch: capacity, drop set, expert-contiguous permutation
+# ---------------------------------------------------------------------------
+def dispatch(idx, E: int, C):
+    """Group routed slots by expert [MoE-Explained, "MoEs and Transformers",
+    expert capacity and overflow].
+
+    counts_e = slots that chose e (pre-drop); each expert keeps its first C
+    slots in ascending token order; kept rows are laid out expert by expert:
+    row = offsets[e] + position, offsets = exclusive scan of min(counts, C).
+    Returns counts [E], offsets [E+1], row_of_slot [T,k] (-1 = dropped) and
+    token_of_row [T*k] (-1 past the last kept row).
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts = np.zeros(E, np.int64)
+    for e in range(E):
+        counts[e] = int(np.count_nonzero(idx == e))
+    kept = counts.copy() if C is None else np.minimum(counts, C)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(kept)
+    row_of_slot = np.full((T, k), -1, np.int64)
+    token_of_row = np.full(T * k, -1, np.int64)
+    for e in range(E):
+        ts, js = np.nonzero(idx == e)          # row-major: ascending token index
+        n = int(kept[e])
+        rows = offsets[e] + np.arange(n)
+        row_of_slot[ts[:n], js[:n]] = rows
+        token_of_row[rows] = ts[:n]
+    return counts, offsets, row_of_slot, token_of_row
+
+
+def permute(x, token_of_row, R: int):
+    """x_perm[r] = x[token_of_row[r]] for the R kept rows."""
+    return np.asarray(x, F64)[np.asarray(token_of_row[:R])]
+
+
+# ---------------------------------------------------------------------------
+# Experts
+# ---------------------------------------------------------------------------
+def silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def gelu(v):
+    """Exact (erf) GELU."""
+    return 0.5 * v * (1.0 + erf(v / math.sqrt(2.0)))
+
+
+def _ffn(X, W13e, W2e, act):
+    X = np.asarray(X, F64)
+    h = X @ np.asarray(W13e, F64).T
+    if act == "swiglu":
+        F = h.shape[1] // 2
+        a = silu(h[:, :F]) * h[:, F:]
+    elif act == "gelu":
+        a = gelu(h)
+    else:
+        raise ValueError(act)
+    return h, a, a @ np.asarray(W2e, F64).T
+
+
+def expert_ffn(x_perm, offsets, W13, W2, act: str, keep_hidden: bool = False):
+    """Each expert is an FFN [MoE-Explained, "What is MoE?": experts are FFNs]
+    applied to its contiguous rows: SwiGLU a = silu(x Wg^T) * (x Wu^T) or GELU
+    a = gelu(x W1^T); o = a W2^T.  Returns o [R,d] (and h, a if asked)."""
+    x_perm = np.asarray(x_perm, F64)
+    G = len(offsets) - 1
+    R = int(offsets[-1])
+    d = W2.shape[1]
+    o = np.zeros((R, d), F64)
+    hs, as_ = [], []
+    for e in range(G):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            hs.append(np.zeros((0, W13.shape[1]))); as_.append(np.zeros((0, W2.shape[2])))
+            continue
+        h, a, oe = _ffn(x_perm[r0:r1], W13[e], W2[e], act)
+        o[r0:r1] = oe
+        if keep_hidden:
+            hs.append(h); as_.append(a)
+    if keep_hidden:
+        return o, hs, as_
+    return o
+
+
+def shared_expert(x, Ws13, Ws2, keep_hidden: bool = False):
+    """Always-on SwiGLU expert applied to every token with gate 1
+    [Handbook-news, "confirmed" bullets on shared experts]."""
+    h, a, o = _ffn(x, Ws13, Ws2, "swiglu")
+    return (o, h, a) if keep_hidden else o
+
+
+def combine(o, row_of_slot, g, shared_out=None):
+    """y_t = sum over kept slots j of g_tj * E_idx(x_t) [MoE-Explained, "What is
+    sparsity?", the weighted expert sum]; experts not kept (gate 0, or dropped
+    over capacity) contribute nothing; plus the shared expert's output."""
+    o = np.asarray(o, F64)
+    T, k = row_of_slot.shape
+    y = np.zeros((T, o.shape[1]), F64)
+    for j in range(k):
+        kept = row_of_slot[:, j] >= 0
+        y[kept] += np.asarray(g, F64)[kept, j, None] * o[row_of_slot[kept, j]]
+    if shared_out is not None:
+        y += np.asarray(shared_out, F64)
+    return y
+
+
+def bias_update(counts, bias, T: int, k: int, gamma: float):
+    """Fixed-step loss-free selection-bias update [Handbook-news, "confirmed":
+    the fixed-step update; Handbook-digest, "the three hard parts", 2]:
+    b_e += gamma * sign(T*k/E - count_e), sign(0) = 0."""
+    counts = np.asarray(counts, F64)
+    E = counts.shape[0]
+    return np.asarray(bias, F64) + float(np.float32(gamma)) * np.sign(T * k / E - counts)
+
+
+# ---------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------
+def layer_fwd(p, inp, keep_hidden: bool = False):
+    """Forward pass of the layer for preset ``p`` on inputs ``inp`` (the dict
+    from the seeded generator).  Steps in order: route, capacity, dispatch,
+    permute, expert FFN, shared expert, combine."""
+    r = route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale,
+              inp.get("offset"), inp.get("sel_bias"), p.aux_coef, p.z_coef)
+    C = capacity(p.T, p.E, p.k, p.capacity_factor)
+    counts, offsets, row_of_slot, token_of_row = dispatch(r["idx"], p.E, C)
+    R = int(offsets[-1])
+    x_perm = permute(inp["x"], token_of_row, R)
+    res = expert_ffn(x_perm, offsets, inp["W13"], inp["W2"], p.act, keep_hidden)
+    o, hs, as_ = res if keep_hidden else (res, None, None)
+    shared = None
+    sh = None
+    if p.F_shared > 0:
+        sh = shared_expert(inp["x"], inp["Ws13"], inp["Ws2"], keep_hidden=True)
+        shared = sh[0]
+    y = combine(o, row_of_slot, r["g"], shared)
+    out = dict(r, C=C, counts=counts, offsets=offsets, row_of_slot=row_of_slot,
+               token_of_row=token_of_row, R=R, x_perm=x_perm, o=o, shared_out=shared, y=y)
+    if keep_hidden:
+        out.update(h=hs, a=as_, shared_h=None if sh is None else sh[1],
+                   shared_a=None if sh is None else sh[2])
+    return out
+
+
+def _ffn_bwd(X, h, a, W13e, W2e, dO, act):
+    """Backward of o = act(X W13^T) W2^T for one expert; returns dX, dW13, dW2."""
+    dA = dO @ np.asarray(W2e, F64)
+    dW2 = dO.T @ a
+    if act == "swiglu":
+        F = h.shape[1] // 2
+        hg, hu = h[:, :F], h[:, F:]
+        sg = 1.0 / (1.0 + np.exp(-hg))
+        dsilu = sg * (1.0 + hg * (1.0 - sg))
+        dH = np.concatenate([dA * hu * dsilu, dA * (hg * sg)], axis=1)
+    else:
+        phi = np.exp(-0.5 * h * h) / math.sqrt(2.0 * math.pi)
+        Phi = 0.5 * (1.0 + erf(h / math.sqrt(2.0)))
+        dH = dA * (Phi + h * phi)
+    dX = dH @ np.asarray(W13e, F64)
+    dW13 = dH.T @ np.asarray(X, F64)
+    return dX, dW13, dW2
+
+
+def layer_bwd(p, inp, fwd, dy):
+    """Gradients of J = <dy, y> + L_aux + L_z, by the chain rule.
+
+    Routing decisions (idx, drops) and the load fractions f_e are piecewise
+    constant and carry no gradient; the selection bias and the logit offset get
+    none (the gradient reaches the router only through the kept gates
+    [Handbook explainer, "router and load balancing": top-k selection is not
+    differentiable]).  Returns dx [T,d], dWg [d,E], dW13, dW2, dWs13, dWs2.
+    """
+    dy = np.asarray(dy, F64)
+    x = np.asarray(inp["x"], F64)
+    T, d = x.shape
+    E, k = p.E, p.k
+    row_of_slot, g, o = fwd["row_of_slot"], fwd["g"], fwd["o"]
+    R = fwd["R"]
+    # combine backward
+    dO = np.zeros((R, d), F64)
+    dg = np.zeros((T, k), F64)
+    for j in range(k):
+        kept = row_of_slot[:, j] >= 0
+        rows = row_of_slot[kept, j]
+        dO[rows] = g[kept, j, None] * dy[kept]
+        dg[kept, j] = np.sum(dy[kept] * o[rows], axis=1)
+    # expert backward
+    offsets = fwd["offsets"]
+    dXp = np.zeros((R, d), F64)
+    dW13 = np.zeros(inp["W13"].shape, F64)
+    dW2 = np.zeros(inp["W2"].shape, F64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        dX, dW13[e], dW2[e] = _ffn_bwd(fwd["x_perm"][r0:r1], fwd["h"][e], fwd["a"][e],
+                                       inp["W13"][e], inp["W2"][e], dO[r0:r1], p.act)
+        dXp[r0:r1] = dX
+    dx = np.zeros((T, d), F64)
+    for j in range(k):
+        kept = row_of_slot[:, j] >= 0
+        dx[kept] += dXp[row_of_slot[kept, j]]
+    dWs13 = dWs2 = None
+    if p.F_shared > 0:
+        dxs, dWs13, dWs2 = _ffn_bwd(x, fwd["shared_h"], fwd["shared_a"], inp["Ws13"],
+                                    inp["Ws2"], dy, "swiglu")
+        dx += dxs
+    # router backward: gates -> scores
+    s, z, idx = fwd["s"], fwd["z"], fwd["idx"]
+    scale = float(np.float32(p.gate_scale))
+    ssel = np.take_along_axis(s, idx, axis=1)
+    if p.renorm:
+        S = ssel.sum(axis=1, keepdims=True)
+        ghat = ssel / S
+        dsel = scale / S * (dg - np.sum(dg * ghat, axis=1, keepdims=True))
+    else:
+        dsel = scale * dg
+    ds = np.zeros((T, E), F64)
+    np.put_along_axis(ds, idx, dsel, axis=1)      # idx rows are distinct experts
+    aux_coef = float(np.float32(p.aux_coef))
+    if aux_coef != 0.0:
+        f = fwd["counts"] / (T * k)
+        c = aux_coef * E * f / T                   # dL_aux / dp_hat_te
+        Ssum = s.sum(axis=1, keepdims=True)
+        p_hat = s / Ssum
+        ds += (c[None, :] - np.sum(p_hat * c[None, :], axis=1, keepdims=True)) / Ssum
+    # scores -> logits
+    if p.score == "softmax":
+        dz = s * (ds - np.sum(ds * s, axis=1, keepdims=True))
+    elif p.score == "sigmoid":
+        dz = ds * s * (1.0 - s)
+    else:
+        sig = 1.0 / (1.0 + np.exp(-z))
+        safe = np.where(s > 0, s, 1.0)
+        dz = ds * np.where(s > 0, sig / (2.0 * safe), 0.5 * np.exp(0.5 * z))
+    z_coef = float(np.float32(p.z_coef))
+    if z_coef != 0.0:
+        lse = logsumexp_rows(z)
+        sm = np.exp(z - lse[:, None])
+        dz += 2.0 * z_coef / T * lse[:, None] * sm
+    dWg = x.T @ dz
+    dx += dz @ np.asarray(inp["Wg"], F64).T
+    return dict(dx=dx, dWg=dWg, dW13=dW13, dW2=dW2, dWs13=dWs13, dWs2=dWs2,
+                dO=dO, dg=dg, dz=dz, dXp=dXp)
