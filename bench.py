@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse MoE layer on one MI355X.
+
+Default workload: the Switch-style top-1 layer (T=8192 tokens, d=1024, E=32
+GELU experts of width 4096, capacity factor 1.0, FP32 router with aux and z
+losses, bf16 experts), seeded synthetic inputs resident in HBM.
+
+A step is one pass of the layer over the batch: forward (route, dispatch and
+permute, grouped expert FFN, combine) and, unless --fwd-only, the backward.
+Prints ONE JSON line with the whole-job tokens/s, a roofline block for the
+grouped expert GEMM measured with HIP events on the stream it runs on, per-step
+rates, and the CPU oracle timed on a bounded sample on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", help="preset name (c1..c5)")
+    ap.add_argument("--fwd-only", action="store_true")
+    ap.add_argument("--stage-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from top_routing_expert_amd import binding as B, perf, presets, synth
+
+    p = presets.get(args.config)
+    train = p.train or not args.fwd_only
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {p.name} inputs")
+    inp = synth.make_inputs(p, seed=0, with_dy=train)
+    x = torch.from_numpy(inp["x"]).to(dev).to(B.TORCH_DTYPE[p.dtype]).contiguous()
+    w = B.weights_to_device(p, inp, dev)
+    dy = torch.from_numpy(inp["dy"]).to(dev) if train else None
+    layer = B.Layer(p, w, dev, train=train)
+
+    def step():
+        layer.fwd(x)
+        if train:
+            layer.bwd(x, dy)
+
+    try:
+        step()
+        torch.cuda.synchronize()
+    except B.MoeError as e:
+        if train and e.status == B.MOE_ERR_UNSUPPORTED:
+            log("[bench] backward not available; timing the forward only")
+            train = False
+            layer = B.Layer(p, w, dev, train=False)
+        else:
+            raise
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done; timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    tok_s = p.T / dt
+    log(f"[bench] {dt * 1e3:.3f} ms/step, {tok_s / 1e6:.2f} M tokens/s")
+
+    # ---- per-step rates, HIP events on the current stream (the library's stream)
+    ws = B.Workspace(dev)
+    y, st = B.layer_fwd(p, w, x, stats=True, ws=ws)
+    r = B.route(p, x, w.Wg, w.offset, w.sel_bias, ws=ws)
+    pm = B.permute(p, x, r["idx"], ws=ws)
+    torch.cuda.synchronize()
+    offsets = pm["offsets"].cpu().numpy()
+    R = int(offsets[-1])
+    active = int(np.count_nonzero(np.diff(offsets)))
+    counts = pm["counts"].cpu().numpy()
+
+    def timed(fn, iters):
+        fn()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2e7))          # keep the GPU busy while the host enqueues
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters * 1e-3   # seconds per call
+
+    it = args.stage_iters
+    ffn_out = torch.empty(p.T * p.k, p.d, dtype=torch.float32, device=dev)
+    t_route = timed(lambda: B.route(p, x, w.Wg, w.offset, w.sel_bias, ws=ws), it)
+    t_perm = timed(lambda: B.permute(p, x, r["idx"], ws=ws), it)
+    t_ffn = timed(lambda: B.expert_ffn(p, pm["x_perm"], pm["offsets"], w.W13, w.W2,
+                                       max_rows=p.T * p.k, ws=ws), it)
+    gate = r["gate"]
+    t_comb = timed(lambda: B.combine(p, ffn_out, pm["row_of_slot"], gate), it)
+
+    fl = perf.ffn_flops(p, R, shared=False)
+    by = perf.ffn_bytes(p, R, active, shared=False)
+    t_mfma = fl / (perf.PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = by / (perf.PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        roof = dict(bound="hbm", achieved=by / t_ffn / 1e9, peak=perf.PEAK_HBM_GBS, unit="GB/s")
+    else:
+        roof = dict(bound="mfma", achieved=fl / t_ffn / 1e12, peak=perf.PEAK_BF16_TFLOPS, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "moe_expert_ffn: grouped GEMM up (fused act) + grouped GEMM down"
+    roof["algorithmic"] = dict(flops=fl, bytes=by, rows=R, active_experts=active,
+                               avg_launch_us=t_ffn * 1e6)
+    stages = {
+        "route": dict(us=t_route * 1e6, GBps=perf.route_bytes(p) / t_route / 1e9,
+                      hbm_frac=perf.route_bytes(p) / t_route / 1e9 / perf.PEAK_HBM_GBS),
+        "permute": dict(us=t_perm * 1e6, GBps=perf.permute_bytes(p, R) / t_perm / 1e9,
+                        hbm_frac=perf.permute_bytes(p, R) / t_perm / 1e9 / perf.PEAK_HBM_GBS),
+        "expert_ffn": dict(us=t_ffn * 1e6, TFLOPs=fl / t_ffn / 1e12,
+                           mfma_frac=fl / t_ffn / 1e12 / perf.PEAK_BF16_TFLOPS,
+                           GBps=by / t_ffn / 1e9),
+        "combine": dict(us=t_comb * 1e6, GBps=perf.combine_bytes(p, R) / t_comb / 1e9,
+                        hbm_frac=perf.combine_bytes(p, R) / t_comb / 1e9 / perf.PEAK_HBM_GBS),
+    }
+    for k_, v in stages.items():
+        log(f"[bench] {k_:10s} " + " ".join(f"{a}={b:.4g}" for a, b in v.items()))
+
+    # ---- CPU oracle on a bounded sample, on this host's cores
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:
+            blas_threads = None
+        Ts = min(p.T, 2048)
+        sub = dict(inp, x=inp["x"][:Ts], dy=None if inp.get("dy") is None else inp["dy"][:Ts])
+        ps = p.with_(T=Ts)
+        t0 = time.perf_counter()
+        oracle.layer_fwd(ps, sub)
+        tc = time.perf_counter() - t0
+        cpu = dict(value=Ts / tc, unit="tokens/s", cores=blas_threads or len(os.sched_getaffinity(0)),
+                   kind="oracle",
+                   sample=f"float64 oracle forward of the first {Ts} of {p.T} tokens of the same "
+                          f"layer (all {p.E} experts' weights), {tc:.1f} s")
+        log(f"[bench] cpu oracle: {Ts / tc:.1f} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "MoE layer tokens/s at 1 GPU; grouped-GEMM % bf16 MFMA peak; permute GB/s",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if p.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian inputs and weights)",
+        "config": {"workload": f"{p.name}: T={p.T} d={p.d} E={p.E} top-{p.k} F={p.F} {p.act} "
+                               f"{p.score} CF={p.capacity_factor} shared={p.F_shared}",
+                   "step": "forward+backward" if train else "forward",
+                   "global_batch": p.T, "parallelism": "single GPU"},
+        "roofline": roof,
+        "stages": stages,
+        "grouped_gemm_mfma_frac": stages["expert_ffn"]["mfma_frac"],
+        "permute_GBps": stages["permute"]["GBps"],
+        "routing": dict(kept_rows=R, dropped=int(p.T * p.k - R), max_over_mean_load=float(
+            counts.max() / max(counts.mean(), 1e-9))),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) sparse mixture-of-experts layer.
+ *
+ * The layer: an FP32 router scores each of T tokens against E experts,
+ * keeps the top-k (optionally after adding a selection-only bias), applies an
+ * expert capacity with overflow left to the residual, permutes the kept
+ * (token, expert) slots into expert-contiguous rows, runs each expert's FFN
+ * and combines y_t = sum_j G_tj * E_idx_tj(x_t) (+ a shared expert).
+ *
+ * Sources (page title, section):
+ *   "Mixture of Experts Explained" — "What is sparsity?" (weighted expert sum,
+ *     softmax gating, KeepTopK, softmax over the kept logits); "MoEs and
+ *     Transformers" (expert capacity, overflow through the residual);
+ *     "Switch Transformers" (top-1 routing, capacity equation and factor,
+ *     bf16 experts with a full-precision router); "Load balancing tokens for
+ *     MoEs" and "Stabilizing training with router Z-loss" (router losses).
+ *   "The Ultimate MoE Training Handbook" digest — "what MoE saves"
+ *     (fine-grained experts), "the three hard parts" (FP32 routing,
+ *     aux loss vs loss-free bias).
+ *   Handbook news digest, "confirmed" bullets — sigmoid and sqrt(softplus)
+ *     scoring, routing scale near sqrt(k), fixed-step bias update, shared
+ *     experts.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
+ *     row-major, owned by the caller.  The struct pointers (dims, opts,
+ *     weights, saved, grads, stats) are HOST pointers read during the call.
+ *   - Weights use the [out, in] layout: W13 [E, n_up, d] with n_up = 2F for
+ *     SwiGLU (rows 0..F-1 gate, F..2F-1 up) and F for GELU; W2 [E, d, F];
+ *     shared Ws13 [2*F_shared, d], Ws2 [d, F_shared].  The router weight is
+ *     Wg [d, E] fp32 (z = x . Wg).
+ *   - x, x_perm, W13, W2, Ws13, Ws2, h, a share one element type, opts.dtype
+ *     (bf16 or fp32).  Router tensors, gates, expert outputs o, y, dx and all
+ *     gradients are fp32.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
+ *     only enqueues work on it: there is no device-to-host synchronisation and
+ *     the library allocates nothing.  Shape-dependent work (per-expert row
+ *     counts) is read on the device.
+ *   - `ws`/`ws_bytes` is caller-owned device scratch of at least
+ *     moe_workspace_size() bytes, 256-byte aligned; contents need no
+ *     initialisation and are clobbered.
+ *   - Errors are returned synchronously as moe_status before anything is
+ *     enqueued; MOE_ERR_HIP reports a failed launch.  T = 0 is a successful
+ *     no-op.  Results are bitwise deterministic for identical inputs.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null required pointer, bad size or option, misalignment */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement (see limits) */
+  MOE_ERR_WORKSPACE = 3,    /* ws_bytes below moe_workspace_size() */
+  MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SQRT_SOFTPLUS = 2 } moe_score;
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GELU = 1 } moe_act;
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+
+/* Problem statement of one layer call.
+ * T tokens, hidden size d, E routed experts, k experts kept per token,
+ * F routed expert width, F_shared width of the one shared SwiGLU expert (0 = none).
+ * Limits: 1 <= k <= min(E, 16); 1 <= E <= 256; T*k < 2^31;
+ * bf16: d, F and F_shared multiples of 128; fp32: d, F, F_shared multiples of 4. */
+typedef struct { int64_t T, d, E, k, F, F_shared; } moe_dims;
+
+/* score: moe_score; act: moe_act; dtype: moe_dtype;
+ * renorm != 0: kept gates are divided by their sum, then multiplied by gate_scale;
+ * capacity_factor <= 0: no capacity limit, else C = ceil(cf * T * k / E) slots per expert;
+ * aux_coef, z_coef: load-balance and z-loss coefficients (0 = not computed). */
+typedef struct {
+  int32_t score, act, dtype, renorm;
+  float gate_scale, capacity_factor, aux_coef, z_coef;
+} moe_opts;
+
+typedef struct {
+  const float* Wg;            /* [d, E] */
+  const float* logit_offset;  /* nullable [E]: added to the logits (part of z) */
+  const float* sel_bias;      /* nullable [E]: added to the scores for selection only */
+  const void* W13;            /* [E, n_up, d] */
+  const void* W2;             /* [E, d, F] */
+  const void* Ws13;           /* [2*F_shared, d] when F_shared > 0 */
+  const void* Ws2;            /* [d, F_shared]   when F_shared > 0 */
+} moe_weights;
+
+/* Forward state kept for the backward pass; every field is a caller-owned
+ * device buffer of the given size.  moe_layer_fwd fills it when passed. */
+typedef struct {
+  int32_t* topk_idx;     /* [T, k] chosen experts, descending selection score */
+  float* topk_gate;      /* [T, k] gates */
+  float* logits;         /* [T, E] router logits z (offset included) */
+  int32_t* counts;       /* [E] slots per expert before capacity */
+  int32_t* offsets;      /* [E+1] first row of each expert; offsets[E] = kept rows R */
+  int32_t* row_of_slot;  /* [T, k] row of each slot, -1 when dropped */
+  int32_t* token_of_row; /* [T*k] token of each row (entries >= R unspecified) */
+  void* x_perm;          /* [T*k, d] expert-contiguous copy of x */
+  void* h;               /* [T*k, n_up] expert pre-activations */
+  void* a;               /* [T*k, F] expert activations */
+  float* o;              /* [T*k, d] expert outputs */
+  void* h_shared;        /* [T, 2*F_shared] (when F_shared > 0) */
+  void* a_shared;        /* [T, F_shared]   (when F_shared > 0) */
+  float* losses;         /* [2] aux loss, z-loss */
+} moe_saved;
+
+typedef struct {
+  float* dWg;    /* [d, E] */
+  float* dW13;   /* [E, n_up, d] */
+  float* dW2;    /* [E, d, F] */
+  float* dWs13;  /* [2*F_shared, d] (when F_shared > 0) */
+  float* dWs2;   /* [d, F_shared]   (when F_shared > 0) */
+} moe_grads;
+
+/* Router monitoring outputs, every field nullable. */
+typedef struct {
+  int32_t* counts;      /* [E] slots per expert before capacity */
+  int32_t* n_dropped;   /* [1] slots dropped over capacity */
+  float* losses;        /* [2] aux loss, z-loss */
+  int32_t* n_nonfinite; /* [1] tokens with a non-finite router logit */
+} moe_stats;
+
+/* Expert capacity ("Switch Transformers", capacity equation, tokens read as
+ * the T*k routed slots): *C = ceil(cf*T*k/E) computed in double from the fp32
+ * factor, or -1 when capacity_factor <= 0.  Host only. */
+int moe_capacity(const moe_dims* dims, const moe_opts* opts, int64_t* C);
+
+/* Bytes of scratch any entry point below needs for these dims/opts, with the
+ * backward pass (with_bwd != 0) or without.  Host only. */
+int moe_workspace_size(const moe_dims* dims, const moe_opts* opts, int with_bwd, size_t* bytes);
+
+/* Router ("What is sparsity?" gating equations; "Switch Transformers" top-1
+ * and full-precision router; news digest: sigmoid / sqrt(softplus) scoring,
+ * selection-only bias, routing scale).
+ * z = x . Wg (+ logit_offset) with fp32 accumulation of exact products;
+ * s = score(z); top-k of s + sel_bias by (value desc, index asc), NaN lowest;
+ * gate_j = s[idx_j], renormalised over the kept experts if opts.renorm, times
+ * gate_scale.  Outputs: topk_idx [T,k], topk_gate [T,k]; nullable: scores
+ * [T,E] (s), logits [T,E] (z), counts [E] (pre-capacity histogram), losses [2]
+ * (aux, z-loss; zero when the coefficient is 0). */
+int moe_route(const moe_dims* dims, const moe_opts* opts, const void* x, const float* Wg,
+              const float* logit_offset, const float* sel_bias, int32_t* topk_idx,
+              float* topk_gate, float* scores, float* logits, int32_t* counts, float* losses,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch ("MoEs and Transformers": expert capacity, overflow to the residual).
+ * counts[e] = slots choosing e; expert e keeps its first C slots in ascending
+ * token order; rows are expert-contiguous from offsets (exclusive scan of
+ * min(counts, C)); row_of_slot[t,j] = row or -1; token_of_row[row] = t;
+ * x_perm[row] = x[t].  topk_idx entries outside [0,E) are ignored (dropped)
+ * and never index memory. */
+int moe_permute(const moe_dims* dims, const moe_opts* opts, const void* x,
+                const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                int32_t* row_of_slot, int32_t* token_of_row, void* x_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs over expert-contiguous rows (the "Making MoEs go brrr" grouped
+ * computation): for group g, rows offsets[g]..offsets[g+1]-1 of x_perm go
+ * through act(x W13[g]^T) W2[g]^T with width F (act: SwiGLU with the gate/up
+ * projections fused, or exact GELU).  out [max_rows, d] fp32.  max_rows is an
+ * upper bound of offsets[n_groups] used to size the launch.  h_save
+ * [max_rows, n_up] and a_save [max_rows, F] (nullable) receive the
+ * pre-activation and the activation in the x element type. */
+int moe_expert_ffn(const moe_dims* dims, const moe_opts* opts, int64_t n_groups,
+                   int64_t max_rows, int64_t F, const void* x_perm, const int32_t* offsets,
+                   const void* W13, const void* W2, void* h_save, void* a_save, float* out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Combine ("What is sparsity?", y = sum_i G(x)_i E_i(x)): y[t] = sum over
+ * kept slots j, in slot order, of topk_gate[t,j] * out_perm[row_of_slot[t,j]]
+ * plus shared_out[t] (nullable).  A fully dropped token gets y = shared or 0. */
+int moe_combine(const moe_dims* dims, const float* out_perm, const int32_t* row_of_slot,
+                const float* topk_gate, const float* shared_out, float* y, void* stream);
+
+/* Whole forward: route, dispatch, routed expert FFNs, shared expert, combine.
+ * y [T,d] fp32 (the caller adds the residual x).  saved and stats nullable. */
+int moe_layer_fwd(const moe_dims* dims, const moe_opts* opts, const moe_weights* w,
+                  const void* x, float* y, moe_saved* saved, moe_stats* stats,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Whole backward of J = <dy, y> + L_aux + L_z from the state saved by
+ * moe_layer_fwd.  Routing decisions and load fractions are constants; the
+ * selection bias and logit offset get no gradient.  dx [T,d] fp32; grads
+ * overwritten (not accumulated), fp32. */
+int moe_layer_bwd(const moe_dims* dims, const moe_opts* opts, const moe_weights* w,
+                  const void* x, const moe_saved* saved, const float* dy, float* dx,
+                  moe_grads* grads, void* ws, size_t ws_bytes, void* stream);
+
+/* Fixed-step loss-free bias update (news digest: the fixed-step baseline;
+ * handbook digest: loss-free bias): bias[e] += gamma * sign(target - counts[e]),
+ * sign(0) = 0; target is normally T*k/E. */
+int moe_bias_update(const int32_t* counts, float* bias, int64_t E, float target, float gamma,
+                    void* stream);
+
+/* Static text for a moe_status value. */
+const char* moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

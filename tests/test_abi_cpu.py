@@ -1,0 +1,108 @@
+"""Host-side checks of the C-ABI library (no GPU compute).
+
+The library loads and exports every entry point ``include/moe.h`` declares; the
+host-only calls (capacity, workspace size) and the synchronous argument checks
+behave as documented.  Nothing here launches a kernel.
+"""
+
+import ctypes as C
+import json
+import os
+import re
+
+import pytest
+
+from top_routing_expert_amd import binding as B, presets
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from top_routing_expert_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(B.ABI_FUNCTIONS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_capacity_matches_golden(L):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "capacity.json")))
+    for c in g["cases"]:
+        p = presets.get("c1").with_(T=c["T"], E=c["E"], k=c["k"], capacity_factor=c["capacity_factor"])
+        want = -1 if c["C"] is None else c["C"]
+        assert B.capacity(p) == want, c
+
+
+def test_strerror(L):
+    for s in range(5):
+        assert L.moe_strerror(s)
+    assert L.moe_strerror(99) == b"unknown status"
+
+
+def test_workspace_size_grows_with_tokens(L):
+    for name in presets.PRESETS:
+        p = presets.get(name)
+        a = B.workspace_size(p, T=p.T // 2)
+        b = B.workspace_size(p)
+        assert 0 < a < b
+        assert b % 256 == 0
+
+
+def _route_status(p, **kw):
+    d, o = B.dims_of(p), B.opts_of(p)
+    for k, v in kw.items():
+        if hasattr(d, k):
+            setattr(d, k, v)
+        else:
+            setattr(o, k, v)
+    dummy = C.c_void_p(256)
+    return B.lib().moe_route(C.byref(d), C.byref(o), dummy, dummy, None, None, dummy, dummy, None,
+                             None, None, None, dummy, 1 << 40, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 0, B.MOE_ERR_INVALID_ARG), ("k", 65, B.MOE_ERR_INVALID_ARG), ("k", 17, B.MOE_ERR_UNSUPPORTED),
+    ("E", 300, B.MOE_ERR_UNSUPPORTED), ("T", -1, B.MOE_ERR_INVALID_ARG),
+    ("d", 100, B.MOE_ERR_UNSUPPORTED), ("score", 7, B.MOE_ERR_INVALID_ARG),
+    ("dtype", 5, B.MOE_ERR_INVALID_ARG), ("capacity_factor", float("nan"), B.MOE_ERR_INVALID_ARG)])
+def test_argument_errors_are_synchronous(L, field, value, status):
+    p = presets.get("c4")
+    assert _route_status(p, **{field: value}) == status
+
+
+def test_null_and_misaligned_pointers(L):
+    p = presets.get("c2")
+    d, o = B.dims_of(p), B.opts_of(p)
+    ok = C.c_void_p(256)
+    bad = C.c_void_p(258)
+    r = B.lib().moe_route
+    assert r(C.byref(d), C.byref(o), None, ok, None, None, ok, ok, None, None, None, None, ok, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert r(C.byref(d), C.byref(o), bad, ok, None, None, ok, ok, None, None, None, None, ok, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    # workspace too small
+    assert r(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None, None, ok, 16, None) == B.MOE_ERR_WORKSPACE
+    # workspace misaligned
+    assert r(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None, None, C.c_void_p(272), 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_noop(L):
+    p = presets.get("c2")
+    d, o = B.dims_of(p, T=0), B.opts_of(p)
+    ok = C.c_void_p(256)
+    assert B.lib().moe_route(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None,
+                             None, ok, 1 << 40, None) == B.MOE_OK
+    assert B.lib().moe_combine(C.byref(d), ok, ok, ok, None, ok, None) == B.MOE_OK

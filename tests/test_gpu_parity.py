@@ -1,0 +1,341 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Step-wise: each GPU step is compared with the oracle step fed the same
+upstream values, so a legitimate near-tie flip in the router cannot cascade.
+Bars (written per test):
+  * router: expert indices exact except at near-ties (k-th vs (k+1)-th, or two
+    adjacent kept scores, closer than 1e-5 relative), where the GPU's choice is
+    checked to be a valid top-k; scores, gates and losses within 1e-5 relative;
+  * dispatch: counts, offsets, row_of_slot, token_of_row and x_perm bit-exact;
+  * expert FFN and layer output: max-abs error <= 2e-2 * RMS(reference) for
+    bf16 experts, <= 1e-4 absolute and <= 1e-4 * RMS for the fp32 layer.
+Full-size presets are checked on sampled rows/tokens the oracle computes one
+by one; the tiny fp32 preset is checked everywhere.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from top_routing_expert_amd import binding as B, presets, synth
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+ALL = ["c1", "c2", "c3", "c4", "c5"]
+
+_cache = {}
+
+
+def case(name, **over):
+    key = (name, tuple(sorted(over.items())))
+    if key not in _cache:
+        p = presets.get(name, **over)
+        print(f"[case] generating {name} {over}", flush=True)
+        inp = synth.make_inputs(p, seed=0)
+        x = torch.from_numpy(inp["x"]).to(DEV).to(B.TORCH_DTYPE[p.dtype]).contiguous()
+        w = B.weights_to_device(p, inp, DEV)
+        _cache[key] = (p, inp, x, w)
+    return _cache[key]
+
+
+def x_host(p, inp):
+    return inp["x"]
+
+
+def check_route(p, out, ref):
+    idx_g = out["idx"].cpu().numpy().astype(np.int64)
+    flag = ref["near_tie"] | ref["near_tie_order"]
+    mism = np.any(idx_g != ref["idx"], axis=1)
+    assert not np.any(mism & ~flag), f"{int(np.sum(mism & ~flag))} non-tie index mismatches"
+    for t in np.nonzero(mism)[0]:
+        assert len(set(idx_g[t].tolist())) == p.k
+        sel = ref["sel"][t]
+        got, want = np.sort(sel[idx_g[t]])[::-1], np.sort(sel[ref["idx"][t]])[::-1]
+        assert np.all(np.abs(got - want) <= 1e-5 * np.maximum(np.abs(got), np.abs(want)))
+    ok = ~mism
+    g = out["gate"].cpu().numpy()
+    np.testing.assert_allclose(g[ok], ref["g"][ok], rtol=1e-5, atol=1e-12)
+    return idx_g, int(np.sum(mism))
+
+
+# --------------------------------------------------------------------------- router
+@pytest.mark.parametrize("name", ALL)
+def test_route_parity(name):
+    p, inp, x, w = case(name)
+    out = B.route(p, x, w.Wg, w.offset, w.sel_bias, want_scores=True, want_logits=True)
+    torch.cuda.synchronize()
+    ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                    inp["sel_bias"], p.aux_coef, p.z_coef)
+    idx_g, nflip = check_route(p, out, ref)
+    np.testing.assert_allclose(out["scores"].cpu().numpy(), ref["s"], rtol=1e-5, atol=1e-12)
+    np.testing.assert_allclose(out["logits"].cpu().numpy(), ref["z"], rtol=1e-5, atol=1e-6)
+    counts = out["counts"].cpu().numpy()
+    np.testing.assert_array_equal(counts, np.bincount(idx_g.ravel(), minlength=p.E))
+    # losses: the oracle's formula evaluated with the GPU's (tie-resolved) counts
+    aux, zl = orc.router_losses(ref["z"], ref["s"], counts, p.k, p.aux_coef, p.z_coef)
+    l = out["losses"].cpu().numpy()
+    np.testing.assert_allclose(l, [aux, zl], rtol=1e-5, atol=0)
+    print(f"{name}: near-tie flips {nflip}, flagged {int(np.sum(ref['near_tie'] | ref['near_tie_order']))}")
+
+
+def test_route_exact_ties_and_nan():
+    p = presets.get("c2", T=96)
+    x = torch.zeros(96, p.d, dtype=torch.bfloat16, device=DEV)
+    x[:64] = 1.0
+    x[64:, 0] = float("nan")
+    Wg = torch.zeros(p.d, p.E, dtype=torch.float32, device=DEV)
+    Wg[0, 5] = Wg[0, 9] = 0.5                      # experts 5 and 9 tie on every token
+    p2 = p.with_(k=3)
+    out = B.route(p2, x, Wg)
+    torch.cuda.synchronize()
+    idx = out["idx"].cpu().numpy()
+    np.testing.assert_array_equal(idx[:64], np.tile([5, 9, 0], (64, 1)))
+    np.testing.assert_array_equal(idx[64:], np.tile([0, 1, 2], (32, 1)))   # NaN rows: lowest indices
+
+
+# --------------------------------------------------------------------------- dispatch
+def _check_dispatch(p, x, idx_np, C):
+    idx = torch.from_numpy(idx_np.astype(np.int32)).to(DEV)
+    out = B.permute(p, x, idx)
+    torch.cuda.synchronize()
+    counts, offsets, ros, tor = orc.dispatch(idx_np, p.E, C)
+    R = int(offsets[-1])
+    np.testing.assert_array_equal(out["counts"].cpu().numpy(), counts)
+    np.testing.assert_array_equal(out["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(out["row_of_slot"].cpu().numpy(), ros)
+    np.testing.assert_array_equal(out["token_of_row"].cpu().numpy()[:R], tor[:R])
+    bits = lambda t: t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+    assert torch.equal(bits(out["x_perm"][:R]), bits(x[torch.from_numpy(tor[:R]).to(DEV)]))
+    return out
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_permute_parity(name):
+    p, inp, x, w = case(name)
+    ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                    inp["sel_bias"])
+    _check_dispatch(p, x, ref["idx"], orc.capacity(p.T, p.E, p.k, p.capacity_factor))
+
+
+@pytest.mark.parametrize("T,k,cf", [(1, 2, 1.25), (255, 2, 1.25), (257, 1, 1.0), (1000, 3, 0.8),
+                                    (777, 8, 0.0)])
+def test_permute_ragged_and_drops(T, k, cf):
+    p = presets.get("c1", T=T, k=k, capacity_factor=cf)
+    rng = np.random.default_rng(T)
+    # skewed choices so that capacity bites
+    prob = np.array([0.4, 0.2, 0.1, 0.1, 0.05, 0.05, 0.05, 0.05])
+    idx = np.stack([rng.choice(p.E, size=k, replace=False, p=prob) for _ in range(T)])
+    x = torch.randn(T, p.d, device=DEV)
+    _check_dispatch(p, x, idx, orc.capacity(T, p.E, k, cf))
+
+
+def test_permute_ignores_out_of_range_experts():
+    p = presets.get("c1", T=300)
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(p.E, size=2, replace=False) for _ in range(300)])
+    idx[::7, 0] = -1
+    idx[::11, 1] = p.E + 3
+    x = torch.randn(300, p.d, device=DEV)
+    out = _check_dispatch(p, x, idx, orc.capacity(300, p.E, 2, p.capacity_factor))
+    assert np.all(out["row_of_slot"].cpu().numpy()[::7, 0] == -1)
+
+
+# --------------------------------------------------------------------------- expert FFN
+def _sample_rows(offsets, rng, per_group=3):
+    rows = []
+    for e in range(len(offsets) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            rows += [r0, r1 - 1] + list(rng.integers(r0, r1, size=per_group))
+    return np.unique(np.array(rows, np.int64))
+
+
+def _ffn_rows(p, inp, xp, offsets, rows, W13=None, W2=None, act=None):
+    W13 = inp["W13"] if W13 is None else W13
+    W2 = inp["W2"] if W2 is None else W2
+    grp = np.searchsorted(offsets, rows, side="right") - 1
+    out = np.zeros((len(rows), W2.shape[1]))
+    for e in np.unique(grp):
+        sel = grp == e
+        out[sel] = orc.expert_ffn(xp[sel], np.array([0, int(sel.sum())]), W13[e:e + 1], W2[e:e + 1],
+                                  act or p.act)
+    return out
+
+
+def _assert_bf16_close(got, ref, what):
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= 2e-2 * rms, f"{what}: max-abs {err:.3e} > 2e-2 * rms {rms:.3e}"
+    return err / rms
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_expert_ffn_parity(name):
+    p, inp, x, w = case(name)
+    ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                    inp["sel_bias"])
+    idx = torch.from_numpy(ref["idx"].astype(np.int32)).to(DEV)
+    pm = B.permute(p, x, idx)
+    res = B.expert_ffn(p, pm["x_perm"], pm["offsets"], w.W13, w.W2, max_rows=p.T * p.k,
+                       save_hidden=True)
+    torch.cuda.synchronize()
+    offsets = pm["offsets"].cpu().numpy()
+    R = int(offsets[-1])
+    if p.dtype == "f32":
+        rows = np.arange(R)
+    else:
+        rows = _sample_rows(offsets, np.random.default_rng(1))
+    xp = pm["x_perm"][torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    o_ref = _ffn_rows(p, inp, xp, offsets, rows)
+    o = res["out"][torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    if p.dtype == "f32":
+        err = np.max(np.abs(o - o_ref))
+        assert err <= 1e-4 and err <= 1e-4 * np.sqrt(np.mean(o_ref ** 2)), err
+    else:
+        r = _assert_bf16_close(o, o_ref, f"{name} expert out")
+        print(f"{name}: expert FFN max-abs/rms {r:.2e} on {len(rows)} rows")
+
+
+# --------------------------------------------------------------------------- combine
+def test_combine_parity():
+    p = presets.get("c4", T=1000)
+    rng = np.random.default_rng(3)
+    idx = np.stack([rng.choice(p.E, size=p.k, replace=False) for _ in range(p.T)])
+    counts, offsets, ros, tor = orc.dispatch(idx, p.E, 700)   # some drops
+    R = int(offsets[-1])
+    o = rng.normal(size=(R, p.d)).astype(np.float32)
+    g = rng.random((p.T, p.k)).astype(np.float32)
+    sh = rng.normal(size=(p.T, p.d)).astype(np.float32)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    y = B.combine(p, t(o), t(ros.astype(np.int32)), t(g), t(sh))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(y.cpu().numpy(), orc.combine(o, ros, g, sh), rtol=1e-5, atol=1e-5)
+
+
+# --------------------------------------------------------------------------- whole layer
+def _layer_ref_sampled(p, inp, saved, tokens):
+    """Oracle y for the given tokens, using the GPU's routing decisions."""
+    ref = orc.route(inp["x"][tokens], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale,
+                    inp["offset"], inp["sel_bias"])
+    idx = saved["topk_idx"].cpu().numpy()[tokens].astype(np.int64)
+    ros = saved["row_of_slot"].cpu().numpy()[tokens]
+    g = orc.gates(ref["s"], idx, p.renorm, p.gate_scale)
+    X = inp["x"][tokens].astype(np.float64)
+    y = np.zeros((len(tokens), p.d))
+    for i in range(len(tokens)):
+        for j in range(p.k):
+            if ros[i, j] >= 0:
+                e = idx[i, j]
+                y[i] += g[i, j] * orc.expert_ffn(X[i:i + 1], np.array([0, 1]), inp["W13"][e:e + 1],
+                                                 inp["W2"][e:e + 1], p.act)[0]
+    if p.F_shared:
+        y += orc.shared_expert(X, inp["Ws13"], inp["Ws2"])
+    return y
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_layer_fwd_parity(name):
+    p, inp, x, w = case(name)
+    saved = B.alloc_saved(p, DEV)
+    y, st = B.layer_fwd(p, w, x, saved=saved, stats=True)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    # routing and dispatch of the layer path are exact given its own indices
+    idx_g = saved["topk_idx"].cpu().numpy().astype(np.int64)
+    C = orc.capacity(p.T, p.E, p.k, p.capacity_factor)
+    counts, offsets, ros, tor = orc.dispatch(idx_g, p.E, C)
+    np.testing.assert_array_equal(saved["row_of_slot"].cpu().numpy(), ros)
+    np.testing.assert_array_equal(saved["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(st["counts"].cpu().numpy(), counts)
+    drops = 0 if C is None else int(np.maximum(counts - C, 0).sum())
+    assert int(st["n_dropped"].cpu()[0]) == drops
+    if p.dtype == "f32":
+        ref = orc.layer_fwd(p, inp)
+        assert np.array_equal(idx_g, ref["idx"])
+        err = np.max(np.abs(y - ref["y"]))
+        rms = np.sqrt(np.mean(ref["y"] ** 2))
+        assert err <= 1e-4 and err <= 1e-4 * rms, (err, rms)
+        return
+    rng = np.random.default_rng(2)
+    tokens = np.unique(np.concatenate([[0, p.T - 1], rng.integers(0, p.T, size=48)]))
+    y_ref = _layer_ref_sampled(p, inp, saved, tokens)
+    r = _assert_bf16_close(y[tokens], y_ref, f"{name} y")
+    print(f"{name}: layer y max-abs/rms {r:.2e} on {len(tokens)} tokens; drops {drops}")
+
+
+@pytest.mark.parametrize("over", [dict(T=200), dict(T=1), dict(k=8, renorm=False),
+                                  dict(E=1, k=1, renorm=False), dict(score="sigmoid", F_shared=64),
+                                  dict(score="sqrt_softplus", act="gelu", T=333, capacity_factor=0.7)])
+def test_layer_fwd_fp32_edge_cases(over):
+    p = presets.get("c1", **over)
+    inp = synth.make_inputs(p, seed=4)
+    x = torch.from_numpy(inp["x"]).to(DEV)
+    w = B.weights_to_device(p, inp, DEV)
+    y = B.layer_fwd(p, w, x)
+    torch.cuda.synchronize()
+    ref = orc.layer_fwd(p, inp)
+    assert not (ref["near_tie"].any() or ref["near_tie_order"].any())
+    err = np.max(np.abs(y.cpu().numpy() - ref["y"]))
+    rms = np.sqrt(np.mean(ref["y"] ** 2))
+    assert err <= 1e-4 and err <= 1e-4 * rms, (err, rms)
+
+
+def test_layer_forced_collapse_drops_to_residual():
+    p = presets.get("c1", T=512, k=1, renorm=False, capacity_factor=1.0)
+    inp = synth.make_inputs(p, seed=6)
+    inp["offset"] = np.array([50.0] + [0.0] * 7, np.float32)
+    x = torch.from_numpy(inp["x"]).to(DEV)
+    w = B.weights_to_device(p, inp, DEV)
+    y, st = B.layer_fwd(p, w, x, stats=True)
+    torch.cuda.synchronize()
+    ref = orc.layer_fwd(p, inp)
+    C = orc.capacity(p.T, p.E, 1, 1.0)
+    assert int(st["n_dropped"].cpu()[0]) == p.T - C
+    y = y.cpu().numpy()
+    assert np.all(y[C:] == 0.0)                   # dropped tokens: residual only
+    assert np.max(np.abs(y - ref["y"])) <= 1e-4
+
+
+def test_zero_tokens_noop():
+    p = presets.get("c2")
+    _, inp, x, w = case("c2")
+    y = B.layer_fwd(p, w, x[:0])
+    torch.cuda.synchronize()
+    assert y.shape == (0, p.d)
+
+
+def test_layer_deterministic_across_runs_and_streams():
+    p, inp, x, w = case("c2")
+    y1 = B.layer_fwd(p, w, x)
+    y2 = B.layer_fwd(p, w, x)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y3 = B.layer_fwd(p, w, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+
+
+def test_bias_update_parity():
+    p = presets.get("c5")
+    rng = np.random.default_rng(9)
+    counts = rng.integers(0, 2 * p.T * p.k // p.E, size=p.E).astype(np.int32)
+    counts[:3] = p.T * p.k // p.E
+    bias = rng.normal(size=p.E).astype(np.float32) * 0.1
+    tb = torch.from_numpy(bias).to(DEV)
+    B.bias_update(torch.from_numpy(counts).to(DEV), tb, p.T * p.k / p.E, p.bias_gamma)
+    torch.cuda.synchronize()
+    ref = orc.bias_update(counts, bias, p.T, p.k, p.bias_gamma)
+    np.testing.assert_allclose(tb.cpu().numpy(), ref, rtol=1e-6, atol=1e-7)
+
+
+def test_native_library_is_loaded():
+    import top_routing_expert_amd
+    L = B.lib()
+    assert os.path.dirname(os.path.abspath(L._name)) == os.path.dirname(top_routing_expert_amd.__file__)
+    maps = open("/proc/self/maps").read()
+    assert "libmoe.so" in maps

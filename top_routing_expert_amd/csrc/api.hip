@@ -1,0 +1,417 @@
+// C ABI of the sparse MoE layer: argument validation, workspace carving and
+// the launch sequence of each entry point on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += (bytes + ALIGN - 1) / ALIGN * ALIGN;
+    return o;
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(const moe_opts* o) { return o->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+int64_t n_up(const moe_opts* o, int64_t F) { return o->act == MOE_ACT_SWIGLU ? 2 * F : F; }
+
+int check_width(const moe_opts* o, int64_t v) {
+  if (v < 1) return MOE_ERR_INVALID_ARG;
+  if (o->dtype == MOE_DTYPE_BF16 ? (v % 128) != 0 : (v % 4) != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_dims(const moe_dims* d, const moe_opts* o) {
+  if (!d || !o) return MOE_ERR_INVALID_ARG;
+  if (o->dtype != MOE_DTYPE_F32 && o->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (o->score < MOE_SCORE_SOFTMAX || o->score > MOE_SCORE_SQRT_SOFTPLUS) return MOE_ERR_INVALID_ARG;
+  if (o->act != MOE_ACT_SWIGLU && o->act != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->E < 1 || d->k < 1 || d->k > d->E || d->F_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(o->gate_scale) || !isfinite(o->capacity_factor) || !isfinite(o->aux_coef) ||
+      !isfinite(o->z_coef))
+    return MOE_ERR_INVALID_ARG;
+  if (d->E > 256 || d->k > 16) return MOE_ERR_UNSUPPORTED;
+  if (d->T * d->k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  int s = check_width(o, d->d);
+  if (s) return s;
+  if ((s = check_width(o, d->F))) return s;
+  if (d->F_shared > 0 && (s = check_width(o, d->F_shared))) return s;
+  return MOE_OK;
+}
+
+int64_t capacity_of(const moe_dims* d, const moe_opts* o) {
+  const double cf = double(o->capacity_factor);
+  if (!(cf > 0.0)) return -1;
+  return int64_t(ceil(cf * double(d->T) * double(d->k) / double(d->E)));
+}
+
+int route_ks(int EP) { return EP == 32 ? 4 : EP == 64 ? 2 : 1; }
+bool route_mfma(const moe_dims* d, const moe_opts* o, int EP) {
+  return o->dtype == MOE_DTYPE_BF16 && d->d % (64 * route_ks(EP)) == 0;
+}
+
+// ---- workspace plans -------------------------------------------------------
+struct RouteWs { size_t wsplit, part_p, part_cnt, part_lse2, part_nf; int nblk, EP; };
+RouteWs plan_route(Carver& c, const moe_dims* d) {
+  RouteWs r;
+  r.EP = route_pad_experts(int(d->E));
+  r.nblk = int(cdiv(d->T, ROUTE_BT));
+  r.wsplit = c.take(size_t(3) * r.EP * d->d * 2);
+  r.part_p = c.take(size_t(r.nblk) * r.EP * 4);
+  r.part_cnt = c.take(size_t(r.nblk) * r.EP * 4);
+  r.part_lse2 = c.take(size_t(r.nblk) * 4);
+  r.part_nf = c.take(size_t(r.nblk) * 4);
+  return r;
+}
+
+struct PermWs { size_t blockcnt, blockbase; int nblk; };
+PermWs plan_perm(Carver& c, const moe_dims* d) {
+  PermWs p;
+  p.nblk = int(cdiv(d->T, DISP_TB));
+  p.blockcnt = c.take(size_t(p.nblk) * d->E * 4);
+  p.blockbase = c.take(size_t(p.nblk) * d->E * 4);
+  return p;
+}
+
+struct FfnWs { size_t tile_up, tile_down, act; };
+FfnWs plan_ffn(Carver& c, int64_t G, int64_t max_rows, int64_t F, int eb, bool need_act) {
+  FfnWs f;
+  f.tile_up = c.take(size_t(G + 1) * 4);
+  f.tile_down = c.take(size_t(G + 1) * 4);
+  f.act = need_act ? c.take(size_t(max_rows) * F * eb) : 0;
+  return f;
+}
+
+struct FwdWs {
+  RouteWs route;
+  PermWs perm;
+  FfnWs ffn, ffn_shared;
+  size_t idx, gate, counts, offsets, ros, tor, xperm, a, o, hs_unused, as, os, shared_off, losses;
+};
+FwdWs plan_fwd(Carver& c, const moe_dims* d, const moe_opts* o) {
+  FwdWs f;
+  const int eb = elem_bytes(o);
+  const int64_t Tk = d->T * d->k;
+  f.route = plan_route(c, d);
+  f.perm = plan_perm(c, d);
+  f.ffn = plan_ffn(c, d->E, Tk, d->F, eb, false);
+  f.ffn_shared = plan_ffn(c, 1, d->T, d->F_shared, eb, false);
+  f.idx = c.take(size_t(Tk) * 4);
+  f.gate = c.take(size_t(Tk) * 4);
+  f.counts = c.take(size_t(d->E) * 4);
+  f.offsets = c.take(size_t(d->E + 1) * 4);
+  f.ros = c.take(size_t(Tk) * 4);
+  f.tor = c.take(size_t(Tk) * 4);
+  f.xperm = c.take(size_t(Tk) * d->d * eb);
+  f.a = c.take(size_t(Tk) * d->F * eb);
+  f.o = c.take(size_t(Tk) * d->d * 4);
+  f.as = c.take(size_t(d->T) * d->F_shared * eb);
+  f.os = c.take(size_t(d->T) * d->d * 4);
+  f.shared_off = c.take(2 * 4);
+  f.losses = c.take(2 * 4);
+  f.hs_unused = 0;
+  return f;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                   \
+  do {                                  \
+    const hipError_t e_ = (expr);       \
+    if (e_ != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+int check_ws(const void* ws, size_t have, size_t need) {
+  if (need > have) return MOE_ERR_WORKSPACE;
+  if (need > 0 && (!ws || (reinterpret_cast<uintptr_t>(ws) % ALIGN) != 0)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// ---- the steps, with validated arguments --------------------------------
+int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* Wg,
+             const float* offset, const float* bias, int32_t* idx, float* gate, float* scores,
+             float* logits, int32_t* counts, float* losses, int32_t* n_nonfinite, void* ws,
+             const RouteWs& rw, hipStream_t st) {
+  RouteArgs a;
+  a.x = x;
+  a.x_bf16 = o->dtype == MOE_DTYPE_BF16;
+  a.Wg = Wg;
+  a.wsplit = at<uint16_t>(ws, rw.wsplit);
+  a.offset = offset;
+  a.bias = bias;
+  a.T = int(d->T);
+  a.d = int(d->d);
+  a.E = int(d->E);
+  a.k = int(d->k);
+  a.EP = rw.EP;
+  a.score = o->score;
+  a.renorm = o->renorm != 0;
+  a.gate_scale = o->gate_scale;
+  a.idx = idx;
+  a.gate = gate;
+  a.scores = scores;
+  a.logits = logits;
+  a.part_p = at<float>(ws, rw.part_p);
+  a.part_cnt = at<int32_t>(ws, rw.part_cnt);
+  a.part_lse2 = at<float>(ws, rw.part_lse2);
+  a.part_nf = at<int32_t>(ws, rw.part_nf);
+  const bool mfma = route_mfma(d, o, rw.EP);
+  if (mfma) MOE_TRY(launch_wg_split(Wg, a.d, a.E, a.EP, at<uint16_t>(ws, rw.wsplit), st));
+  MOE_TRY(launch_route(a, mfma, st));
+  if (counts || losses || n_nonfinite)
+    MOE_TRY(launch_route_reduce(a, rw.nblk, o->aux_coef, o->z_coef, counts, losses, n_nonfinite, st));
+  return MOE_OK;
+}
+
+int do_permute(const moe_dims* d, const moe_opts* o, const void* x, const int32_t* idx,
+               int32_t* counts, int32_t* offsets, int32_t* ros, int32_t* tor, void* xperm,
+               int32_t* n_dropped, void* ws, const PermWs& pw, hipStream_t st) {
+  const int T = int(d->T), k = int(d->k), E = int(d->E);
+  const int64_t C = capacity_of(d, o);
+  int32_t* bc = at<int32_t>(ws, pw.blockcnt);
+  int32_t* bb = at<int32_t>(ws, pw.blockbase);
+  MOE_TRY(launch_dispatch_hist(idx, T, k, E, bc, st));
+  MOE_TRY(launch_dispatch_scan(bc, pw.nblk, E, C, bb, counts, offsets, n_dropped, st));
+  MOE_TRY(launch_dispatch_permute(idx, T, k, E, C, bb, offsets, x, int(d->d), elem_bytes(o), ros,
+                                  tor, xperm, st));
+  return MOE_OK;
+}
+
+int do_ffn(const moe_opts* o, int64_t d, int64_t G, int64_t max_rows, int64_t F, int act,
+           const void* xperm, const int32_t* offsets, const void* W13, const void* W2,
+           void* h_save, void* a_buf, float* out, void* ws, const FfnWs& fw, hipStream_t st) {
+  const bool bf16 = o->dtype == MOE_DTYPE_BF16;
+  const int64_t nu = act == MOE_ACT_SWIGLU ? 2 * F : F;
+  GemmArgs g;
+  g.A = xperm;
+  g.B = W13;
+  g.b_group_stride = nu * d;
+  g.offsets = offsets;
+  g.G = int(G);
+  g.max_rows = max_rows;
+  g.N = int(F);
+  g.K = int(d);
+  g.up_off = act == MOE_ACT_SWIGLU ? int(F) : 0;
+  g.epi = act == MOE_ACT_SWIGLU ? EPI_SWIGLU : EPI_GELU;
+  g.out = a_buf;
+  g.h_save = h_save;
+  g.n_b = int(nu);
+  g.tile_start = at<int32_t>(ws, fw.tile_up);
+  MOE_TRY(bf16 ? launch_grouped_gemm_bf16(g, st) : launch_grouped_gemm_f32(g, st));
+  GemmArgs g2 = g;
+  g2.A = a_buf;
+  g2.B = W2;
+  g2.b_group_stride = d * F;
+  g2.N = int(d);
+  g2.K = int(F);
+  g2.up_off = 0;
+  g2.epi = EPI_STORE_F32;
+  g2.out = out;
+  g2.h_save = nullptr;
+  g2.n_b = 0;
+  g2.tile_start = at<int32_t>(ws, fw.tile_down);
+  MOE_TRY(bf16 ? launch_grouped_gemm_bf16(g2, st) : launch_grouped_gemm_f32(g2, st));
+  return MOE_OK;
+}
+
+hipError_t fill_offsets_1(int32_t* off, int32_t rows, hipStream_t st) {
+  return launch_fill_i32(off, 2, 0, rows, 0, 0, st);
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+const char* moe_strerror(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_capacity(const moe_dims* d, const moe_opts* o, int64_t* C) {
+  if (!d || !o || !C) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->E < 1 || d->k < 1 || !isfinite(o->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  *C = capacity_of(d, o);
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_dims* d, const moe_opts* o, int with_bwd, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const int s = check_dims(d, o);
+  if (s) return s;
+  Carver c;
+  plan_fwd(c, d, o);
+  (void)with_bwd;
+  *bytes = c.off;
+  return MOE_OK;
+}
+
+int moe_route(const moe_dims* d, const moe_opts* o, const void* x, const float* Wg,
+              const float* logit_offset, const float* sel_bias, int32_t* topk_idx,
+              float* topk_gate, float* scores, float* logits, int32_t* counts, float* losses,
+              void* ws, size_t ws_bytes, void* stream) {
+  int s = check_dims(d, o);
+  if (s) return s;
+  if (!x || !Wg || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
+  Carver c;
+  const RouteWs rw = plan_route(c, d);
+  if ((s = check_ws(ws, ws_bytes, c.off))) return s;
+  if (d->T == 0) return MOE_OK;
+  return do_route(d, o, x, Wg, logit_offset, sel_bias, topk_idx, topk_gate, scores, logits, counts,
+                  losses, nullptr, ws, rw, static_cast<hipStream_t>(stream));
+}
+
+int moe_permute(const moe_dims* d, const moe_opts* o, const void* x, const int32_t* topk_idx,
+                int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
+                void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_dims(d, o);
+  if (s) return s;
+  if (!x || !topk_idx || !offsets || !row_of_slot || !token_of_row || !x_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  Carver c;
+  const PermWs pw = plan_perm(c, d);
+  if ((s = check_ws(ws, ws_bytes, c.off))) return s;
+  if (d->T == 0) {
+    // no tokens: every expert is empty
+    return hip_status(launch_zero_i32(offsets, d->E + 1, static_cast<hipStream_t>(stream)));
+  }
+  return do_permute(d, o, x, topk_idx, counts, offsets, row_of_slot, token_of_row, x_perm, nullptr,
+                    ws, pw, static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_ffn(const moe_dims* d, const moe_opts* o, int64_t n_groups, int64_t max_rows,
+                   int64_t F, const void* x_perm, const int32_t* offsets, const void* W13,
+                   const void* W2, void* h_save, void* a_save, float* out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int s = check_dims(d, o);
+  if (s) return s;
+  if (n_groups < 1 || n_groups > 256 || max_rows < 0 || max_rows >= (int64_t(1) << 31))
+    return MOE_ERR_INVALID_ARG;
+  if ((s = check_width(o, F))) return s;
+  if (!x_perm || !offsets || !W13 || !W2 || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(W13) || !aligned16(W2) || !aligned16(out))
+    return MOE_ERR_INVALID_ARG;
+  Carver c;
+  const FfnWs fw = plan_ffn(c, n_groups, max_rows, F, elem_bytes(o), a_save == nullptr);
+  if ((s = check_ws(ws, ws_bytes, c.off))) return s;
+  if (max_rows == 0) return MOE_OK;
+  void* a_buf = a_save ? a_save : at<void>(ws, fw.act);
+  return do_ffn(o, d->d, n_groups, max_rows, F, o->act, x_perm, offsets, W13, W2, h_save, a_buf,
+                out, ws, fw, static_cast<hipStream_t>(stream));
+}
+
+int moe_combine(const moe_dims* d, const float* out_perm, const int32_t* row_of_slot,
+                const float* topk_gate, const float* shared_out, float* y, void* stream) {
+  if (!d || d->T < 0 || d->k < 1 || d->k > 16 || d->d < 4 || d->d % 4) return MOE_ERR_INVALID_ARG;
+  if (!out_perm || !row_of_slot || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(out_perm) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARG;
+  if (d->T == 0) return MOE_OK;
+  return hip_status(launch_combine(out_perm, row_of_slot, topk_gate, shared_out, int(d->T),
+                                   int(d->k), int(d->d), y, static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, const void* x,
+                  float* y, moe_saved* sv, moe_stats* stats, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int s = check_dims(d, o);
+  if (s) return s;
+  if (!w || !x || !y || !w->Wg || !w->W13 || !w->W2) return MOE_ERR_INVALID_ARG;
+  if (d->F_shared > 0 && (!w->Ws13 || !w->Ws2)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(w->W13) || !aligned16(w->W2) ||
+      (d->F_shared > 0 && (!aligned16(w->Ws13) || !aligned16(w->Ws2))))
+    return MOE_ERR_INVALID_ARG;
+  if (sv && (!sv->topk_idx || !sv->topk_gate || !sv->logits || !sv->counts || !sv->offsets ||
+             !sv->row_of_slot || !sv->token_of_row || !sv->x_perm || !sv->h || !sv->a || !sv->o ||
+             !sv->losses || (d->F_shared > 0 && (!sv->h_shared || !sv->a_shared))))
+    return MOE_ERR_INVALID_ARG;
+  if (sv && (!aligned16(sv->x_perm) || !aligned16(sv->o) || !aligned16(sv->a) || !aligned16(sv->h)))
+    return MOE_ERR_INVALID_ARG;
+  Carver c;
+  const FwdWs f = plan_fwd(c, d, o);
+  if ((s = check_ws(ws, ws_bytes, c.off))) return s;
+  if (d->T == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  int32_t* idx = sv ? sv->topk_idx : at<int32_t>(ws, f.idx);
+  float* gate = sv ? sv->topk_gate : at<float>(ws, f.gate);
+  int32_t* counts = sv ? sv->counts : at<int32_t>(ws, f.counts);
+  int32_t* offsets = sv ? sv->offsets : at<int32_t>(ws, f.offsets);
+  int32_t* ros = sv ? sv->row_of_slot : at<int32_t>(ws, f.ros);
+  int32_t* tor = sv ? sv->token_of_row : at<int32_t>(ws, f.tor);
+  void* xperm = sv ? sv->x_perm : at<void>(ws, f.xperm);
+  void* abuf = sv ? sv->a : at<void>(ws, f.a);
+  float* obuf = sv ? sv->o : at<float>(ws, f.o);
+  float* losses = sv ? sv->losses : (stats ? stats->losses : nullptr);
+
+  s = do_route(d, o, x, w->Wg, w->logit_offset, w->sel_bias, idx, gate, nullptr,
+               sv ? sv->logits : nullptr, nullptr, losses, stats ? stats->n_nonfinite : nullptr,
+               ws, f.route, st);
+  if (s) return s;
+  s = do_permute(d, o, x, idx, counts, offsets, ros, tor, xperm, stats ? stats->n_dropped : nullptr,
+                 ws, f.perm, st);
+  if (s) return s;
+  s = do_ffn(o, d->d, d->E, d->T * d->k, d->F, o->act, xperm, offsets, w->W13, w->W2,
+             sv ? sv->h : nullptr, abuf, obuf, ws, f.ffn, st);
+  if (s) return s;
+  float* shared = nullptr;
+  if (d->F_shared > 0) {
+    int32_t* soff = at<int32_t>(ws, f.shared_off);
+    MOE_TRY(fill_offsets_1(soff, int32_t(d->T), st));
+    shared = at<float>(ws, f.os);
+    s = do_ffn(o, d->d, 1, d->T, d->F_shared, MOE_ACT_SWIGLU, x, soff, w->Ws13, w->Ws2,
+               sv ? sv->h_shared : nullptr, sv ? sv->a_shared : at<void>(ws, f.as), shared, ws,
+               f.ffn_shared, st);
+    if (s) return s;
+  }
+  MOE_TRY(launch_combine(obuf, ros, gate, shared, int(d->T), int(d->k), int(d->d), y, st));
+  if (stats) {
+    if (stats->counts) MOE_TRY(hipMemcpyAsync(stats->counts, counts, size_t(d->E) * 4,
+                                              hipMemcpyDeviceToDevice, st));
+    if (stats->losses && stats->losses != losses)
+      MOE_TRY(hipMemcpyAsync(stats->losses, losses, 8, hipMemcpyDeviceToDevice, st));
+  }
+  return MOE_OK;
+}
+
+int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, const void* x,
+                  const moe_saved* sv, const float* dy, float* dx, moe_grads* grads, void* ws,
+                  size_t ws_bytes, void* stream) {
+  (void)d; (void)o; (void)w; (void)x; (void)sv; (void)dy; (void)dx; (void)grads; (void)ws;
+  (void)ws_bytes; (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+int moe_bias_update(const int32_t* counts, float* bias, int64_t E, float target, float gamma,
+                    void* stream) {
+  if (!counts || !bias || E < 1 || E > (int64_t(1) << 30) || !isfinite(target) || !isfinite(gamma))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_bias_update(counts, bias, int(E), target, gamma,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

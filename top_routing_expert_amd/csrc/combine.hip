@@ -1,0 +1,93 @@
+// Weighted unpermute-combine of the sparse MoE layer for gfx950, and the
+// fixed-step selection-bias update.
+//
+// y[t] = sum over kept slots j (slot order) of gate[t,j] * o[row_of_slot[t,j]]
+// + shared[t] ("Mixture of Experts Explained", "What is sparsity?": the
+// gate-weighted sum of expert outputs; dropped slots add nothing, the token
+// travels on through the caller's residual, "MoEs and Transformers").
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// One wave per token; each lane owns 4 consecutive floats per 256-float slab.
+// The slot loop is sequential, so the sum order is fixed.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
+                                                      const int32_t* __restrict__ row_of_slot,
+                                                      const float* __restrict__ gate,
+                                                      const float* __restrict__ shared, int T,
+                                                      int k, int d, float* __restrict__ y) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + w;
+  if (t >= T) return;
+  int rows[16];
+  float gs[16];
+  for (int j = 0; j < 16; ++j) {
+    rows[j] = j < k ? row_of_slot[int64_t(t) * k + j] : -1;
+    gs[j] = j < k ? gate[int64_t(t) * k + j] : 0.0f;
+  }
+  const int nv = d >> 2;
+  for (int c = l; c < nv; c += 64) {
+    float4 acc = shared ? reinterpret_cast<const float4*>(shared + int64_t(t) * d)[c]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      if (rows[j] < 0) continue;
+      const float4 v = reinterpret_cast<const float4*>(o + int64_t(rows[j]) * d)[c];
+      acc.x = fmaf(gs[j], v.x, acc.x);
+      acc.y = fmaf(gs[j], v.y, acc.y);
+      acc.z = fmaf(gs[j], v.z, acc.z);
+      acc.w = fmaf(gs[j], v.w, acc.w);
+    }
+    reinterpret_cast<float4*>(y + int64_t(t) * d)[c] = acc;
+  }
+}
+
+// bias[e] += gamma * sign(target - counts[e]), sign(0) = 0 (handbook news
+// digest, "confirmed": the fixed-step loss-free bias update).
+__global__ void bias_update_kernel(const int32_t* __restrict__ counts, float* __restrict__ bias,
+                                   int E, float target, float gamma) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const float c = float(counts[e]);
+  const float sgn = target > c ? 1.0f : (target < c ? -1.0f : 0.0f);
+  bias[e] = bias[e] + gamma * sgn;
+}
+
+// out[i] = v[i] for i < n (n <= 4): tiny device-side constants (group offsets).
+__global__ void fill_i32_kernel(int32_t* out, int n, int32_t v0, int32_t v1, int32_t v2, int32_t v3) {
+  const int i = threadIdx.x;
+  if (i < n) out[i] = i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3;
+}
+
+__global__ void zero_i32_kernel(int32_t* out, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = 0;
+}
+
+hipError_t launch_fill_i32(int32_t* out, int n, int32_t v0, int32_t v1, int32_t v2, int32_t v3,
+                           hipStream_t st) {
+  fill_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(out, n, v0, v1, v2, v3);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int32_t* out, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  zero_i32_kernel<<<dim3(unsigned(cdiv(n, 256))), dim3(256), 0, st>>>(out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* o, const int32_t* row_of_slot, const float* gate,
+                          const float* shared, int T, int k, int d, float* y, hipStream_t st) {
+  combine_kernel<<<dim3(unsigned(cdiv(T, 4))), dim3(256), 0, st>>>(o, row_of_slot, gate, shared, T,
+                                                                    k, d, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, float target,
+                              float gamma, hipStream_t st) {
+  bias_update_kernel<<<dim3(unsigned(cdiv(E, 256))), dim3(256), 0, st>>>(counts, bias, E, target,
+                                                                          gamma);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,220 @@
+// Dispatch of the sparse MoE layer for gfx950: per-expert histogram, capacity
+// clip and exclusive scan, and a stable (token-order) permutation of the kept
+// slots into expert-contiguous rows with a coalesced copy of the token rows
+// ("Mixture of Experts Explained", "MoEs and Transformers": expert capacity,
+// overflow through the residual; "Switch Transformers": capacity factor).
+//
+// Determinism: the position of a slot inside its expert is its rank by token
+// index, built from per-block counts (scanned in block order), per-wave counts
+// (scanned in wave order) and a ballot/popcount rank inside the wave.  No
+// global atomics decide any order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int DISP_KMAX = 16;
+
+// Per-block histogram of the slots' experts.  LDS atomics only count, so the
+// result is order independent.  Entries outside [0, E) are skipped.
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ idx, int T,
+                                                            int k, int E,
+                                                            int32_t* __restrict__ blockcnt) {
+  __shared__ int32_t hist[256];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * DISP_TB + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[int64_t(t) * k + j];
+      if (unsigned(e) < unsigned(E)) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) blockcnt[int64_t(blockIdx.x) * E + e] = hist[e];
+}
+
+// One block of 256 threads, thread e: exclusive scan of expert e's counts over
+// the blocks, its total, the kept count min(total, C), then an exclusive scan
+// over experts of the kept counts -> offsets.  C < 0: no capacity.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __restrict__ blockcnt,
+                                                            int nblk, int E, int64_t C,
+                                                            int32_t* __restrict__ blockbase,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ n_dropped) {
+  __shared__ int32_t sk[256];
+  __shared__ int32_t sd[256];
+  const int e = threadIdx.x;
+  int32_t total = 0;
+  if (e < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int32_t c = blockcnt[int64_t(b) * E + e];
+      blockbase[int64_t(b) * E + e] = total;
+      total += c;
+    }
+    if (counts) counts[e] = total;
+  }
+  const int32_t kept = (e < E) ? ((C >= 0 && int64_t(total) > C) ? int32_t(C) : total) : 0;
+  sk[e] = kept;
+  sd[e] = (e < E) ? total - kept : 0;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of kept counts and drop counts.
+  for (int s = 1; s < 256; s <<= 1) {
+    const int32_t vk = e >= s ? sk[e - s] : 0;
+    const int32_t vd = e >= s ? sd[e - s] : 0;
+    __syncthreads();
+    sk[e] += vk;
+    sd[e] += vd;
+    __syncthreads();
+  }
+  if (e < E) offsets[e] = sk[e] - kept;
+  if (e == 0) {
+    offsets[E] = sk[255];
+    if (n_dropped) n_dropped[0] = sd[255];
+  }
+}
+
+// Stable ranks and the row copy.  Block b covers tokens [b*256, b*256+256),
+// wave w the 64 tokens from b*256 + 64w, one token per lane.
+//   1. peel: repeatedly take the expert of the first lane with a pending slot,
+//      ballot the lanes holding that expert, rank = popcount of lower lanes;
+//      the leader records the wave's count for the expert;
+//   2. rank in expert = blockbase[b][e] + counts of lower waves + rank in wave;
+//      kept iff rank < C; row = offsets[e] + rank;
+//   3. copy: each wave reads each of its tokens' x row once (16-byte lanes)
+//      and writes it to every kept row of the token.
+template <int KM>
+__global__ __launch_bounds__(256) void dispatch_permute_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int64_t C,
+    const int32_t* __restrict__ blockbase, const int32_t* __restrict__ offsets,
+    const uint8_t* __restrict__ x, int row_bytes, int32_t* __restrict__ row_of_slot,
+    int32_t* __restrict__ token_of_row, uint8_t* __restrict__ x_perm) {
+  __shared__ int32_t wavecnt[4][256];
+  __shared__ int32_t srow[DISP_TB * KM];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  for (int i = tid; i < 4 * 256; i += blockDim.x) (&wavecnt[0][0])[i] = 0;
+  const int t = blockIdx.x * DISP_TB + tid;
+  const bool valid = t < T;
+  int ex[KM];
+  int rk[KM];
+  uint32_t pending = 0;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    ex[j] = -1;
+    rk[j] = 0;
+    if (valid && j < k) {
+      const int e = idx[int64_t(t) * k + j];
+      if (unsigned(e) < unsigned(E)) {
+        ex[j] = e;
+        pending |= 1u << j;
+      }
+    }
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  while (true) {
+    const uint64_t act = __ballot(pending != 0);
+    if (act == 0) break;
+    const int leader = __ffsll(static_cast<unsigned long long>(act)) - 1;
+    int mine = -1;
+    if (pending) {
+      const int j0 = __ffs(pending) - 1;
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (j == j0) mine = ex[j];
+    }
+    const int e = __shfl(mine, leader, 64);
+    int jm = -1;
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if ((pending >> j & 1u) && ex[j] == e) jm = j;
+    const uint64_t m = __ballot(jm >= 0);
+    if (jm >= 0) {
+      const int r = __popcll(m & lt_mask);
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (j == jm) rk[j] = r;
+      pending &= ~(1u << jm);
+    }
+    if (l == leader) wavecnt[w][e] = __popcll(m);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j < k) {
+      int row = -1;
+      const int e = ex[j];
+      if (e >= 0) {
+        int32_t rank = blockbase[int64_t(blockIdx.x) * E + e] + rk[j];
+        for (int ww = 0; ww < w; ++ww) rank += wavecnt[ww][e];
+        if (C < 0 || rank < C) {
+          row = offsets[e] + rank;
+          token_of_row[row] = t;
+        }
+      }
+      srow[tid * KM + j] = row;
+      if (valid) row_of_slot[int64_t(t) * k + j] = row;
+    }
+  }
+  __syncthreads();
+  // Row copy, token-major: the wave owns tokens w*64 .. w*64+63 of the block.
+  const int chunks = row_bytes >> 4;
+  for (int tt = 0; tt < 64; ++tt) {
+    const int tl = w * 64 + tt;
+    const int tok = blockIdx.x * DISP_TB + tl;
+    if (tok >= T) break;
+    int rows[KM];
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      rows[j] = j < k ? srow[tl * KM + j] : -1;
+      any = any || rows[j] >= 0;
+    }
+    if (!any) continue;
+    const uint8_t* src = x + int64_t(tok) * row_bytes;
+    for (int c = l; c < chunks; c += 64) {
+      const uint4 v = ld16(src + 16 * c);
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (rows[j] >= 0) st16(x_perm + int64_t(rows[j]) * row_bytes + 16 * c, v);
+    }
+  }
+}
+
+hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, int32_t* blockcnt,
+                                hipStream_t st) {
+  const unsigned nblk = unsigned(cdiv(T, DISP_TB));
+  dispatch_hist_kernel<<<dim3(nblk), dim3(256), 0, st>>>(idx, T, k, E, blockcnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scan(const int32_t* blockcnt, int nblk, int E, int64_t C,
+                                int32_t* blockbase, int32_t* counts, int32_t* offsets,
+                                int32_t* n_dropped, hipStream_t st) {
+  dispatch_scan_kernel<<<dim3(1), dim3(256), 0, st>>>(blockcnt, nblk, E, C, blockbase, counts,
+                                                      offsets, n_dropped);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int64_t C,
+                                   const int32_t* blockbase, const int32_t* offsets,
+                                   const void* x, int d, int elem_bytes, int32_t* row_of_slot,
+                                   int32_t* token_of_row, void* x_perm, hipStream_t st) {
+  const unsigned nblk = unsigned(cdiv(T, DISP_TB));
+  const int row_bytes = d * elem_bytes;
+  const auto* xs = static_cast<const uint8_t*>(x);
+  auto* xp = static_cast<uint8_t*>(x_perm);
+#define MOE_PERMUTE(KM)                                                                        \
+  dispatch_permute_kernel<KM><<<dim3(nblk), dim3(256), 0, st>>>(                               \
+      idx, T, k, E, C, blockbase, offsets, xs, row_bytes, row_of_slot, token_of_row, xp)
+  if (k <= 1) MOE_PERMUTE(1);
+  else if (k <= 2) MOE_PERMUTE(2);
+  else if (k <= 4) MOE_PERMUTE(4);
+  else if (k <= 8) MOE_PERMUTE(8);
+  else MOE_PERMUTE(16);
+#undef MOE_PERMUTE
+  return hipGetLastError();
+}
+
+}  // namespace moe

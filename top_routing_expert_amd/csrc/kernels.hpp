@@ -1,0 +1,82 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------ router
+struct RouteArgs {
+  const void* x;            // [T, d] bf16 or fp32
+  int x_bf16;
+  const float* Wg;          // [d, E]
+  const uint16_t* wsplit;   // [3][EP][d] bf16 planes of Wg (MFMA path)
+  const float* offset;      // nullable [E]
+  const float* bias;        // nullable [E]
+  int T, d, E, k, EP;
+  int score, renorm;
+  float gate_scale;
+  int32_t* idx;             // [T, k]
+  float* gate;              // [T, k]
+  float* scores;            // nullable [T, E]
+  float* logits;            // nullable [T, E]
+  float* part_p;            // [nblk][EP]  sum_t of scores normalised over E
+  int32_t* part_cnt;        // [nblk][EP]  selections per expert
+  float* part_lse2;         // [nblk]      sum_t logsumexp(z_t)^2
+  int32_t* part_nf;         // [nblk]      tokens with a non-finite logit
+};
+constexpr int ROUTE_BT = 32;   // tokens per route block
+
+int route_pad_experts(int E);  // 32, 64, 128 or 256
+hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, uint16_t* out, hipStream_t st);
+hipError_t launch_route(const RouteArgs& a, bool mfma, hipStream_t st);
+hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, float z_coef,
+                               int32_t* counts, float* losses, int32_t* n_nonfinite,
+                               hipStream_t st);
+
+// ------------------------------------------------------------------ dispatch
+constexpr int DISP_TB = 256;   // tokens per dispatch block
+hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, int32_t* blockcnt,
+                                hipStream_t st);
+hipError_t launch_dispatch_scan(const int32_t* blockcnt, int nblk, int E, int64_t C,
+                                int32_t* blockbase, int32_t* counts, int32_t* offsets,
+                                int32_t* n_dropped, hipStream_t st);
+hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int64_t C,
+                                   const int32_t* blockbase, const int32_t* offsets,
+                                   const void* x, int d, int elem_bytes, int32_t* row_of_slot,
+                                   int32_t* token_of_row, void* x_perm, hipStream_t st);
+
+// ------------------------------------------------------------------ grouped GEMM
+enum Epi { EPI_STORE_F32 = 0, EPI_GELU = 1, EPI_SWIGLU = 2 };
+
+struct GemmArgs {
+  const void* A;            // [rows, K] group-contiguous rows
+  const void* B;            // [G][n_b, K] (K-contiguous, [out, in])
+  int64_t b_group_stride;   // elements between groups of B
+  const int32_t* offsets;   // [G+1] row offsets of the groups
+  int G;
+  int64_t max_rows;
+  int N;                    // output columns (F for activations, d for the down GEMM)
+  int K;
+  int up_off;               // SwiGLU: row offset of the up projection inside B (= F)
+  int epi;
+  void* out;                // [rows, N] bf16/fp32 activation, or fp32 for EPI_STORE_F32
+  void* h_save;             // nullable [rows, n_b] pre-activation
+  int n_b;                  // row length of h_save (2F SwiGLU, F GELU)
+  int32_t* tile_start;      // [G+1] scratch, filled by the planner
+};
+hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st);
+hipError_t launch_grouped_gemm_f32(const GemmArgs& g, hipStream_t st);
+int64_t gemm_tile_bound(int64_t max_rows, int G, int N, bool bf16);
+
+// ------------------------------------------------------------------ combine
+hipError_t launch_combine(const float* o, const int32_t* row_of_slot, const float* gate,
+                          const float* shared, int T, int k, int d, float* y, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* out, int n, int32_t v0, int32_t v1, int32_t v2, int32_t v3,
+                           hipStream_t st);
+hipError_t launch_zero_i32(int32_t* out, int64_t n, hipStream_t st);
+hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, float target,
+                              float gamma, hipStream_t st);
+
+}  // namespace moe

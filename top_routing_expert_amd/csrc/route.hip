@@ -1,0 +1,377 @@
+// Router of the sparse MoE layer for gfx950.
+//
+// z = x . Wg (+ offset) in FP32, scores, selection-only bias, top-k with
+// lowest-index tie-breaking, gates, and per-block partial sums for the load
+// balance and z losses ("Mixture of Experts Explained", "What is sparsity?"
+// gating equations and "Switch Transformers" full-precision router; handbook
+// news digest, "confirmed" bullets on sigmoid / sqrt(softplus) scoring).
+//
+// The logits are an [T, d] x [d, E] contraction.  With bf16 tokens it runs on
+// bf16 MFMA: Wg is split once per call into three bf16 planes whose sum is
+// exactly Wg, so every product x*w is formed exactly and accumulated in FP32.
+// fp32 tokens use a plain FMA loop.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+int route_pad_experts(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256; }
+
+// ---------------------------------------------------------------------------
+// Wg [d, E] fp32 -> three bf16 planes [3][EP][d], expert-major (K-contiguous).
+// hi = rne(w), mid = rne(w - hi), lo = rne(w - hi - mid); each residual is
+// exact in fp32 and the last has at most 8 significant bits, so
+// hi + mid + lo == w for every normal w.  Experts e >= E are zero.
+__global__ void wg_split_kernel(const float* __restrict__ Wg, int d, int E, int EP,
+                                uint16_t* __restrict__ out) {
+  const int64_t n = int64_t(EP) * d;
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int e = int(i / d), kk = int(i % d);
+  const float w = e < E ? Wg[int64_t(kk) * E + e] : 0.0f;
+  const uint16_t hi = f2bf(w);
+  const float r1 = w - bf2f(hi);
+  const uint16_t mid = f2bf(r1);
+  const float r2 = r1 - bf2f(mid);
+  out[i] = hi;
+  out[n + i] = mid;
+  out[2 * n + i] = f2bf(r2);
+}
+
+// ---------------------------------------------------------------------------
+// Per-token epilogue shared by both logit kernels.  zs holds KS partial logit
+// sums for the block's 32 tokens.  Each token is handled by a group of LG
+// lanes, each owning VPL experts e = lane_in_group + LG * v.
+template <int EP, int KS>
+__device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[ROUTE_BT][EP + 1],
+                                               int t0, float* red_p, int32_t* red_c,
+                                               float* red_s) {
+  constexpr int LG = EP < 64 ? EP : 64;
+  constexpr int TPI = 64 / LG;
+  constexpr int VPL = EP / LG;
+  constexpr int KMAX = 16;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int gi = l / LG, lg = l % LG;
+  const int E = a.E, k = a.k;
+
+  float off[VPL], bia[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lg + LG * v;
+    off[v] = (a.offset && e < E) ? a.offset[e] : 0.0f;
+    bia[v] = (a.bias && e < E) ? a.bias[e] : 0.0f;
+  }
+  float pacc[VPL];
+  int32_t cacc[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) { pacc[v] = 0.0f; cacc[v] = 0; }
+  float lse2 = 0.0f;
+  int32_t nf = 0;
+
+  constexpr int TOK_PER_WAVE = ROUTE_BT / 4;
+  for (int it = 0; it < TOK_PER_WAVE / TPI; ++it) {
+    const int tl = w * TOK_PER_WAVE + it * TPI + gi;
+    const int t = t0 + tl;
+    const bool valid = t < a.T;
+    float z[VPL], s[VPL];
+    bool finite = true;
+    float m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lg + LG * v;
+      float zz = 0.0f;
+#pragma unroll
+      for (int q = 0; q < KS; ++q) zz += zs[q][tl][e];
+      zz += off[v];
+      z[v] = zz;
+      if (e < E) {
+        m = fmaxf(m, zz);
+        finite = finite && isfinite(zz);
+      }
+    }
+    m = group_max<LG>(m);
+    float sexp = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (lg + LG * v < E) sexp += expf(z[v] - m);
+    sexp = group_sum<LG>(sexp);
+    float ssum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lg + LG * v;
+      float sv;
+      if (a.score == 0) {
+        sv = expf(z[v] - m) / sexp;
+      } else if (a.score == 1) {
+        sv = 1.0f / (1.0f + expf(-z[v]));
+      } else {
+        sv = sqrtf(fmaxf(z[v], 0.0f) + log1pf(expf(-fabsf(z[v]))));
+      }
+      s[v] = e < E ? sv : 0.0f;
+      ssum += s[v];
+    }
+    ssum = group_sum<LG>(ssum);
+    const float lse = m + logf(sexp);
+
+    uint64_t key[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lg + LG * v;
+      key[v] = e < E ? (uint64_t(order_key(s[v] + bia[v])) << 32) | uint32_t(~uint32_t(e)) : 0ull;
+    }
+    int isel[KMAX];
+    float gsel[KMAX];
+    float gs = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      isel[j] = 0;
+      gsel[j] = 0.0f;
+      if (j < k) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+        best = group_max_u64<LG>(best);
+        const int e = int(~uint32_t(best));
+        float sv = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (lg + LG * v == e) {
+            sv = s[v];
+            key[v] = 0;
+            cacc[v] += valid ? 1 : 0;
+          }
+        const float ge = __shfl(sv, gi * LG + (e % LG), 64);
+        isel[j] = e;
+        gsel[j] = ge;
+        gs += ge;
+      }
+    }
+    if (valid) {
+      const float scale = a.renorm ? a.gate_scale / gs : a.gate_scale;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k && lg == j) {
+          const float g = a.renorm ? (gsel[j] / gs) * a.gate_scale : gsel[j] * a.gate_scale;
+          a.idx[int64_t(t) * k + j] = isel[j];
+          a.gate[int64_t(t) * k + j] = g;
+        }
+      }
+      (void)scale;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int e = lg + LG * v;
+        if (e < E) {
+          if (a.scores) a.scores[int64_t(t) * E + e] = s[v];
+          if (a.logits) a.logits[int64_t(t) * E + e] = z[v];
+          pacc[v] += s[v] / ssum;
+        }
+      }
+      lse2 += lse * lse;
+      nf += finite ? 0 : 1;
+    }
+  }
+  // Combine the groups of a wave, then the four waves, in a fixed order.
+#pragma unroll
+  for (int msk = LG; msk < 64; msk <<= 1) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      pacc[v] += shfl_xor(pacc[v], msk);
+      cacc[v] += shfl_xor(cacc[v], msk);
+    }
+    lse2 += shfl_xor(lse2, msk);
+    nf += shfl_xor(nf, msk);
+  }
+  if (gi == 0) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      red_p[w * EP + lg + LG * v] = pacc[v];
+      red_c[w * EP + lg + LG * v] = cacc[v];
+    }
+  }
+  if (l == 0) {
+    red_s[w] = lse2;
+    red_s[4 + w] = __int_as_float(nf);
+  }
+  __syncthreads();
+  const int blk = blockIdx.x;
+  for (int e = tid; e < EP; e += blockDim.x) {
+    a.part_p[int64_t(blk) * EP + e] = ((red_p[e] + red_p[EP + e]) + red_p[2 * EP + e]) + red_p[3 * EP + e];
+    a.part_cnt[int64_t(blk) * EP + e] = red_c[e] + red_c[EP + e] + red_c[2 * EP + e] + red_c[3 * EP + e];
+  }
+  if (tid == 0) {
+    a.part_lse2[blk] = ((red_s[0] + red_s[1]) + red_s[2]) + red_s[3];
+    a.part_nf[blk] = __float_as_int(red_s[4]) + __float_as_int(red_s[5]) +
+                     __float_as_int(red_s[6]) + __float_as_int(red_s[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 tokens: logits on MFMA 32x32x16.  A block covers 32 tokens and all EP
+// experts in NB = EP/32 output blocks of 32x32.  With fewer than four output
+// blocks the four waves also split d (KS parts), summed in order afterwards.
+// Within a 64-wide K chunk a lane loads 32 contiguous k of its token row (and
+// of its expert row of each Wg plane); MFMA step s uses elements 8s..8s+7 of
+// them, the same permutation of k for both operands.
+template <int EP>
+__global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a) {
+  constexpr int NB = EP / 32;
+  constexpr int KS = NB >= 4 ? 1 : 4 / NB;
+  constexpr int WPK = 4 / KS;
+  constexpr int BPW = NB / WPK;
+  __shared__ float zs[KS][ROUTE_BT][EP + 1];
+  __shared__ float red_p[4 * EP];
+  __shared__ int32_t red_c[4 * EP];
+  __shared__ float red_s[8];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int t0 = blockIdx.x * ROUTE_BT;
+  const int kp = w / WPK, wb = w % WPK;
+  const int dpart = a.d / KS;
+  const int row = l & 31, g = l >> 5;
+  const int trow = min(t0 + row, a.T - 1);
+  const uint16_t* xr = static_cast<const uint16_t*>(a.x) + int64_t(trow) * a.d + kp * dpart + 32 * g;
+  const int64_t plane = int64_t(EP) * a.d;
+
+  floatx16 acc[BPW];
+#pragma unroll
+  for (int b = 0; b < BPW; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+
+  for (int kc = 0; kc < dpart; kc += 64) {
+    uint4 xa[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xa[q] = ld16(xr + kc + 8 * q);
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+      const int eb = wb + b * WPK;
+      const uint16_t* wr = a.wsplit + int64_t(eb * 32 + row) * a.d + kp * dpart + 32 * g + kc;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        uint4 wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wv[q] = ld16(wr + p * plane + 8 * q);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, xa[s]), __builtin_bit_cast(bf16x8, wv[s]), acc[b], 0, 0, 0);
+      }
+    }
+  }
+  // D[i][j] of a 32x32 block: lane l holds column j = l%32 and rows
+  // i = 8*(r/4) + 4*(l/32) + r%4 in accumulator register r.
+#pragma unroll
+  for (int b = 0; b < BPW; ++b) {
+    const int eb = wb + b * WPK;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zs[kp][8 * (r >> 2) + 4 * g + (r & 3)][eb * 32 + row] = acc[b][r];
+  }
+  __syncthreads();
+  route_epilogue<EP, KS>(a, zs, t0, red_p, red_c, red_s);
+}
+
+// ---------------------------------------------------------------------------
+// Plain FMA logits (fp32 tokens, or shapes the MFMA tiling does not cover).
+template <int EP>
+__global__ __launch_bounds__(256) void route_simt_kernel(RouteArgs a) {
+  __shared__ float zs[1][ROUTE_BT][EP + 1];
+  __shared__ float red_p[4 * EP];
+  __shared__ int32_t red_c[4 * EP];
+  __shared__ float red_s[8];
+  const int t0 = blockIdx.x * ROUTE_BT;
+  for (int o = threadIdx.x; o < ROUTE_BT * EP; o += blockDim.x) {
+    const int tl = o / EP, e = o % EP;
+    const int t = min(t0 + tl, a.T - 1);
+    float acc = 0.0f;
+    if (e < a.E) {
+      if (a.x_bf16) {
+        const uint16_t* xr = static_cast<const uint16_t*>(a.x) + int64_t(t) * a.d;
+        for (int kk = 0; kk < a.d; ++kk) acc = fmaf(bf2f(xr[kk]), a.Wg[int64_t(kk) * a.E + e], acc);
+      } else {
+        const float* xr = static_cast<const float*>(a.x) + int64_t(t) * a.d;
+        for (int kk = 0; kk < a.d; ++kk) acc = fmaf(xr[kk], a.Wg[int64_t(kk) * a.E + e], acc);
+      }
+    }
+    zs[0][tl][e] = acc;
+  }
+  __syncthreads();
+  route_epilogue<EP, 1>(a, zs, t0, red_p, red_c, red_s);
+}
+
+// ---------------------------------------------------------------------------
+// One block: per-expert totals over the route blocks, in block order, and the
+// two losses.  L_aux = aux_coef * E * sum_e (count_e / (T k)) * (P_e / T);
+// L_z = z_coef * sum_t lse_t^2 / T.  Reductions in double, fixed order.
+__global__ __launch_bounds__(256) void route_reduce_kernel(RouteArgs a, int nblk, float aux_coef,
+                                                           float z_coef, int32_t* counts,
+                                                           float* losses, int32_t* n_nonfinite) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  double term = 0.0;
+  if (tid < a.E) {
+    double P = 0.0;
+    int64_t c = 0;
+    for (int b = 0; b < nblk; ++b) {
+      P += double(a.part_p[int64_t(b) * a.EP + tid]);
+      c += a.part_cnt[int64_t(b) * a.EP + tid];
+    }
+    if (counts) counts[tid] = int32_t(c);
+    term = (double(c) / (double(a.T) * a.k)) * (P / a.T);
+  }
+  red[tid] = term;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    double l2 = 0.0;
+    int64_t nf = 0;
+    for (int b = 0; b < nblk; ++b) {
+      l2 += double(a.part_lse2[b]);
+      nf += a.part_nf[b];
+    }
+    if (losses) {
+      losses[0] = aux_coef != 0.0f ? float(double(aux_coef) * a.E * red[0]) : 0.0f;
+      losses[1] = z_coef != 0.0f ? float(double(z_coef) * l2 / a.T) : 0.0f;
+    }
+    if (n_nonfinite) n_nonfinite[0] = int32_t(nf);
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, uint16_t* out, hipStream_t st) {
+  const int64_t n = int64_t(EP) * d;
+  wg_split_kernel<<<dim3(unsigned(cdiv(n, 256))), dim3(256), 0, st>>>(Wg, d, E, EP, out);
+  return hipGetLastError();
+}
+
+template <int EP>
+static void launch_route_ep(const RouteArgs& a, bool mfma, hipStream_t st) {
+  const unsigned nblk = unsigned(cdiv(a.T, ROUTE_BT));
+  if (mfma)
+    route_mfma_kernel<EP><<<dim3(nblk), dim3(256), 0, st>>>(a);
+  else
+    route_simt_kernel<EP><<<dim3(nblk), dim3(256), 0, st>>>(a);
+}
+
+hipError_t launch_route(const RouteArgs& a, bool mfma, hipStream_t st) {
+  switch (a.EP) {
+    case 32: launch_route_ep<32>(a, mfma, st); break;
+    case 64: launch_route_ep<64>(a, mfma, st); break;
+    case 128: launch_route_ep<128>(a, mfma, st); break;
+    case 256: launch_route_ep<256>(a, mfma, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, float z_coef,
+                               int32_t* counts, float* losses, int32_t* n_nonfinite,
+                               hipStream_t st) {
+  route_reduce_kernel<<<dim3(1), dim3(256), 0, st>>>(a, nblk, aux_coef, z_coef, counts, losses,
+                                                     n_nonfinite);
+  return hipGetLastError();
+}
+
+}  // namespace moe

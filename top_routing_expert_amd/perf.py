@@ -1,0 +1,66 @@
+"""Algorithmic work of each step of the MoE layer (FLOPs and HBM bytes).
+
+Only real work is counted: kept rows R (not tile padding), weights of experts
+that received at least one row, each tensor read or written once.  These are
+the figures the roofline fractions are computed from.
+
+Peaks of one MI355X (AMD's published dense figures): HBM3E 8 TB/s; bf16 MFMA
+2.5 PFLOP/s; fp32 vector 157.3 TFLOP/s (packed), 78.6 TFLOP/s without packed
+FP32 instructions.
+"""
+
+from __future__ import annotations
+
+from .presets import Preset
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+
+
+def eb(p: Preset) -> int:
+    return 2 if p.dtype == "bf16" else 4
+
+
+def n_mats(p: Preset) -> int:
+    """Matrices per expert: gate, up, down for SwiGLU; up, down for GELU."""
+    return 3 if p.act == "swiglu" else 2
+
+
+def ffn_flops(p: Preset, R: int, shared: bool = True) -> float:
+    f = 2.0 * n_mats(p) * p.d * p.F * R
+    if shared and p.F_shared:
+        f += 2.0 * 3 * p.d * p.F_shared * p.T
+    return f
+
+
+def ffn_bytes(p: Preset, R: int, active_experts: int, shared: bool = True) -> float:
+    """Routed expert FFN: weights of active experts, x_perm read, activation
+    written then read (x dtype), fp32 output written."""
+    b = active_experts * n_mats(p) * p.d * p.F * eb(p)
+    b += R * p.d * eb(p) + 2 * R * p.F * eb(p) + R * p.d * 4
+    if shared and p.F_shared:
+        b += 3 * p.d * p.F_shared * eb(p) + p.T * p.d * eb(p) + 2 * p.T * p.F_shared * eb(p) + p.T * p.d * 4
+    return float(b)
+
+
+def route_flops(p: Preset) -> float:
+    return 2.0 * p.T * p.d * p.E
+
+
+def route_bytes(p: Preset) -> float:
+    """x read once, Wg read once, indices and gates written."""
+    return float(p.T * p.d * eb(p) + p.d * p.E * 4 + p.T * p.k * 8)
+
+
+def permute_bytes(p: Preset, R: int) -> float:
+    """x read once, R rows written, indices read, slot/row maps written."""
+    return float(p.T * p.d * eb(p) + R * p.d * eb(p) + p.T * p.k * 8 + R * 4)
+
+
+def combine_bytes(p: Preset, R: int) -> float:
+    """fp32 expert rows read once, y written, gates and rows read (+ shared)."""
+    b = R * p.d * 4 + p.T * p.d * 4 + p.T * p.k * 8
+    if p.F_shared:
+        b += p.T * p.d * 4
+    return float(b)
