@@ -41,7 +41,8 @@
  *     initialisation and are clobbered.
  *   - Errors are returned synchronously as moe_status before anything is
  *     enqueued; MOE_ERR_HIP reports a failed launch.  T = 0 is a successful
- *     no-op.  Results are bitwise deterministic for identical inputs.
+ *     no-op (nothing is read, pointers may be NULL; moe_permute still
+ *     zeroes offsets).  Results are bitwise deterministic for identical inputs.
  */
 #ifndef MOE_H_
 #define MOE_H_

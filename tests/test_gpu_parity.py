@@ -72,7 +72,12 @@ def test_route_parity(name):
                     inp["sel_bias"], p.aux_coef, p.z_coef)
     idx_g, nflip = check_route(p, out, ref)
     np.testing.assert_allclose(out["scores"].cpu().numpy(), ref["s"], rtol=1e-5, atol=1e-12)
-    np.testing.assert_allclose(out["logits"].cpu().numpy(), ref["z"], rtol=1e-5, atol=1e-6)
+    # logits: FP32 accumulation of exact products; forward error bound
+    # |dz| <= c * u * sum_i |x_i w_ie| with u = 2^-24 and c ~ log2(d) for a tree /
+    # blocked sum: allow 2e-6 * sum|x||w| (c = 33).
+    cond = np.abs(inp["x"]).astype(np.float64) @ np.abs(inp["Wg"]).astype(np.float64)
+    dz = np.abs(out["logits"].cpu().numpy() - ref["z"])
+    assert np.all(dz <= 2e-6 * cond + 1e-7), float(np.max(dz / (cond + 1e-30)))
     counts = out["counts"].cpu().numpy()
     np.testing.assert_array_equal(counts, np.bincount(idx_g.ravel(), minlength=p.E))
     # losses: the oracle's formula evaluated with the GPU's (tie-resolved) counts

@@ -274,6 +274,7 @@ int moe_route(const moe_dims* d, const moe_opts* o, const void* x, const float* 
               void* ws, size_t ws_bytes, void* stream) {
   int s = check_dims(d, o);
   if (s) return s;
+  if (d->T == 0) return MOE_OK;
   if (!x || !Wg || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
   Carver c;
@@ -327,6 +328,7 @@ int moe_expert_ffn(const moe_dims* d, const moe_opts* o, int64_t n_groups, int64
 int moe_combine(const moe_dims* d, const float* out_perm, const int32_t* row_of_slot,
                 const float* topk_gate, const float* shared_out, float* y, void* stream) {
   if (!d || d->T < 0 || d->k < 1 || d->k > 16 || d->d < 4 || d->d % 4) return MOE_ERR_INVALID_ARG;
+  if (d->T == 0) return MOE_OK;
   if (!out_perm || !row_of_slot || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(out_perm) || !aligned16(y) || (shared_out && !aligned16(shared_out)))
     return MOE_ERR_INVALID_ARG;
@@ -340,6 +342,7 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
                   void* stream) {
   int s = check_dims(d, o);
   if (s) return s;
+  if (d->T == 0) return MOE_OK;
   if (!w || !x || !y || !w->Wg || !w->W13 || !w->W2) return MOE_ERR_INVALID_ARG;
   if (d->F_shared > 0 && (!w->Ws13 || !w->Ws2)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(y) || !aligned16(w->W13) || !aligned16(w->W2) ||
