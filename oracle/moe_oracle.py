@@ -62,6 +62,7 @@ __all__ = [
     "capacity", "router_logits", "score", "select_topk", "near_tie_flags", "gates",
     "logsumexp_rows", "router_losses", "route", "dispatch", "permute", "silu", "gelu",
     "expert_ffn", "shared_expert", "combine", "bias_update", "layer_fwd", "layer_bwd",
+    "router_bwd", "expert_bwd",
     "NEAR_TIE_REL",
 ]
 
@@ -352,7 +353,7 @@ def layer_fwd(p, inp, keep_hidden: bool = False):
     return out
 
 
-def _ffn_bwd(X, h, a, W13e, W2e, dO, act):
+def expert_bwd(X, h, a, W13e, W2e, dO, act):
     """Backward of o = act(X W13^T) W2^T for one expert; returns dX, dW13, dW2."""
     dA = dO @ np.asarray(W2e, F64)
     dW2 = dO.T @ a
@@ -369,6 +370,51 @@ def _ffn_bwd(X, h, a, W13e, W2e, dO, act):
     dX = dH @ np.asarray(W13e, F64)
     dW13 = dH.T @ np.asarray(X, F64)
     return dX, dW13, dW2
+
+
+def router_bwd(p, s, z, idx, counts, dg):
+    """Gradient of <dy, y> + L_aux + L_z with respect to the router logits z,
+    given dg [T,k] = d<dy,y>/d(gate) of the kept gates.  The gradient reaches
+    the router only through the kept gates and the two losses; idx, the
+    pre-drop counts (hence f_e) and the selection bias are constants."""
+    s = np.asarray(s, F64)
+    z = np.asarray(z, F64)
+    dg = np.asarray(dg, F64)
+    T, E = s.shape
+    k = idx.shape[1]
+    # gates -> scores
+    scale = float(np.float32(p.gate_scale))
+    ssel = np.take_along_axis(s, idx, axis=1)
+    if p.renorm:
+        S = ssel.sum(axis=1, keepdims=True)
+        ghat = ssel / S
+        dsel = scale / S * (dg - np.sum(dg * ghat, axis=1, keepdims=True))
+    else:
+        dsel = scale * dg
+    ds = np.zeros((T, E), F64)
+    np.put_along_axis(ds, idx, dsel, axis=1)      # idx rows are distinct experts
+    aux_coef = float(np.float32(p.aux_coef))
+    if aux_coef != 0.0:
+        f = np.asarray(counts, F64) / (T * k)
+        c = aux_coef * E * f / T                   # dL_aux / dp_hat_te
+        Ssum = s.sum(axis=1, keepdims=True)
+        p_hat = s / Ssum
+        ds += (c[None, :] - np.sum(p_hat * c[None, :], axis=1, keepdims=True)) / Ssum
+    # scores -> logits
+    if p.score == "softmax":
+        dz = s * (ds - np.sum(ds * s, axis=1, keepdims=True))
+    elif p.score == "sigmoid":
+        dz = ds * s * (1.0 - s)
+    else:
+        sig = 1.0 / (1.0 + np.exp(-z))
+        safe = np.where(s > 0, s, 1.0)
+        dz = ds * np.where(s > 0, sig / (2.0 * safe), 0.5 * np.exp(0.5 * z))
+    z_coef = float(np.float32(p.z_coef))
+    if z_coef != 0.0:
+        lse = logsumexp_rows(z)
+        sm = np.exp(z - lse[:, None])
+        dz += 2.0 * z_coef / T * lse[:, None] * sm
+    return dz
 
 
 def layer_bwd(p, inp, fwd, dy):
@@ -403,7 +449,7 @@ def layer_bwd(p, inp, fwd, dy):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 == r0:
             continue
-        dX, dW13[e], dW2[e] = _ffn_bwd(fwd["x_perm"][r0:r1], fwd["h"][e], fwd["a"][e],
+        dX, dW13[e], dW2[e] = expert_bwd(fwd["x_perm"][r0:r1], fwd["h"][e], fwd["a"][e],
                                        inp["W13"][e], inp["W2"][e], dO[r0:r1], p.act)
         dXp[r0:r1] = dX
     dx = np.zeros((T, d), F64)
@@ -412,42 +458,10 @@ def layer_bwd(p, inp, fwd, dy):
         dx[kept] += dXp[row_of_slot[kept, j]]
     dWs13 = dWs2 = None
     if p.F_shared > 0:
-        dxs, dWs13, dWs2 = _ffn_bwd(x, fwd["shared_h"], fwd["shared_a"], inp["Ws13"],
+        dxs, dWs13, dWs2 = expert_bwd(x, fwd["shared_h"], fwd["shared_a"], inp["Ws13"],
                                     inp["Ws2"], dy, "swiglu")
         dx += dxs
-    # router backward: gates -> scores
-    s, z, idx = fwd["s"], fwd["z"], fwd["idx"]
-    scale = float(np.float32(p.gate_scale))
-    ssel = np.take_along_axis(s, idx, axis=1)
-    if p.renorm:
-        S = ssel.sum(axis=1, keepdims=True)
-        ghat = ssel / S
-        dsel = scale / S * (dg - np.sum(dg * ghat, axis=1, keepdims=True))
-    else:
-        dsel = scale * dg
-    ds = np.zeros((T, E), F64)
-    np.put_along_axis(ds, idx, dsel, axis=1)      # idx rows are distinct experts
-    aux_coef = float(np.float32(p.aux_coef))
-    if aux_coef != 0.0:
-        f = fwd["counts"] / (T * k)
-        c = aux_coef * E * f / T                   # dL_aux / dp_hat_te
-        Ssum = s.sum(axis=1, keepdims=True)
-        p_hat = s / Ssum
-        ds += (c[None, :] - np.sum(p_hat * c[None, :], axis=1, keepdims=True)) / Ssum
-    # scores -> logits
-    if p.score == "softmax":
-        dz = s * (ds - np.sum(ds * s, axis=1, keepdims=True))
-    elif p.score == "sigmoid":
-        dz = ds * s * (1.0 - s)
-    else:
-        sig = 1.0 / (1.0 + np.exp(-z))
-        safe = np.where(s > 0, s, 1.0)
-        dz = ds * np.where(s > 0, sig / (2.0 * safe), 0.5 * np.exp(0.5 * z))
-    z_coef = float(np.float32(p.z_coef))
-    if z_coef != 0.0:
-        lse = logsumexp_rows(z)
-        sm = np.exp(z - lse[:, None])
-        dz += 2.0 * z_coef / T * lse[:, None] * sm
+    dz = router_bwd(p, fwd["s"], fwd["z"], fwd["idx"], fwd["counts"], dg)
     dWg = x.T @ dz
     dx += dz @ np.asarray(inp["Wg"], F64).T
     return dict(dx=dx, dWg=dWg, dW13=dW13, dW2=dW2, dWs13=dWs13, dWs2=dWs2,

@@ -1,0 +1,187 @@
+"""GPU parity of the layer backward (moe_layer_bwd through the C ABI) against
+the CPU oracle.
+
+fp32 layers: every gradient is compared in full with the oracle's chain rule,
+max-abs error <= 1e-4 * RMS(reference) (+1e-7).
+
+c5 training shape (bf16 experts, FP32 router), step-wise on the GPU's own
+routing.  The bf16 path stores dO = g*dy, the pre-activation h, the
+activation a and dH in bf16 (round-to-nearest, relative error <= 2^-9 each)
+and accumulates every product in fp32.  A gradient entry sum_r u_r v_r built
+from such factors is off by at most a few of these roundings per term, so the
+bar is elementwise:
+    |got - ref| <= 2^-6 * (|U|^T |V|)   (the sum of absolute terms),
+plus an RMS-level check  rms(got - ref) <= 1e-2 * rms(ref).
+(A flat max-abs <= 2e-2 * rms bar is wrong for experts with a handful of rows:
+replaying the bf16 roundings in fp64 gives 6.9% for a 7-row expert.)
+dWg (fp32 router, reduction over T in fp32) keeps max-abs <= 2e-2 * rms.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from top_routing_expert_amd import binding as B, presets, synth
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+BF16_BOUND = 2.0 ** -6
+
+
+def _train(p, inp):
+    x = torch.from_numpy(inp["x"]).to(DEV).to(B.TORCH_DTYPE[p.dtype]).contiguous()
+    w = B.weights_to_device(p, inp, DEV)
+    saved = B.alloc_saved(p, DEV)
+    ws = B.Workspace(DEV)
+    y = B.layer_fwd(p, w, x, saved=saved, ws=ws)
+    dy = torch.from_numpy(inp["dy"]).to(DEV)
+    g = B.layer_bwd(p, w, x, saved, dy, ws=ws)
+    torch.cuda.synchronize()
+    return x, w, saved, y, g
+
+
+def _close(got, ref, rel, what):
+    got = np.asarray(got, np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert err <= rel * rms + 1e-7, f"{what}: max-abs {err:.3e} vs {rel} * rms {rms:.3e}"
+    return err / max(rms, 1e-30)
+
+
+def _bounded(got, ref, cond, what):
+    """Elementwise bound BF16_BOUND * cond and an RMS-level check."""
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    worst = float(np.max(err / (BF16_BOUND * cond + 1e-6 * rms + 1e-30)))
+    assert worst <= 1.0, f"{what}: error exceeds 2^-6 * sum|terms| by {worst:.2f}x"
+    rel_rms = float(np.sqrt(np.mean(err ** 2))) / max(rms, 1e-30)
+    assert rel_rms <= 1e-2, f"{what}: rms error {rel_rms:.3e} of rms(ref)"
+    return rel_rms
+
+
+@pytest.mark.parametrize("over", [
+    dict(),
+    dict(act="gelu"),
+    dict(score="sigmoid", F_shared=64, aux_coef=0.1, z_coef=0.05, sel_bias_std=0.1, zipf_s=1.1,
+         gate_scale=math.sqrt(2.0)),
+    dict(score="sqrt_softplus", capacity_factor=0.8, aux_coef=0.1, z_coef=0.1, F_shared=128,
+         gate_scale=math.sqrt(2.0)),
+    dict(T=333, k=3, aux_coef=0.05),
+    dict(renorm=False, k=1, z_coef=0.2),
+])
+def test_layer_bwd_fp32(over):
+    p = presets.get("c1", train=True, **over)
+    inp = synth.make_inputs(p, seed=5, with_dy=True)
+    fk = orc.layer_fwd(p, inp, keep_hidden=True)
+    assert not (fk["near_tie"].any() or fk["near_tie_order"].any())
+    ref = orc.layer_bwd(p, inp, fk, inp["dy"])
+    _, _, saved, y, g = _train(p, inp)
+    np.testing.assert_array_equal(saved["topk_idx"].cpu().numpy(), fk["idx"])
+    for name in ("dx", "dWg", "dW13", "dW2") + (("dWs13", "dWs2") if p.F_shared else ()):
+        _close(g[name].cpu().numpy(), ref[name], 1e-4, name)
+
+
+def _swiglu_bwd_terms(X, W13e, W2e, dO, F):
+    """Oracle expert backward, plus the magnitudes that carry the bf16
+    roundings into dH (for the error bounds) and |a|.
+
+    dA = dO W2 can cancel, so its rounding error scales with |dO| |W2|; the
+    rounding of the saved pre-activation h moves the activation factors by
+    their derivative: dsilu(h) by h * dsilu'(h) (dsilu has a zero near
+    h = -2.4), silu(h) by h * dsilu(h)."""
+    h = X @ W13e.T
+    a = orc.silu(h[:, :F]) * h[:, F:]
+    dX, dW13, dW2 = orc.expert_bwd(X, h, a, W13e, W2e, dO, "swiglu")
+    hg, hu = h[:, :F], h[:, F:]
+    sg = 1.0 / (1.0 + np.exp(-hg))
+    ds = sg * (1 + hg * (1 - sg))
+    dds = sg * (1 - sg) * (2 + hg * (1 - 2 * sg))
+    cA = np.abs(dO) @ np.abs(W2e)
+    adH = np.concatenate([cA * np.abs(hu) * (np.abs(ds) + np.abs(hg * dds)),
+                          cA * (np.abs(hg * sg) + np.abs(hg * ds))], 1)
+    return dX, dW13, dW2, adH, np.abs(a)
+
+
+def test_layer_bwd_c5_full_size():
+    p = presets.get("c5")
+    print("[c5 bwd] generating inputs", flush=True)
+    inp = synth.make_inputs(p, seed=0, with_dy=True)
+    x, w, saved, y, g = _train(p, inp)
+    print("[c5 bwd] GPU done; oracle steps", flush=True)
+    T, k, E, d, F = p.T, p.k, p.E, p.d, p.F
+    idx = saved["topk_idx"].cpu().numpy().astype(np.int64)
+    ros = saved["row_of_slot"].cpu().numpy().astype(np.int64)
+    offsets = saved["offsets"].cpu().numpy().astype(np.int64)
+    counts = saved["counts"].cpu().numpy()
+    gate = saved["topk_gate"].cpu().numpy().astype(np.float64)
+    o = saved["o"].cpu().numpy()
+    R = int(offsets[-1])
+    tor = saved["token_of_row"].cpu().numpy()[:R].astype(np.int64)
+    slot_of_row = np.zeros(R, np.int64)
+    kept = ros >= 0
+    slot_of_row[ros[kept]] = np.nonzero(kept)[1]
+    X64 = inp["x"].astype(np.float64)
+    dy = inp["dy"].astype(np.float64)
+
+    # router gradient, step-wise on the GPU's routing and expert outputs
+    r = orc.route(inp["x"], inp["Wg"], k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                  inp["sel_bias"])
+    dg = np.zeros((T, k))
+    for j in range(k):
+        m = ros[:, j] >= 0
+        dg[m, j] = np.sum(dy[m] * o[ros[m, j]], axis=1)
+    dz = orc.router_bwd(p, r["s"], r["z"], idx, counts, dg)
+    e1 = _close(g["dWg"].cpu().numpy(), X64.T @ dz, 2e-2, "dWg")
+
+    # sampled experts: hottest, median, last, and empty ones
+    sizes = np.diff(offsets)
+    order = np.argsort(sizes)
+    sample = sorted(set([int(order[-1]), int(order[len(order) // 2]), E - 1] +
+                        [int(e) for e in np.nonzero(sizes == 0)[0][:2]]))
+    dW13 = g["dW13"]
+    dW2 = g["dW2"]
+    for e in sample:
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        got13 = dW13[e].cpu().numpy()
+        got2 = dW2[e].cpu().numpy()
+        if r1 == r0:
+            assert not got13.any() and not got2.any(), f"empty expert {e} must have zero grads"
+            continue
+        toks = tor[r0:r1]
+        Xe = X64[toks]
+        dO = gate[toks, slot_of_row[r0:r1], None] * dy[toks]
+        _, dW13_ref, dW2_ref, adH, aa = _swiglu_bwd_terms(
+            Xe, inp["W13"][e].astype(np.float64), inp["W2"][e].astype(np.float64), dO, F)
+        _bounded(got13, dW13_ref, adH.T @ np.abs(Xe), f"dW13[{e}]")
+        _bounded(got2, dW2_ref, np.abs(dO).T @ aa, f"dW2[{e}]")
+    print(f"[c5 bwd] experts {sample} sizes {[int(sizes[e]) for e in sample]}", flush=True)
+
+    # shared expert, full
+    Ws13 = inp["Ws13"].astype(np.float64)
+    Ws2 = inp["Ws2"].astype(np.float64)
+    dxs_ref, dWs13_ref, dWs2_ref, adHs, aas = _swiglu_bwd_terms(X64, Ws13, Ws2, dy, p.F_shared)
+    _bounded(g["dWs13"].cpu().numpy(), dWs13_ref, adHs.T @ np.abs(X64), "dWs13")
+    _bounded(g["dWs2"].cpu().numpy(), dWs2_ref, np.abs(dy).T @ aas, "dWs2")
+
+    # dx on sampled tokens: each kept slot's expert backward for that one row
+    dx = g["dx"].cpu().numpy()
+    Wg = inp["Wg"].astype(np.float64)
+    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).integers(0, T, 30)]))
+    ref = dxs_ref[toks] + dz[toks] @ Wg.T
+    cond = adHs[toks] @ np.abs(Ws13) + np.abs(dz[toks]) @ np.abs(Wg.T)
+    for i, t in enumerate(toks):
+        for j in range(k):
+            if ros[t, j] < 0:
+                continue
+            e = int(idx[t, j])
+            W13e = inp["W13"][e].astype(np.float64)
+            dX, _, _, adH, _ = _swiglu_bwd_terms(X64[t:t + 1], W13e, inp["W2"][e].astype(np.float64),
+                                                 gate[t, j] * dy[t:t + 1], F)
+            ref[i] += dX[0]
+            cond[i] += (adH @ np.abs(W13e))[0]
+    e2 = _bounded(dx[toks], ref, cond, "dx")
+    print(f"[c5 bwd] dWg err/rms {e1:.2e}, dx rms-err/rms {e2:.2e} on {len(toks)} tokens")

@@ -58,7 +58,8 @@ int64_t capacity_of(const moe_dims* d, const moe_opts* o) {
   return int64_t(ceil(cf * double(d->T) * double(d->k) / double(d->E)));
 }
 
-int route_ks(int EP) { return EP == 32 ? 4 : EP == 64 ? 2 : 1; }
+// d-split of the MFMA router (8 waves over EP/32 output blocks).
+int route_ks(int EP) { return 256 / EP; }
 bool route_mfma(const moe_dims* d, const moe_opts* o, int EP) {
   return o->dtype == MOE_DTYPE_BF16 && d->d % (64 * route_ks(EP)) == 0;
 }
@@ -148,7 +149,7 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
              const float* offset, const float* bias, int32_t* idx, float* gate, float* scores,
              float* logits, int32_t* counts, float* losses, int32_t* n_nonfinite, void* ws,
              const RouteWs& rw, hipStream_t st) {
-  RouteArgs a;
+  RouteArgs a{};
   a.x = x;
   a.x_bf16 = o->dtype == MOE_DTYPE_BF16;
   a.Wg = Wg;
@@ -198,7 +199,7 @@ int do_ffn(const moe_opts* o, int64_t d, int64_t G, int64_t max_rows, int64_t F,
            void* h_save, void* a_buf, float* out, void* ws, const FfnWs& fw, hipStream_t st) {
   const bool bf16 = o->dtype == MOE_DTYPE_BF16;
   const int64_t nu = act == MOE_ACT_SWIGLU ? 2 * F : F;
-  GemmArgs g;
+  GemmArgs g{};
   g.A = xperm;
   g.B = W13;
   g.b_group_stride = nu * d;
@@ -234,6 +235,72 @@ hipError_t fill_offsets_1(int32_t* off, int32_t rows, hipStream_t st) {
   return launch_fill_i32(off, 2, 0, rows, 0, 0, st);
 }
 
+// ---- backward workspace ------------------------------------------------------
+constexpr int DWG_SPLIT = 16;   // k-chunks of the T-reduction of dWg
+
+int64_t padded_rows(int64_t rows, int64_t G) { return cdiv(rows, 64) * 64 + 64 * G; }
+
+struct BwdWs {
+  FfnWs ffn, ffn_s;
+  size_t dO, dg, dH, dXp, W2T, W13T, dOT, aT, dHT, xpT, dz, dwg_part, dxr;
+  size_t dyx, dHs, dxs, Ws2T, Ws13T, dyxT, asT, dHsT, xT, soff;
+};
+BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
+  BwdWs b;
+  const size_t eb = elem_bytes(o);
+  const int64_t R = d->T * d->k, nu = n_up(o, d->F), PR = padded_rows(R, d->E);
+  const int64_t Fs = d->F_shared, PRs = padded_rows(d->T, 1);
+  b.ffn = plan_ffn(c, d->E, R, d->F, int(eb), false);
+  b.ffn_s = plan_ffn(c, 1, d->T, Fs, int(eb), false);
+  b.dO = c.take(size_t(R) * d->d * eb);
+  b.dg = c.take(size_t(R) * 4);
+  b.dH = c.take(size_t(R) * nu * eb);
+  b.dXp = c.take(size_t(R) * d->d * 4);
+  b.W2T = c.take(size_t(d->E) * d->F * d->d * eb);
+  b.W13T = c.take(size_t(d->E) * d->d * nu * eb);
+  b.dOT = c.take(size_t(d->d) * PR * eb);
+  b.aT = c.take(size_t(d->F) * PR * eb);
+  b.dHT = c.take(size_t(nu) * PR * eb);
+  b.xpT = c.take(size_t(d->d) * PR * eb);
+  b.dz = c.take(size_t(d->T) * d->E * 4);
+  b.dwg_part = c.take(size_t(DWG_SPLIT) * d->d * d->E * 4);
+  b.dxr = c.take(size_t(d->T) * d->d * 4);
+  b.dyx = c.take(Fs ? size_t(d->T) * d->d * eb : 0);
+  b.dHs = c.take(size_t(d->T) * 2 * Fs * eb);
+  b.dxs = c.take(Fs ? size_t(d->T) * d->d * 4 : 0);
+  b.Ws2T = c.take(size_t(Fs) * d->d * eb);
+  b.Ws13T = c.take(size_t(d->d) * 2 * Fs * eb);
+  b.dyxT = c.take(Fs ? size_t(d->d) * PRs * eb : 0);
+  b.asT = c.take(size_t(Fs) * PRs * eb);
+  b.dHsT = c.take(size_t(2 * Fs) * PRs * eb);
+  b.xT = c.take(Fs ? size_t(d->d) * PRs * eb : 0);
+  b.soff = c.take(2 * 4);
+  return b;
+}
+
+GemmArgs gemm_rows(const void* A, const void* B, int64_t bstride, const int32_t* offsets, int G,
+                   int64_t max_rows, int N, int K, int epi, void* out, const void* h_in, int n_b,
+                   int up_off) {
+  GemmArgs g{};
+  g.A = A; g.B = B; g.b_group_stride = bstride; g.offsets = offsets; g.G = G;
+  g.max_rows = max_rows; g.N = N; g.K = K; g.epi = epi; g.out = out; g.h_in = h_in;
+  g.n_b = n_b; g.up_off = up_off; g.kgroup = 0;
+  return g;
+}
+
+GemmArgs gemm_kgroup(const void* AT, const void* BT, const int32_t* offsets, int G, int M_fixed,
+                     int N, float* out) {
+  GemmArgs g{};
+  g.A = AT; g.B = BT; g.offsets = offsets; g.G = G; g.M_fixed = M_fixed; g.N = N;
+  g.epi = EPI_STORE_F32; g.out = out; g.kgroup = 1;
+  return g;
+}
+
+hipError_t gemm_on(const moe_opts* o, GemmArgs g, int32_t* tile_start, hipStream_t st) {
+  g.tile_start = tile_start;
+  return o->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, st) : launch_grouped_gemm_f32(g, st);
+}
+
 }  // namespace
 
 // ============================================================================
@@ -263,8 +330,13 @@ int moe_workspace_size(const moe_dims* d, const moe_opts* o, int with_bwd, size_
   if (s) return s;
   Carver c;
   plan_fwd(c, d, o);
-  (void)with_bwd;
-  *bytes = c.off;
+  size_t need = c.off;
+  if (with_bwd) {
+    Carver cb;
+    plan_bwd(cb, d, o);
+    need = need > cb.off ? need : cb.off;
+  }
+  *bytes = need;
   return MOE_OK;
 }
 
@@ -369,7 +441,12 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
   void* xperm = sv ? sv->x_perm : at<void>(ws, f.xperm);
   void* abuf = sv ? sv->a : at<void>(ws, f.a);
   float* obuf = sv ? sv->o : at<float>(ws, f.o);
-  float* losses = sv ? sv->losses : (stats ? stats->losses : nullptr);
+  // The router losses are part of the forward whenever a coefficient is set;
+  // with nowhere else to put them they land in the workspace.
+  const bool want_losses = o->aux_coef != 0.0f || o->z_coef != 0.0f;
+  float* losses = sv ? sv->losses
+                     : (stats && stats->losses) ? stats->losses
+                     : want_losses ? at<float>(ws, f.losses) : nullptr;
 
   s = do_route(d, o, x, w->Wg, w->logit_offset, w->sel_bias, idx, gate, nullptr,
                sv ? sv->logits : nullptr, nullptr, losses, stats ? stats->n_nonfinite : nullptr,
@@ -404,9 +481,99 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
 int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, const void* x,
                   const moe_saved* sv, const float* dy, float* dx, moe_grads* grads, void* ws,
                   size_t ws_bytes, void* stream) {
-  (void)d; (void)o; (void)w; (void)x; (void)sv; (void)dy; (void)dx; (void)grads; (void)ws;
-  (void)ws_bytes; (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  int s = check_dims(d, o);
+  if (s) return s;
+  if (d->T == 0) return MOE_OK;
+  const int64_t Fs = d->F_shared;
+  if (!w || !x || !sv || !dy || !dx || !grads || !w->Wg || !w->W13 || !w->W2) return MOE_ERR_INVALID_ARG;
+  if (!grads->dWg || !grads->dW13 || !grads->dW2) return MOE_ERR_INVALID_ARG;
+  if (Fs > 0 && (!w->Ws13 || !w->Ws2 || !grads->dWs13 || !grads->dWs2 || !sv->h_shared ||
+                 !sv->a_shared))
+    return MOE_ERR_INVALID_ARG;
+  if (!sv->topk_idx || !sv->topk_gate || !sv->logits || !sv->counts || !sv->offsets ||
+      !sv->row_of_slot || !sv->x_perm || !sv->h || !sv->a || !sv->o)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(sv->o) ||
+      !aligned16(sv->x_perm) || !aligned16(sv->h) || !aligned16(sv->a) || !aligned16(w->W13) ||
+      !aligned16(w->W2))
+    return MOE_ERR_INVALID_ARG;
+  Carver c;
+  const BwdWs b = plan_bwd(c, d, o);
+  if ((s = check_ws(ws, ws_bytes, c.off))) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = o->dtype == MOE_DTYPE_BF16;
+  const int eb = elem_bytes(o);
+  const int T = int(d->T), k = int(d->k), E = int(d->E), D = int(d->d), F = int(d->F);
+  const int nu = int(n_up(o, d->F));
+  const int64_t R = d->T * d->k;
+  const bool swiglu = o->act == MOE_ACT_SWIGLU;
+  int32_t* ts = at<int32_t>(ws, b.ffn.tile_up);
+  int32_t* ts_s = at<int32_t>(ws, b.ffn_s.tile_up);
+
+  // combine backward: dO, dg, and dy in the x type for the shared expert
+  void* dyx = Fs ? at<void>(ws, b.dyx) : nullptr;
+  MOE_TRY(launch_combine_bwd(dy, sv->o, sv->row_of_slot, sv->topk_gate, T, k, D, bf16,
+                             at<void>(ws, b.dO), at<float>(ws, b.dg), dyx, st));
+  // routed experts, data gradients: dA = dO W2 (+ activation backward) -> dH; dXp = dH W13
+  MOE_TRY(launch_batched_transpose(w->W2, E, D, F, eb, at<void>(ws, b.W2T), st));
+  MOE_TRY(gemm_on(o, gemm_rows(at<void>(ws, b.dO), at<void>(ws, b.W2T), int64_t(F) * D,
+                               sv->offsets, E, R, F, D, swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD,
+                               at<void>(ws, b.dH), sv->h, nu, swiglu ? F : 0),
+                  ts, st));
+  MOE_TRY(launch_batched_transpose(w->W13, E, nu, D, eb, at<void>(ws, b.W13T), st));
+  MOE_TRY(gemm_on(o, gemm_rows(at<void>(ws, b.dH), at<void>(ws, b.W13T), int64_t(D) * nu,
+                               sv->offsets, E, R, D, nu, EPI_STORE_F32, at<void>(ws, b.dXp),
+                               nullptr, 0, 0),
+                  ts, st));
+  // routed experts, weight gradients over each expert's rows
+  MOE_TRY(launch_group_transpose(at<void>(ws, b.dO), D, sv->offsets, E, R, eb, at<void>(ws, b.dOT), st));
+  MOE_TRY(launch_group_transpose(sv->a, F, sv->offsets, E, R, eb, at<void>(ws, b.aT), st));
+  MOE_TRY(gemm_on(o, gemm_kgroup(at<void>(ws, b.dOT), at<void>(ws, b.aT), sv->offsets, E, D, F,
+                                 grads->dW2),
+                  ts, st));
+  MOE_TRY(launch_group_transpose(at<void>(ws, b.dH), nu, sv->offsets, E, R, eb, at<void>(ws, b.dHT), st));
+  MOE_TRY(launch_group_transpose(sv->x_perm, D, sv->offsets, E, R, eb, at<void>(ws, b.xpT), st));
+  MOE_TRY(gemm_on(o, gemm_kgroup(at<void>(ws, b.dHT), at<void>(ws, b.xpT), sv->offsets, E, nu, D,
+                                 grads->dW13),
+                  ts, st));
+  // shared expert (gate 1 on every token)
+  float* dxs = nullptr;
+  if (Fs > 0) {
+    const int fs = int(Fs);
+    int32_t* soff = at<int32_t>(ws, b.soff);
+    MOE_TRY(fill_offsets_1(soff, int32_t(T), st));
+    dxs = at<float>(ws, b.dxs);
+    MOE_TRY(launch_batched_transpose(w->Ws2, 1, D, fs, eb, at<void>(ws, b.Ws2T), st));
+    MOE_TRY(gemm_on(o, gemm_rows(dyx, at<void>(ws, b.Ws2T), 0, soff, 1, T, fs, D, EPI_SWIGLU_BWD,
+                                 at<void>(ws, b.dHs), sv->h_shared, 2 * fs, fs),
+                    ts_s, st));
+    MOE_TRY(launch_batched_transpose(w->Ws13, 1, 2 * fs, D, eb, at<void>(ws, b.Ws13T), st));
+    MOE_TRY(gemm_on(o, gemm_rows(at<void>(ws, b.dHs), at<void>(ws, b.Ws13T), 0, soff, 1, T, D,
+                                 2 * fs, EPI_STORE_F32, dxs, nullptr, 0, 0),
+                    ts_s, st));
+    MOE_TRY(launch_group_transpose(dyx, D, soff, 1, T, eb, at<void>(ws, b.dyxT), st));
+    MOE_TRY(launch_group_transpose(sv->a_shared, fs, soff, 1, T, eb, at<void>(ws, b.asT), st));
+    MOE_TRY(gemm_on(o, gemm_kgroup(at<void>(ws, b.dyxT), at<void>(ws, b.asT), soff, 1, D, fs,
+                                   grads->dWs2),
+                    ts_s, st));
+    MOE_TRY(launch_group_transpose(at<void>(ws, b.dHs), 2 * fs, soff, 1, T, eb, at<void>(ws, b.dHsT), st));
+    MOE_TRY(launch_group_transpose(x, D, soff, 1, T, eb, at<void>(ws, b.xT), st));
+    MOE_TRY(gemm_on(o, gemm_kgroup(at<void>(ws, b.dHsT), at<void>(ws, b.xT), soff, 1, 2 * fs, D,
+                                   grads->dWs13),
+                    ts_s, st));
+  }
+  // router: dz from the kept gates' gradient and the two losses; dWg = x^T dz;
+  // dx_router = dz Wg^T
+  float* dz = at<float>(ws, b.dz);
+  MOE_TRY(launch_router_bwd(sv->logits, sv->topk_idx, at<float>(ws, b.dg), sv->counts, T, E, k,
+                            o->score, o->renorm != 0, o->gate_scale, o->aux_coef, o->z_coef, dz,
+                            st));
+  MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, DWG_SPLIT,
+                              at<float>(ws, b.dwg_part), grads->dWg, st));
+  float* dxr = at<float>(ws, b.dxr);
+  MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, st));
+  MOE_TRY(launch_unpermute_sum(at<float>(ws, b.dXp), sv->row_of_slot, dxs, dxr, T, k, D, dx, st));
+  return MOE_OK;
 }
 
 int moe_bias_update(const int32_t* counts, float* bias, int64_t E, float target, float gamma,

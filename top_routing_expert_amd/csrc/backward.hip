@@ -1,0 +1,348 @@
+// Backward pass pieces of the MoE layer for gfx950 (everything except the
+// grouped expert GEMMs and the transposes).
+//
+// The gradient is that of J = <dy, y> + L_aux + L_z.  Routing decisions (the
+// kept experts, the drops) and the load fractions f_e are constants; the
+// gradient reaches the router only through the kept gates ("Mixture of Experts
+// Explained", "What is sparsity?": y = sum_i G(x)_i E_i(x) with G zero outside
+// the top-k), plus the two router losses.
+#include "common.hpp"
+#include "gemm_common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int BWD_KMAX = 16;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Combine backward, one wave per token.  For kept slot j of token t:
+//   dO[row] = gate[t,j] * dy[t]   (x element type, feeds the expert dgrad/wgrad)
+//   dg[t,j] = <dy[t], o[row]>     (fp32; 0 for a dropped slot)
+// and dy_x[t] = dy[t] in the x element type (the shared expert's gradient).
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const float* __restrict__ dy, const float* __restrict__ o, const int32_t* __restrict__ ros,
+    const float* __restrict__ gate, int T, int k, int d, void* __restrict__ dO,
+    float* __restrict__ dg, void* __restrict__ dy_x) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (t >= T) return;
+  int rows[BWD_KMAX];
+  float gs[BWD_KMAX], dot[BWD_KMAX];
+#pragma unroll
+  for (int j = 0; j < BWD_KMAX; ++j) {
+    rows[j] = j < k ? ros[int64_t(t) * k + j] : -1;
+    gs[j] = j < k ? gate[int64_t(t) * k + j] : 0.0f;
+    dot[j] = 0.0f;
+  }
+  const float4* dyr = reinterpret_cast<const float4*>(dy + int64_t(t) * d);
+  for (int c = l; c < (d >> 2); c += 64) {
+    const float4 v = dyr[c];
+    if (dy_x) {
+      if constexpr (BF16)
+        reinterpret_cast<uint2*>(static_cast<uint16_t*>(dy_x) + int64_t(t) * d)[c] =
+            make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+      else
+        reinterpret_cast<float4*>(static_cast<float*>(dy_x) + int64_t(t) * d)[c] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < BWD_KMAX; ++j) {
+      if (rows[j] < 0) continue;
+      const float4 ov = reinterpret_cast<const float4*>(o + int64_t(rows[j]) * d)[c];
+      dot[j] += v.x * ov.x + v.y * ov.y + v.z * ov.z + v.w * ov.w;
+      const float g = gs[j];
+      if constexpr (BF16)
+        reinterpret_cast<uint2*>(static_cast<uint16_t*>(dO) + int64_t(rows[j]) * d)[c] =
+            make_uint2(pack_bf2(g * v.x, g * v.y), pack_bf2(g * v.z, g * v.w));
+      else
+        reinterpret_cast<float4*>(static_cast<float*>(dO) + int64_t(rows[j]) * d)[c] =
+            make_float4(g * v.x, g * v.y, g * v.z, g * v.w);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < BWD_KMAX; ++j) {
+    if (j >= k) break;
+    const float s = wave_sum(dot[j]);
+    if (l == 0) dg[int64_t(t) * k + j] = rows[j] >= 0 ? s : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router backward, one wave per token; lane l owns experts l, l+64, l+128, l+192.
+// From the saved logits z it recomputes the scores s, then
+//   gates -> scores: renormalised gates g_j = scale * s_j / S (S = sum of kept s):
+//     ds_j = scale / S * (dg_j - sum_i dg_i * s_i / S); otherwise ds_j = scale * dg_j;
+//   aux loss L_aux = a * E * sum_e f_e * mean_t p_te, p = s / sum_e s:
+//     ds_e += (c_e - sum_e' p_e' c_e') / sum_e s,  c_e = a * E * f_e / T;
+//   scores -> logits: softmax Jacobian, s(1-s) for sigmoid, sigma(z) / (2 s) for
+//     sqrt(softplus) (e^{z/2}/2 where s underflows);
+//   z-loss L_z = b * mean_t lse_t^2:  dz_e += 2 b / T * lse * softmax(z)_e.
+__global__ __launch_bounds__(256) void router_bwd_kernel(
+    const float* __restrict__ z, const int32_t* __restrict__ idx, const float* __restrict__ dg,
+    const int32_t* __restrict__ counts, int T, int E, int k, int score, int renorm, float scale,
+    float aux_coef, float z_coef, float* __restrict__ dz) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (t >= T) return;
+  constexpr int VPL = 4;
+  float zv[VPL], s[VPL], ds[VPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = l + 64 * v;
+    zv[v] = e < E ? z[int64_t(t) * E + e] : -INFINITY;
+    if (e < E) m = fmaxf(m, zv[v]);
+    ds[v] = 0.0f;
+  }
+  m = wave_max(m);
+  float se = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+    if (l + 64 * v < E) se += expf(zv[v] - m);
+  se = wave_sum(se);
+  float ssum = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = l + 64 * v;
+    float sv = 0.0f;
+    if (e < E) {
+      if (score == 0) sv = expf(zv[v] - m) / se;
+      else if (score == 1) sv = 1.0f / (1.0f + expf(-zv[v]));
+      else sv = sqrtf(fmaxf(zv[v], 0.0f) + log1pf(expf(-fabsf(zv[v]))));
+    }
+    s[v] = sv;
+    ssum += sv;
+  }
+  ssum = wave_sum(ssum);
+  // kept gates
+  int ix[BWD_KMAX];
+  float dgv[BWD_KMAX], ssel[BWD_KMAX];
+  float S = 0.0f;
+#pragma unroll
+  for (int j = 0; j < BWD_KMAX; ++j) {
+    ix[j] = j < k ? idx[int64_t(t) * k + j] : -1;
+    dgv[j] = j < k ? dg[int64_t(t) * k + j] : 0.0f;
+    ssel[j] = 0.0f;
+    if (j < k && unsigned(ix[j]) < unsigned(E)) {
+      const int slot = ix[j] >> 6;
+      float mine = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (v == slot) mine = s[v];
+      ssel[j] = __shfl(mine, ix[j] & 63, 64);
+      S += ssel[j];
+    }
+  }
+  float sum_dg_ghat = 0.0f;
+  if (renorm) {
+#pragma unroll
+    for (int j = 0; j < BWD_KMAX; ++j)
+      if (j < k) sum_dg_ghat += dgv[j] * (ssel[j] / S);
+  }
+#pragma unroll
+  for (int j = 0; j < BWD_KMAX; ++j) {
+    if (j >= k || unsigned(ix[j]) >= unsigned(E)) continue;
+    const float dsel = renorm ? scale / S * (dgv[j] - sum_dg_ghat) : scale * dgv[j];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (l + 64 * v == ix[j]) ds[v] += dsel;
+  }
+  if (aux_coef != 0.0f) {
+    float c[VPL], pc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = l + 64 * v;
+      c[v] = e < E ? aux_coef * float(E) * (float(counts[e]) / (float(T) * k)) / float(T) : 0.0f;
+      pc += (s[v] / ssum) * c[v];
+    }
+    pc = wave_sum(pc);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (l + 64 * v < E) ds[v] += (c[v] - pc) / ssum;
+  }
+  float dsum = 0.0f;
+  if (score == 0) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) dsum += ds[v] * s[v];
+    dsum = wave_sum(dsum);
+  }
+  const float lse = m + logf(se);
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = l + 64 * v;
+    if (e >= E) continue;
+    float d;
+    if (score == 0) {
+      d = s[v] * (ds[v] - dsum);
+    } else if (score == 1) {
+      d = ds[v] * s[v] * (1.0f - s[v]);
+    } else {
+      const float sig = 1.0f / (1.0f + expf(-zv[v]));
+      d = ds[v] * (s[v] > 0.0f ? sig / (2.0f * s[v]) : 0.5f * expf(0.5f * zv[v]));
+    }
+    if (z_coef != 0.0f) d += 2.0f * z_coef / float(T) * lse * (expf(zv[v] - m) / se);
+    dz[int64_t(t) * E + e] = d;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 FMA GEMM with arbitrary strides for the router gradients:
+//   P[kz][m][n] = sum over k in chunk kz of A(m,k) * B(k,n),
+//   A(m,k) = A[m*sam + k*sak] (bf16 or fp32), B(k,n) = B[k*sbk + n*sbn] (fp32).
+// 64x64 tiles, 256 threads with 4x4 micro-tiles; the k-chunks (grid.z) are
+// summed afterwards in chunk order, so the result is deterministic.
+template <typename TA>
+__global__ __launch_bounds__(256) void strided_gemm_kernel(
+    const TA* __restrict__ A, int64_t sam, int64_t sak, const float* __restrict__ B, int64_t sbk,
+    int64_t sbn, int M, int N, int K, int kchunk, float* __restrict__ P) {
+  __shared__ float As[16][68];
+  __shared__ float Bs[16][68];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = kb; k0 < ke; k0 += 16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;          // 1024 elements of each 64x16 tile
+      int mm, kk;
+      if (sam == 1) { mm = e & 63; kk = e >> 6; } else { kk = e & 15; mm = e >> 4; }
+      const int gm = m0 + mm, gk = k0 + kk;
+      float av = 0.0f;
+      if (gm < M && gk < ke) {
+        if constexpr (sizeof(TA) == 2) av = bf2f(A[int64_t(gm) * sam + int64_t(gk) * sak]);
+        else av = A[int64_t(gm) * sam + int64_t(gk) * sak];
+      }
+      As[kk][mm] = av;
+      int nn, kk2;
+      if (sbn == 1) { nn = e & 63; kk2 = e >> 6; } else { kk2 = e & 15; nn = e >> 4; }
+      const int gn = n0 + nn, gk2 = k0 + kk2;
+      Bs[kk2][nn] = (gn < N && gk2 < ke) ? B[int64_t(gk2) * sbk + int64_t(gn) * sbn] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* Pz = P + int64_t(blockIdx.z) * M * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gm = m0 + ty * 4 + i;
+    if (gm >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + tx * 4 + j;
+      if (gn < N) Pz[int64_t(gm) * N + gn] = acc[i][j];
+    }
+  }
+}
+
+// out[i] = sum over z of P[z][i], z in order.
+__global__ void sum_partials_kernel(const float* __restrict__ P, int nz, int64_t n,
+                                    float* __restrict__ out) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int z = 0; z < nz; ++z) s += P[int64_t(z) * n + i];
+  out[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// dx[t] = sum over kept slots j (slot order) of dXp[row_tj] + extra1[t] + extra2[t].
+__global__ __launch_bounds__(256) void unpermute_sum_kernel(
+    const float* __restrict__ dxp, const int32_t* __restrict__ ros, const float* __restrict__ e1,
+    const float* __restrict__ e2, int T, int k, int d, float* __restrict__ dx) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (t >= T) return;
+  int rows[BWD_KMAX];
+#pragma unroll
+  for (int j = 0; j < BWD_KMAX; ++j) rows[j] = j < k ? ros[int64_t(t) * k + j] : -1;
+  for (int c = l; c < (d >> 2); c += 64) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < BWD_KMAX; ++j) {
+      if (rows[j] < 0) continue;
+      const float4 v = reinterpret_cast<const float4*>(dxp + int64_t(rows[j]) * d)[c];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (e1) {
+      const float4 v = reinterpret_cast<const float4*>(e1 + int64_t(t) * d)[c];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (e2) {
+      const float4 v = reinterpret_cast<const float4*>(e2 + int64_t(t) * d)[c];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    reinterpret_cast<float4*>(dx + int64_t(t) * d)[c] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_combine_bwd(const float* dy, const float* o, const int32_t* ros, const float* gate,
+                              int T, int k, int d, bool bf16, void* dO, float* dg, void* dy_x,
+                              hipStream_t st) {
+  const unsigned grid = unsigned(cdiv(T, 4));
+  if (bf16) combine_bwd_kernel<true><<<grid, 256, 0, st>>>(dy, o, ros, gate, T, k, d, dO, dg, dy_x);
+  else combine_bwd_kernel<false><<<grid, 256, 0, st>>>(dy, o, ros, gate, T, k, d, dO, dg, dy_x);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* z, const int32_t* idx, const float* dg,
+                             const int32_t* counts, int T, int E, int k, int score, int renorm,
+                             float scale, float aux_coef, float z_coef, float* dz, hipStream_t st) {
+  router_bwd_kernel<<<unsigned(cdiv(T, 4)), 256, 0, st>>>(z, idx, dg, counts, T, E, k, score,
+                                                          renorm, scale, aux_coef, z_coef, dz);
+  return hipGetLastError();
+}
+
+hipError_t launch_strided_gemm(const void* A, bool a_bf16, int64_t sam, int64_t sak, const float* B,
+                               int64_t sbk, int64_t sbn, int M, int N, int K, int nsplit, float* P,
+                               float* out, hipStream_t st) {
+  const int kchunk = int(cdiv(cdiv(K, nsplit), 16) * 16);
+  const dim3 grid(unsigned(cdiv(N, 64)), unsigned(cdiv(M, 64)), unsigned(nsplit));
+  if (a_bf16)
+    strided_gemm_kernel<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(A), sam, sak,
+                                                        B, sbk, sbn, M, N, K, kchunk, P);
+  else
+    strided_gemm_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(A), sam, sak, B,
+                                                     sbk, sbn, M, N, K, kchunk, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || out == nullptr) return e;
+  const int64_t n = int64_t(M) * N;
+  sum_partials_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(P, nsplit, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute_sum(const float* dxp, const int32_t* ros, const float* e1,
+                                const float* e2, int T, int k, int d, float* dx, hipStream_t st) {
+  unpermute_sum_kernel<<<unsigned(cdiv(T, 4)), 256, 0, st>>>(dxp, ros, e1, e2, T, k, d, dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

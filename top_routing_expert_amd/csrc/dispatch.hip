@@ -48,10 +48,16 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __res
   const int e = threadIdx.x;
   int32_t total = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int32_t c = blockcnt[int64_t(b) * E + e];
-      blockbase[int64_t(b) * E + e] = total;
-      total += c;
+    // eight independent loads in flight per step; the running sum stays in order
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+      int32_t c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = b0 + i < nblk ? blockcnt[int64_t(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (b0 + i < nblk) blockbase[int64_t(b0 + i) * E + e] = total;
+        total += c[i];
+      }
     }
     if (counts) counts[e] = total;
   }
@@ -82,16 +88,13 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __res
 //      the leader records the wave's count for the expert;
 //   2. rank in expert = blockbase[b][e] + counts of lower waves + rank in wave;
 //      kept iff rank < C; row = offsets[e] + rank;
-//   3. copy: each wave reads each of its tokens' x row once (16-byte lanes)
-//      and writes it to every kept row of the token.
+// The row copy is a separate, token-parallel kernel (permute_copy_kernel).
 template <int KM>
-__global__ __launch_bounds__(256) void dispatch_permute_kernel(
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int64_t C,
     const int32_t* __restrict__ blockbase, const int32_t* __restrict__ offsets,
-    const uint8_t* __restrict__ x, int row_bytes, int32_t* __restrict__ row_of_slot,
-    int32_t* __restrict__ token_of_row, uint8_t* __restrict__ x_perm) {
+    int32_t* __restrict__ row_of_slot, int32_t* __restrict__ token_of_row) {
   __shared__ int32_t wavecnt[4][256];
-  __shared__ int32_t srow[DISP_TB * KM];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   for (int i = tid; i < 4 * 256; i += blockDim.x) (&wavecnt[0][0])[i] = 0;
   const int t = blockIdx.x * DISP_TB + tid;
@@ -153,32 +156,37 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(
           token_of_row[row] = t;
         }
       }
-      srow[tid * KM + j] = row;
       if (valid) row_of_slot[int64_t(t) * k + j] = row;
     }
   }
-  __syncthreads();
-  // Row copy, token-major: the wave owns tokens w*64 .. w*64+63 of the block.
+}
+
+// Row copy, token-major, one wave per token: the token's x row is read once
+// (16-byte lanes) and written to each of its kept rows.
+template <int KM>
+__global__ __launch_bounds__(256) void permute_copy_kernel(const int32_t* __restrict__ row_of_slot,
+                                                           int T, int k,
+                                                           const uint8_t* __restrict__ x,
+                                                           int row_bytes,
+                                                           uint8_t* __restrict__ x_perm) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (t >= T) return;
+  int rows[KM];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    rows[j] = j < k ? row_of_slot[int64_t(t) * k + j] : -1;
+    any = any || rows[j] >= 0;
+  }
+  if (!any) return;
+  const uint8_t* src = x + int64_t(t) * row_bytes;
   const int chunks = row_bytes >> 4;
-  for (int tt = 0; tt < 64; ++tt) {
-    const int tl = w * 64 + tt;
-    const int tok = blockIdx.x * DISP_TB + tl;
-    if (tok >= T) break;
-    int rows[KM];
-    bool any = false;
+  for (int c = l; c < chunks; c += 64) {
+    const uint4 v = ld16(src + 16 * c);
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      rows[j] = j < k ? srow[tl * KM + j] : -1;
-      any = any || rows[j] >= 0;
-    }
-    if (!any) continue;
-    const uint8_t* src = x + int64_t(tok) * row_bytes;
-    for (int c = l; c < chunks; c += 64) {
-      const uint4 v = ld16(src + 16 * c);
-#pragma unroll
-      for (int j = 0; j < KM; ++j)
-        if (rows[j] >= 0) st16(x_perm + int64_t(rows[j]) * row_bytes + 16 * c, v);
-    }
+    for (int j = 0; j < KM; ++j)
+      if (rows[j] >= 0) st16(x_perm + int64_t(rows[j]) * row_bytes + 16 * c, v);
   }
 }
 
@@ -202,17 +210,19 @@ hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int6
                                    const void* x, int d, int elem_bytes, int32_t* row_of_slot,
                                    int32_t* token_of_row, void* x_perm, hipStream_t st) {
   const unsigned nblk = unsigned(cdiv(T, DISP_TB));
+  const unsigned ncopy = unsigned(cdiv(T, 4));
   const int row_bytes = d * elem_bytes;
   const auto* xs = static_cast<const uint8_t*>(x);
   auto* xp = static_cast<uint8_t*>(x_perm);
 #define MOE_PERMUTE(KM)                                                                        \
-  dispatch_permute_kernel<KM><<<dim3(nblk), dim3(256), 0, st>>>(                               \
-      idx, T, k, E, C, blockbase, offsets, xs, row_bytes, row_of_slot, token_of_row, xp)
-  if (k <= 1) MOE_PERMUTE(1);
-  else if (k <= 2) MOE_PERMUTE(2);
-  else if (k <= 4) MOE_PERMUTE(4);
-  else if (k <= 8) MOE_PERMUTE(8);
-  else MOE_PERMUTE(16);
+  dispatch_rank_kernel<KM><<<dim3(nblk), dim3(256), 0, st>>>(idx, T, k, E, C, blockbase,        \
+                                                             offsets, row_of_slot, token_of_row); \
+  permute_copy_kernel<KM><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp)
+  if (k <= 1) { MOE_PERMUTE(1); }
+  else if (k <= 2) { MOE_PERMUTE(2); }
+  else if (k <= 4) { MOE_PERMUTE(4); }
+  else if (k <= 8) { MOE_PERMUTE(8); }
+  else { MOE_PERMUTE(16); }
 #undef MOE_PERMUTE
   return hipGetLastError();
 }

@@ -39,10 +39,11 @@ __global__ void wg_split_kernel(const float* __restrict__ Wg, int d, int E, int 
 }
 
 // ---------------------------------------------------------------------------
-// Per-token epilogue shared by both logit kernels.  zs holds KS partial logit
-// sums for the block's 32 tokens.  Each token is handled by a group of LG
-// lanes, each owning VPL experts e = lane_in_group + LG * v.
-template <int EP, int KS>
+// Per-token epilogue shared by both logit kernels (NW waves per block).  zs
+// holds KS partial logit sums for the block's 32 tokens.  Each token is
+// handled by a group of LG lanes, each owning VPL experts e = lane_in_group +
+// LG * v.  LDS scratch: red_p/red_c [NW * EP], red_s [2 * NW].
+template <int EP, int KS, int NW>
 __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[ROUTE_BT][EP + 1],
                                                int t0, float* red_p, int32_t* red_c,
                                                float* red_s) {
@@ -50,6 +51,8 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
   constexpr int TPI = 64 / LG;
   constexpr int VPL = EP / LG;
   constexpr int KMAX = 16;
+  constexpr int TOK_PER_WAVE = ROUTE_BT / NW;
+  static_assert(TOK_PER_WAVE % TPI == 0, "tokens per wave");
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int gi = l / LG, lg = l % LG;
   const int E = a.E, k = a.k;
@@ -68,7 +71,6 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
   float lse2 = 0.0f;
   int32_t nf = 0;
 
-  constexpr int TOK_PER_WAVE = ROUTE_BT / 4;
   for (int it = 0; it < TOK_PER_WAVE / TPI; ++it) {
     const int tl = w * TOK_PER_WAVE + it * TPI + gi;
     const int t = t0 + tl;
@@ -147,7 +149,6 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
       }
     }
     if (valid) {
-      const float scale = a.renorm ? a.gate_scale / gs : a.gate_scale;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (j < k && lg == j) {
@@ -156,7 +157,6 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
           a.gate[int64_t(t) * k + j] = g;
         }
       }
-      (void)scale;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         const int e = lg + LG * v;
@@ -170,7 +170,7 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
       nf += finite ? 0 : 1;
     }
   }
-  // Combine the groups of a wave, then the four waves, in a fixed order.
+  // Combine the groups of a wave, then the waves, in a fixed order.
 #pragma unroll
   for (int msk = LG; msk < 64; msk <<= 1) {
 #pragma unroll
@@ -190,94 +190,110 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
   }
   if (l == 0) {
     red_s[w] = lse2;
-    red_s[4 + w] = __int_as_float(nf);
+    red_s[NW + w] = __int_as_float(nf);
   }
   __syncthreads();
   const int blk = blockIdx.x;
   for (int e = tid; e < EP; e += blockDim.x) {
-    a.part_p[int64_t(blk) * EP + e] = ((red_p[e] + red_p[EP + e]) + red_p[2 * EP + e]) + red_p[3 * EP + e];
-    a.part_cnt[int64_t(blk) * EP + e] = red_c[e] + red_c[EP + e] + red_c[2 * EP + e] + red_c[3 * EP + e];
+    float ps = 0.0f;
+    int32_t cs = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      ps += red_p[ww * EP + e];
+      cs += red_c[ww * EP + e];
+    }
+    a.part_p[int64_t(blk) * EP + e] = ps;
+    a.part_cnt[int64_t(blk) * EP + e] = cs;
   }
   if (tid == 0) {
-    a.part_lse2[blk] = ((red_s[0] + red_s[1]) + red_s[2]) + red_s[3];
-    a.part_nf[blk] = __float_as_int(red_s[4]) + __float_as_int(red_s[5]) +
-                     __float_as_int(red_s[6]) + __float_as_int(red_s[7]);
+    float ls = 0.0f;
+    int32_t ns = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      ls += red_s[ww];
+      ns += __float_as_int(red_s[NW + ww]);
+    }
+    a.part_lse2[blk] = ls;
+    a.part_nf[blk] = ns;
   }
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tokens: logits on MFMA 32x32x16.  A block covers 32 tokens and all EP
-// experts in NB = EP/32 output blocks of 32x32.  With fewer than four output
-// blocks the four waves also split d (KS parts), summed in order afterwards.
-// Within a 64-wide K chunk a lane loads 32 contiguous k of its token row (and
-// of its expert row of each Wg plane); MFMA step s uses elements 8s..8s+7 of
-// them, the same permutation of k for both operands.
+// bf16 tokens: logits on MFMA 32x32x16.  A block of 8 waves covers 32 tokens
+// and all EP experts: wave w computes output block (w % NB) (32 experts) over
+// the d-range (w / NB) of KS = 8 / NB parts, summed in order afterwards.
+// Within a 64-wide K chunk a lane loads 32 contiguous k of its token row and
+// of its expert row in each Wg plane; MFMA step s uses elements 8s..8s+7 of
+// them, the same permutation of k for both operands.  All loads of a chunk
+// are issued together and the next chunk is prefetched during the MFMAs.
 template <int EP>
-__global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a) {
+__global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
+  constexpr int NW = 8;
   constexpr int NB = EP / 32;
-  constexpr int KS = NB >= 4 ? 1 : 4 / NB;
-  constexpr int WPK = 4 / KS;
-  constexpr int BPW = NB / WPK;
+  constexpr int KS = NW / NB;
   __shared__ float zs[KS][ROUTE_BT][EP + 1];
-  __shared__ float red_p[4 * EP];
-  __shared__ int32_t red_c[4 * EP];
-  __shared__ float red_s[8];
+  __shared__ float red_p[NW * EP];
+  __shared__ int32_t red_c[NW * EP];
+  __shared__ float red_s[2 * NW];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int t0 = blockIdx.x * ROUTE_BT;
-  const int kp = w / WPK, wb = w % WPK;
+  const int eb = w % NB, kp = w / NB;
   const int dpart = a.d / KS;
   const int row = l & 31, g = l >> 5;
   const int trow = min(t0 + row, a.T - 1);
   const uint16_t* xr = static_cast<const uint16_t*>(a.x) + int64_t(trow) * a.d + kp * dpart + 32 * g;
   const int64_t plane = int64_t(EP) * a.d;
+  const uint16_t* wr = a.wsplit + int64_t(eb * 32 + row) * a.d + kp * dpart + 32 * g;
 
-  floatx16 acc[BPW];
+  floatx16 acc;
 #pragma unroll
-  for (int b = 0; b < BPW; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-  for (int kc = 0; kc < dpart; kc += 64) {
-    uint4 xa[4];
+  uint4 xa[4], wv[3][4];
+  auto load = [&](int kc) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) xa[q] = ld16(xr + kc + 8 * q);
 #pragma unroll
-    for (int b = 0; b < BPW; ++b) {
-      const int eb = wb + b * WPK;
-      const uint16_t* wr = a.wsplit + int64_t(eb * 32 + row) * a.d + kp * dpart + 32 * g + kc;
+    for (int p = 0; p < 3; ++p)
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        uint4 wv[4];
+      for (int q = 0; q < 4; ++q) wv[p][q] = ld16(wr + p * plane + kc + 8 * q);
+  };
+  load(0);
+  for (int kc = 0; kc < dpart; kc += 64) {
+    uint4 xc[4], wc[3][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) wv[q] = ld16(wr + p * plane + 8 * q);
+    for (int q = 0; q < 4; ++q) {
+      xc[q] = xa[q];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, xa[s]), __builtin_bit_cast(bf16x8, wv[s]), acc[b], 0, 0, 0);
-      }
+      for (int p = 0; p < 3; ++p) wc[p][q] = wv[p][q];
     }
+    if (kc + 64 < dpart) load(kc + 64);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xc[s]),
+                                                      __builtin_bit_cast(bf16x8, wc[p][s]), acc,
+                                                      0, 0, 0);
   }
   // D[i][j] of a 32x32 block: lane l holds column j = l%32 and rows
   // i = 8*(r/4) + 4*(l/32) + r%4 in accumulator register r.
 #pragma unroll
-  for (int b = 0; b < BPW; ++b) {
-    const int eb = wb + b * WPK;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) zs[kp][8 * (r >> 2) + 4 * g + (r & 3)][eb * 32 + row] = acc[b][r];
-  }
+  for (int r = 0; r < 16; ++r) zs[kp][8 * (r >> 2) + 4 * g + (r & 3)][eb * 32 + row] = acc[r];
   __syncthreads();
-  route_epilogue<EP, KS>(a, zs, t0, red_p, red_c, red_s);
+  route_epilogue<EP, KS, NW>(a, zs, t0, red_p, red_c, red_s);
 }
 
 // ---------------------------------------------------------------------------
 // Plain FMA logits (fp32 tokens, or shapes the MFMA tiling does not cover).
 template <int EP>
 __global__ __launch_bounds__(256) void route_simt_kernel(RouteArgs a) {
+  constexpr int NW = 4;
   __shared__ float zs[1][ROUTE_BT][EP + 1];
-  __shared__ float red_p[4 * EP];
-  __shared__ int32_t red_c[4 * EP];
-  __shared__ float red_s[8];
+  __shared__ float red_p[NW * EP];
+  __shared__ int32_t red_c[NW * EP];
+  __shared__ float red_s[2 * NW];
   const int t0 = blockIdx.x * ROUTE_BT;
   for (int o = threadIdx.x; o < ROUTE_BT * EP; o += blockDim.x) {
     const int tl = o / EP, e = o % EP;
@@ -295,47 +311,79 @@ __global__ __launch_bounds__(256) void route_simt_kernel(RouteArgs a) {
     zs[0][tl][e] = acc;
   }
   __syncthreads();
-  route_epilogue<EP, 1>(a, zs, t0, red_p, red_c, red_s);
+  route_epilogue<EP, 1, NW>(a, zs, t0, red_p, red_c, red_s);
 }
 
 // ---------------------------------------------------------------------------
-// One block: per-expert totals over the route blocks, in block order, and the
+// One block of 1024 threads: per-expert totals over the route blocks and the
 // two losses.  L_aux = aux_coef * E * sum_e (count_e / (T k)) * (P_e / T);
-// L_z = z_coef * sum_t lse_t^2 / T.  Reductions in double, fixed order.
-__global__ __launch_bounds__(256) void route_reduce_kernel(RouteArgs a, int nblk, float aux_coef,
-                                                           float z_coef, int32_t* counts,
-                                                           float* losses, int32_t* n_nonfinite) {
-  __shared__ double red[256];
+// L_z = z_coef * sum_t lse_t^2 / T.  Lane q of expert e sums blocks
+// b = q, q + L, ... in order; lanes, then experts, are combined in a fixed
+// order, in double.
+__global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nblk, float aux_coef,
+                                                            float z_coef, int32_t* counts,
+                                                            float* losses, int32_t* n_nonfinite) {
+  __shared__ double sp[1024];
+  __shared__ int64_t sc[1024];
+  __shared__ double sl[1024];
+  __shared__ int64_t sn[1024];
   const int tid = threadIdx.x;
+  const int EP = a.EP, L = 1024 / EP;
+  const int e = tid % EP, q = tid / EP;
+  double P = 0.0;
+  int64_t c = 0;
+  if (e < a.E) {
+#pragma unroll 8
+    for (int b = q; b < nblk; b += L) {
+      P += double(a.part_p[int64_t(b) * EP + e]);
+      c += a.part_cnt[int64_t(b) * EP + e];
+    }
+  }
+  double l2 = 0.0;
+  int64_t nf = 0;
+#pragma unroll 4
+  for (int b = tid; b < nblk; b += 1024) {
+    l2 += double(a.part_lse2[b]);
+    nf += a.part_nf[b];
+  }
+  sp[tid] = P;
+  sc[tid] = c;
+  sl[tid] = l2;
+  sn[tid] = nf;
+  __syncthreads();
+  // lanes of each expert -> lane 0 (fixed order); lse / nonfinite tree
+  if (q == 0) {
+    for (int qq = 1; qq < L; ++qq) {
+      sp[e] += sp[qq * EP + e];
+      sc[e] += sc[qq * EP + e];
+    }
+  }
+  for (int s = 512; s > 0; s >>= 1) {
+    if (tid < s) {
+      sl[tid] += sl[tid + s];
+      sn[tid] += sn[tid + s];
+    }
+    __syncthreads();
+  }
+  // per-expert terms, then a fixed-order tree over experts (reusing sp as the term buffer)
   double term = 0.0;
   if (tid < a.E) {
-    double P = 0.0;
-    int64_t c = 0;
-    for (int b = 0; b < nblk; ++b) {
-      P += double(a.part_p[int64_t(b) * a.EP + tid]);
-      c += a.part_cnt[int64_t(b) * a.EP + tid];
-    }
-    if (counts) counts[tid] = int32_t(c);
-    term = (double(c) / (double(a.T) * a.k)) * (P / a.T);
+    if (counts) counts[tid] = int32_t(sc[tid]);
+    term = (double(sc[tid]) / (double(a.T) * a.k)) * (sp[tid] / a.T);
   }
-  red[tid] = term;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
+  sp[tid] = tid < EP ? term : 0.0;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (tid < s) sp[tid] += sp[tid + s];
     __syncthreads();
   }
   if (tid == 0) {
-    double l2 = 0.0;
-    int64_t nf = 0;
-    for (int b = 0; b < nblk; ++b) {
-      l2 += double(a.part_lse2[b]);
-      nf += a.part_nf[b];
-    }
     if (losses) {
-      losses[0] = aux_coef != 0.0f ? float(double(aux_coef) * a.E * red[0]) : 0.0f;
-      losses[1] = z_coef != 0.0f ? float(double(z_coef) * l2 / a.T) : 0.0f;
+      losses[0] = aux_coef != 0.0f ? float(double(aux_coef) * a.E * sp[0]) : 0.0f;
+      losses[1] = z_coef != 0.0f ? float(double(z_coef) * sl[0] / a.T) : 0.0f;
     }
-    if (n_nonfinite) n_nonfinite[0] = int32_t(nf);
+    if (n_nonfinite) n_nonfinite[0] = int32_t(sn[0]);
   }
 }
 
@@ -350,7 +398,7 @@ template <int EP>
 static void launch_route_ep(const RouteArgs& a, bool mfma, hipStream_t st) {
   const unsigned nblk = unsigned(cdiv(a.T, ROUTE_BT));
   if (mfma)
-    route_mfma_kernel<EP><<<dim3(nblk), dim3(256), 0, st>>>(a);
+    route_mfma_kernel<EP><<<dim3(nblk), dim3(512), 0, st>>>(a);
   else
     route_simt_kernel<EP><<<dim3(nblk), dim3(256), 0, st>>>(a);
 }
@@ -369,8 +417,8 @@ hipError_t launch_route(const RouteArgs& a, bool mfma, hipStream_t st) {
 hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, float z_coef,
                                int32_t* counts, float* losses, int32_t* n_nonfinite,
                                hipStream_t st) {
-  route_reduce_kernel<<<dim3(1), dim3(256), 0, st>>>(a, nblk, aux_coef, z_coef, counts, losses,
-                                                     n_nonfinite);
+  route_reduce_kernel<<<dim3(1), dim3(1024), 0, st>>>(a, nblk, aux_coef, z_coef, counts, losses,
+                                                      n_nonfinite);
   return hipGetLastError();
 }
 
