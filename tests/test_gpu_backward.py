@@ -21,6 +21,7 @@ import math
 
 import numpy as np
 import pytest
+import scipy.special as sps
 import torch
 
 import oracle as orc
@@ -85,33 +86,41 @@ def test_layer_bwd_fp32(over):
         _close(g[name].cpu().numpy(), ref[name], 1e-4, name)
 
 
-def _swiglu_bwd_terms(X, W13e, W2e, dO, F):
+def _bwd_terms(X, W13e, W2e, dO, F, act):
     """Oracle expert backward, plus the magnitudes that carry the bf16
     roundings into dH (for the error bounds) and |a|.
 
     dA = dO W2 can cancel, so its rounding error scales with |dO| |W2|; the
-    rounding of the saved pre-activation h moves the activation factors by
-    their derivative: dsilu(h) by h * dsilu'(h) (dsilu has a zero near
-    h = -2.4), silu(h) by h * dsilu(h)."""
+    rounding of the saved pre-activation h moves each activation factor by its
+    derivative times h: dsilu(h) by h * dsilu'(h) (dsilu has a zero near
+    h = -2.4), silu(h) by h * dsilu(h), gelu'(h) by h * gelu''(h)."""
     h = X @ W13e.T
-    a = orc.silu(h[:, :F]) * h[:, F:]
-    dX, dW13, dW2 = orc.expert_bwd(X, h, a, W13e, W2e, dO, "swiglu")
-    hg, hu = h[:, :F], h[:, F:]
-    sg = 1.0 / (1.0 + np.exp(-hg))
-    ds = sg * (1 + hg * (1 - sg))
-    dds = sg * (1 - sg) * (2 + hg * (1 - 2 * sg))
     cA = np.abs(dO) @ np.abs(W2e)
-    adH = np.concatenate([cA * np.abs(hu) * (np.abs(ds) + np.abs(hg * dds)),
-                          cA * (np.abs(hg * sg) + np.abs(hg * ds))], 1)
+    if act == "swiglu":
+        a = orc.silu(h[:, :F]) * h[:, F:]
+        hg, hu = h[:, :F], h[:, F:]
+        sg = 1.0 / (1.0 + np.exp(-hg))
+        ds = sg * (1 + hg * (1 - sg))
+        dds = sg * (1 - sg) * (2 + hg * (1 - 2 * sg))
+        adH = np.concatenate([cA * np.abs(hu) * (np.abs(ds) + np.abs(hg * dds)),
+                              cA * (np.abs(hg * sg) + np.abs(hg * ds))], 1)
+    else:
+        a = orc.gelu(h)
+        phi = np.exp(-0.5 * h * h) / math.sqrt(2 * math.pi)
+        dg1 = 0.5 * (1 + sps.erf(h / math.sqrt(2))) + h * phi
+        dg2 = phi * (2 - h * h)
+        adH = cA * (np.abs(dg1) + np.abs(h * dg2))
+    dX, dW13, dW2 = orc.expert_bwd(X, h, a, W13e, W2e, dO, act)
     return dX, dW13, dW2, adH, np.abs(a)
 
 
-def test_layer_bwd_c5_full_size():
-    p = presets.get("c5")
-    print("[c5 bwd] generating inputs", flush=True)
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_layer_bwd_full_size(name):
+    p = presets.get(name)
+    print(f"[{name} bwd] generating inputs", flush=True)
     inp = synth.make_inputs(p, seed=0, with_dy=True)
     x, w, saved, y, g = _train(p, inp)
-    print("[c5 bwd] GPU done; oracle steps", flush=True)
+    print(f"[{name} bwd] GPU done; oracle steps", flush=True)
     T, k, E, d, F = p.T, p.k, p.E, p.d, p.F
     idx = saved["topk_idx"].cpu().numpy().astype(np.int64)
     ros = saved["row_of_slot"].cpu().numpy().astype(np.int64)
@@ -154,34 +163,37 @@ def test_layer_bwd_c5_full_size():
         toks = tor[r0:r1]
         Xe = X64[toks]
         dO = gate[toks, slot_of_row[r0:r1], None] * dy[toks]
-        _, dW13_ref, dW2_ref, adH, aa = _swiglu_bwd_terms(
-            Xe, inp["W13"][e].astype(np.float64), inp["W2"][e].astype(np.float64), dO, F)
+        _, dW13_ref, dW2_ref, adH, aa = _bwd_terms(
+            Xe, inp["W13"][e].astype(np.float64), inp["W2"][e].astype(np.float64), dO, F, p.act)
         _bounded(got13, dW13_ref, adH.T @ np.abs(Xe), f"dW13[{e}]")
         _bounded(got2, dW2_ref, np.abs(dO).T @ aa, f"dW2[{e}]")
-    print(f"[c5 bwd] experts {sample} sizes {[int(sizes[e]) for e in sample]}", flush=True)
+    print(f"[{name} bwd] experts {sample} sizes {[int(sizes[e]) for e in sample]}", flush=True)
 
     # shared expert, full
-    Ws13 = inp["Ws13"].astype(np.float64)
-    Ws2 = inp["Ws2"].astype(np.float64)
-    dxs_ref, dWs13_ref, dWs2_ref, adHs, aas = _swiglu_bwd_terms(X64, Ws13, Ws2, dy, p.F_shared)
-    _bounded(g["dWs13"].cpu().numpy(), dWs13_ref, adHs.T @ np.abs(X64), "dWs13")
-    _bounded(g["dWs2"].cpu().numpy(), dWs2_ref, np.abs(dy).T @ aas, "dWs2")
+    Wg = inp["Wg"].astype(np.float64)
+    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).integers(0, T, 30)]))
+    ref = dz[toks] @ Wg.T
+    cond = np.abs(dz[toks]) @ np.abs(Wg.T)
+    if p.F_shared:
+        Ws13 = inp["Ws13"].astype(np.float64)
+        Ws2 = inp["Ws2"].astype(np.float64)
+        dxs_ref, dWs13_ref, dWs2_ref, adHs, aas = _bwd_terms(X64, Ws13, Ws2, dy, p.F_shared, "swiglu")
+        _bounded(g["dWs13"].cpu().numpy(), dWs13_ref, adHs.T @ np.abs(X64), "dWs13")
+        _bounded(g["dWs2"].cpu().numpy(), dWs2_ref, np.abs(dy).T @ aas, "dWs2")
+        ref += dxs_ref[toks]
+        cond += adHs[toks] @ np.abs(Ws13)
 
     # dx on sampled tokens: each kept slot's expert backward for that one row
     dx = g["dx"].cpu().numpy()
-    Wg = inp["Wg"].astype(np.float64)
-    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).integers(0, T, 30)]))
-    ref = dxs_ref[toks] + dz[toks] @ Wg.T
-    cond = adHs[toks] @ np.abs(Ws13) + np.abs(dz[toks]) @ np.abs(Wg.T)
     for i, t in enumerate(toks):
         for j in range(k):
             if ros[t, j] < 0:
                 continue
             e = int(idx[t, j])
             W13e = inp["W13"][e].astype(np.float64)
-            dX, _, _, adH, _ = _swiglu_bwd_terms(X64[t:t + 1], W13e, inp["W2"][e].astype(np.float64),
-                                                 gate[t, j] * dy[t:t + 1], F)
+            dX, _, _, adH, _ = _bwd_terms(X64[t:t + 1], W13e, inp["W2"][e].astype(np.float64),
+                                          gate[t, j] * dy[t:t + 1], F, p.act)
             ref[i] += dX[0]
             cond[i] += (adH @ np.abs(W13e))[0]
     e2 = _bounded(dx[toks], ref, cond, "dx")
-    print(f"[c5 bwd] dWg err/rms {e1:.2e}, dx rms-err/rms {e2:.2e} on {len(toks)} tokens")
+    print(f"[{name} bwd] dWg err/rms {e1:.2e}, dx rms-err/rms {e2:.2e} on {len(toks)} tokens")

@@ -236,7 +236,15 @@ hipError_t fill_offsets_1(int32_t* off, int32_t rows, hipStream_t st) {
 }
 
 // ---- backward workspace ------------------------------------------------------
-constexpr int DWG_SPLIT = 16;   // k-chunks of the T-reduction of dWg
+// k-chunks of the T-reduction of dWg: enough 64x64 tiles x chunks to fill the
+// chip (about 2048 workgroups), at most 64 chunks and at least 128 tokens each.
+int dwg_split(const moe_dims* d) {
+  const int64_t tiles = cdiv(d->d, 64) * cdiv(d->E, 64);
+  int64_t s = cdiv(2048, tiles);
+  s = s < 1 ? 1 : (s > 64 ? 64 : s);
+  const int64_t by_t = d->T / 128 > 0 ? d->T / 128 : 1;
+  return int(s < by_t ? s : by_t);
+}
 
 int64_t padded_rows(int64_t rows, int64_t G) { return cdiv(rows, 64) * 64 + 64 * G; }
 
@@ -263,7 +271,7 @@ BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   b.dHT = c.take(size_t(nu) * PR * eb);
   b.xpT = c.take(size_t(d->d) * PR * eb);
   b.dz = c.take(size_t(d->T) * d->E * 4);
-  b.dwg_part = c.take(size_t(DWG_SPLIT) * d->d * d->E * 4);
+  b.dwg_part = c.take(size_t(dwg_split(d)) * d->d * d->E * 4);
   b.dxr = c.take(size_t(d->T) * d->d * 4);
   b.dyx = c.take(Fs ? size_t(d->T) * d->d * eb : 0);
   b.dHs = c.take(size_t(d->T) * 2 * Fs * eb);
@@ -568,7 +576,7 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
   MOE_TRY(launch_router_bwd(sv->logits, sv->topk_idx, at<float>(ws, b.dg), sv->counts, T, E, k,
                             o->score, o->renorm != 0, o->gate_scale, o->aux_coef, o->z_coef, dz,
                             st));
-  MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, DWG_SPLIT,
+  MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
                               at<float>(ws, b.dwg_part), grads->dWg, st));
   float* dxr = at<float>(ws, b.dxr);
   MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, st));
