@@ -246,61 +246,51 @@ int dwg_split(const moe_dims* d) {
   return int(s < by_t ? s : by_t);
 }
 
-int64_t padded_rows(int64_t rows, int64_t G) { return cdiv(rows, 64) * 64 + 64 * G; }
-
 struct BwdWs {
   FfnWs ffn, ffn_s;
-  size_t dO, dg, dH, dXp, W2T, W13T, dOT, aT, dHT, xpT, dz, dwg_part, dxr;
-  size_t dyx, dHs, dxs, Ws2T, Ws13T, dyxT, asT, dHsT, xT, soff;
+  size_t dO, dg, dH, dXp, dz, dwg_part, dxr;
+  size_t dyx, dHs, dxs, soff;
 };
 BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   BwdWs b;
   const size_t eb = elem_bytes(o);
-  const int64_t R = d->T * d->k, nu = n_up(o, d->F), PR = padded_rows(R, d->E);
-  const int64_t Fs = d->F_shared, PRs = padded_rows(d->T, 1);
+  const int64_t R = d->T * d->k, nu = n_up(o, d->F);
+  const int64_t Fs = d->F_shared;
   b.ffn = plan_ffn(c, d->E, R, d->F, int(eb), false);
   b.ffn_s = plan_ffn(c, 1, d->T, Fs, int(eb), false);
   b.dO = c.take(size_t(R) * d->d * eb);
   b.dg = c.take(size_t(R) * 4);
   b.dH = c.take(size_t(R) * nu * eb);
   b.dXp = c.take(size_t(R) * d->d * 4);
-  b.W2T = c.take(size_t(d->E) * d->F * d->d * eb);
-  b.W13T = c.take(size_t(d->E) * d->d * nu * eb);
-  b.dOT = c.take(size_t(d->d) * PR * eb);
-  b.aT = c.take(size_t(d->F) * PR * eb);
-  b.dHT = c.take(size_t(nu) * PR * eb);
-  b.xpT = c.take(size_t(d->d) * PR * eb);
   b.dz = c.take(size_t(d->T) * d->E * 4);
   b.dwg_part = c.take(size_t(dwg_split(d)) * d->d * d->E * 4);
   b.dxr = c.take(size_t(d->T) * d->d * 4);
   b.dyx = c.take(Fs ? size_t(d->T) * d->d * eb : 0);
   b.dHs = c.take(size_t(d->T) * 2 * Fs * eb);
   b.dxs = c.take(Fs ? size_t(d->T) * d->d * 4 : 0);
-  b.Ws2T = c.take(size_t(Fs) * d->d * eb);
-  b.Ws13T = c.take(size_t(d->d) * 2 * Fs * eb);
-  b.dyxT = c.take(Fs ? size_t(d->d) * PRs * eb : 0);
-  b.asT = c.take(size_t(Fs) * PRs * eb);
-  b.dHsT = c.take(size_t(2 * Fs) * PRs * eb);
-  b.xT = c.take(Fs ? size_t(d->d) * PRs * eb : 0);
   b.soff = c.take(2 * 4);
   return b;
 }
 
-GemmArgs gemm_rows(const void* A, const void* B, int64_t bstride, const int32_t* offsets, int G,
-                   int64_t max_rows, int N, int K, int epi, void* out, const void* h_in, int n_b,
-                   int up_off) {
+// Data gradient of an expert projection: out[rows] = epi(A[rows] . W[g]) with
+// the weights W [g][K, N] read as stored.
+GemmArgs gemm_dgrad(const void* A, const void* W, int64_t wstride, const int32_t* offsets, int G,
+                    int64_t max_rows, int N, int K, int epi, void* out, const void* h_in, int n_b,
+                    int up_off) {
   GemmArgs g{};
-  g.A = A; g.B = B; g.b_group_stride = bstride; g.offsets = offsets; g.G = G;
+  g.A = A; g.B = W; g.b_group_stride = wstride; g.offsets = offsets; g.G = G;
   g.max_rows = max_rows; g.N = N; g.K = K; g.epi = epi; g.out = out; g.h_in = h_in;
-  g.n_b = n_b; g.up_off = up_off; g.kgroup = 0;
+  g.n_b = n_b; g.up_off = up_off; g.mode = GM_NN;
   return g;
 }
 
-GemmArgs gemm_kgroup(const void* AT, const void* BT, const int32_t* offsets, int G, int M_fixed,
-                     int N, float* out) {
+// Weight gradient: out[g] = U_g^T . V_g over the rows of group g, U [rows, M],
+// V [rows, N] as stored.
+GemmArgs gemm_wgrad(const void* U, const void* V, const int32_t* offsets, int G, int M, int N,
+                    float* out) {
   GemmArgs g{};
-  g.A = AT; g.B = BT; g.offsets = offsets; g.G = G; g.M_fixed = M_fixed; g.N = N;
-  g.epi = EPI_STORE_F32; g.out = out; g.kgroup = 1;
+  g.A = U; g.B = V; g.offsets = offsets; g.G = G; g.M_fixed = M; g.N = N;
+  g.epi = EPI_STORE_F32; g.out = out; g.mode = GM_KGROUP;
   return g;
 }
 
@@ -510,7 +500,6 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
   if ((s = check_ws(ws, ws_bytes, c.off))) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = o->dtype == MOE_DTYPE_BF16;
-  const int eb = elem_bytes(o);
   const int T = int(d->T), k = int(d->k), E = int(d->E), D = int(d->d), F = int(d->F);
   const int nu = int(n_up(o, d->F));
   const int64_t R = d->T * d->k;
@@ -523,26 +512,17 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
   MOE_TRY(launch_combine_bwd(dy, sv->o, sv->row_of_slot, sv->topk_gate, T, k, D, bf16,
                              at<void>(ws, b.dO), at<float>(ws, b.dg), dyx, st));
   // routed experts, data gradients: dA = dO W2 (+ activation backward) -> dH; dXp = dH W13
-  MOE_TRY(launch_batched_transpose(w->W2, E, D, F, eb, at<void>(ws, b.W2T), st));
-  MOE_TRY(gemm_on(o, gemm_rows(at<void>(ws, b.dO), at<void>(ws, b.W2T), int64_t(F) * D,
-                               sv->offsets, E, R, F, D, swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD,
-                               at<void>(ws, b.dH), sv->h, nu, swiglu ? F : 0),
+  MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dO), w->W2, int64_t(D) * F, sv->offsets, E, R, F, D,
+                                swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, at<void>(ws, b.dH), sv->h,
+                                nu, swiglu ? F : 0),
                   ts, st));
-  MOE_TRY(launch_batched_transpose(w->W13, E, nu, D, eb, at<void>(ws, b.W13T), st));
-  MOE_TRY(gemm_on(o, gemm_rows(at<void>(ws, b.dH), at<void>(ws, b.W13T), int64_t(D) * nu,
-                               sv->offsets, E, R, D, nu, EPI_STORE_F32, at<void>(ws, b.dXp),
-                               nullptr, 0, 0),
+  MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dH), w->W13, int64_t(nu) * D, sv->offsets, E, R, D,
+                                nu, EPI_STORE_F32, at<void>(ws, b.dXp), nullptr, 0, 0),
                   ts, st));
-  // routed experts, weight gradients over each expert's rows
-  MOE_TRY(launch_group_transpose(at<void>(ws, b.dO), D, sv->offsets, E, R, eb, at<void>(ws, b.dOT), st));
-  MOE_TRY(launch_group_transpose(sv->a, F, sv->offsets, E, R, eb, at<void>(ws, b.aT), st));
-  MOE_TRY(gemm_on(o, gemm_kgroup(at<void>(ws, b.dOT), at<void>(ws, b.aT), sv->offsets, E, D, F,
-                                 grads->dW2),
-                  ts, st));
-  MOE_TRY(launch_group_transpose(at<void>(ws, b.dH), nu, sv->offsets, E, R, eb, at<void>(ws, b.dHT), st));
-  MOE_TRY(launch_group_transpose(sv->x_perm, D, sv->offsets, E, R, eb, at<void>(ws, b.xpT), st));
-  MOE_TRY(gemm_on(o, gemm_kgroup(at<void>(ws, b.dHT), at<void>(ws, b.xpT), sv->offsets, E, nu, D,
-                                 grads->dW13),
+  // routed experts, weight gradients over each expert's rows:
+  // dW2[e] = dO_e^T a_e, dW13[e] = dH_e^T x_e
+  MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dO), sv->a, sv->offsets, E, D, F, grads->dW2), ts, st));
+  MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dH), sv->x_perm, sv->offsets, E, nu, D, grads->dW13),
                   ts, st));
   // shared expert (gate 1 on every token)
   float* dxs = nullptr;
@@ -551,23 +531,14 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
     int32_t* soff = at<int32_t>(ws, b.soff);
     MOE_TRY(fill_offsets_1(soff, int32_t(T), st));
     dxs = at<float>(ws, b.dxs);
-    MOE_TRY(launch_batched_transpose(w->Ws2, 1, D, fs, eb, at<void>(ws, b.Ws2T), st));
-    MOE_TRY(gemm_on(o, gemm_rows(dyx, at<void>(ws, b.Ws2T), 0, soff, 1, T, fs, D, EPI_SWIGLU_BWD,
-                                 at<void>(ws, b.dHs), sv->h_shared, 2 * fs, fs),
+    MOE_TRY(gemm_on(o, gemm_dgrad(dyx, w->Ws2, 0, soff, 1, T, fs, D, EPI_SWIGLU_BWD,
+                                  at<void>(ws, b.dHs), sv->h_shared, 2 * fs, fs),
                     ts_s, st));
-    MOE_TRY(launch_batched_transpose(w->Ws13, 1, 2 * fs, D, eb, at<void>(ws, b.Ws13T), st));
-    MOE_TRY(gemm_on(o, gemm_rows(at<void>(ws, b.dHs), at<void>(ws, b.Ws13T), 0, soff, 1, T, D,
-                                 2 * fs, EPI_STORE_F32, dxs, nullptr, 0, 0),
+    MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dHs), w->Ws13, 0, soff, 1, T, D, 2 * fs,
+                                  EPI_STORE_F32, dxs, nullptr, 0, 0),
                     ts_s, st));
-    MOE_TRY(launch_group_transpose(dyx, D, soff, 1, T, eb, at<void>(ws, b.dyxT), st));
-    MOE_TRY(launch_group_transpose(sv->a_shared, fs, soff, 1, T, eb, at<void>(ws, b.asT), st));
-    MOE_TRY(gemm_on(o, gemm_kgroup(at<void>(ws, b.dyxT), at<void>(ws, b.asT), soff, 1, D, fs,
-                                   grads->dWs2),
-                    ts_s, st));
-    MOE_TRY(launch_group_transpose(at<void>(ws, b.dHs), 2 * fs, soff, 1, T, eb, at<void>(ws, b.dHsT), st));
-    MOE_TRY(launch_group_transpose(x, D, soff, 1, T, eb, at<void>(ws, b.xT), st));
-    MOE_TRY(gemm_on(o, gemm_kgroup(at<void>(ws, b.dHsT), at<void>(ws, b.xT), soff, 1, 2 * fs, D,
-                                   grads->dWs13),
+    MOE_TRY(gemm_on(o, gemm_wgrad(dyx, sv->a_shared, soff, 1, D, fs, grads->dWs2), ts_s, st));
+    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dHs), x, soff, 1, 2 * fs, D, grads->dWs13),
                     ts_s, st));
   }
   // router: dz from the kept gates' gradient and the two losses; dWg = x^T dz;

@@ -1,5 +1,5 @@
 // Backward pass pieces of the MoE layer for gfx950 (everything except the
-// grouped expert GEMMs and the transposes).
+// grouped expert GEMMs).
 //
 // The gradient is that of J = <dy, y> + L_aux + L_z.  Routing decisions (the
 // kept experts, the drops) and the load fractions f_e are constants; the

@@ -1,39 +1,56 @@
 // Grouped expert GEMM on bf16 MFMA for gfx950 (the expert FFN of the MoE
-// layer: "Mixture of Experts Explained", "Making MoEs go brrr" — experts run
-// as grouped, not branchy, computation over expert-contiguous rows).
+// layer and its backward: "Mixture of Experts Explained", "Making MoEs go
+// brrr" — experts run as grouped, not branchy, computation over
+// expert-contiguous rows).
 //
-// out[rows of g] = epilogue(A[rows of g] . B[g]^T), A [rows, K] and B [g][n, K]
-// both K-contiguous (B in the [out, in] layout), fp32 accumulation.
+// Three operand layouts (GemmArgs::mode), fp32 accumulation:
+//  * GM_NT (forward): out[rows of g] = epi(A[rows] . B[g]^T), A [rows, K] and
+//    B [g][n, K] both K-contiguous (B in the [out, in] weight layout).
+//  * GM_NN (data gradients): out[rows of g] = epi(A[rows] . B[g]), B [g][K, n]:
+//    the same weights read as stored, K-major.
+//  * GM_KGROUP (weight gradients): out[g] = A_g^T . B_g, reduced over the M_g
+//    rows of group g; A [rows, M_fixed] and B [rows, N] are the saved
+//    activations as stored (K-major), out [g][M_fixed, N] fp32.
 //
 // Design for CDNA4:
 //  * 256 threads = 4 waves in a 2x2 grid; each wave owns a (BM/2) x (BN/2)
 //    sub-tile of every panel as (BM/64) x (BN/64) blocks of
 //    v_mfma_f32_32x32x16_bf16.  With BM = BN = 256 a wave issues 16 MFMAs per
-//    8 LDS fragment reads, half the LDS bytes per MFMA of a 64x64 wave tile.
+//    8 operand fragments, half the LDS bytes per MFMA of a 64x64 wave tile.
 //  * Global -> LDS with global_load_lds_dwordx4 (no staging registers): each
-//    wave instruction fills 1 KB = 8 tile rows of 64 bf16.  The eight 16-byte
-//    chunks of a row are XOR-swizzled by swz(row) = (row & 7) ^ ((row >> 3) & 1),
-//    which keeps a fragment read conflict-free whether the LDS serves 8 lanes
-//    (128 B) or 16 lanes (256 B) per pass; the swizzle is applied on the source
-//    address a lane loads, since the LDS slot is fixed by the lane.
-//    Two K stages of 64 are double buffered: the loads of stage k+1 are in
-//    flight while stage k multiplies.
+//    wave instruction fills 1 KB of LDS.  Two K stages of 64 are double
+//    buffered: the loads of stage k+1 are in flight while stage k multiplies.
+//  * A K-contiguous operand is staged as rows of 64 k (128 B) whose eight
+//    16-byte chunks are XOR-swizzled by (row & 7) ^ ((row >> 3) & 1); an MFMA
+//    fragment is one 16-byte LDS read per lane, conflict-free whether the LDS
+//    serves 8 or 16 lanes per pass.
+//  * A K-major operand is staged as 64 rows of k, each holding the tile's X
+//    columns (2*X bytes).  The 32-byte segments of row r are XOR-swizzled by
+//    kswz(r) = (r & 3) ^ ((r & 3) << 1) (0, 3, 6, 5); a fragment is two LDS
+//    transpose reads (ds_read_b64_tr_b16) per lane, which hand each lane four
+//    consecutive k of one column.  Each 16-lane read touches four rows at four
+//    distinct 32-byte bank groups, and the two 16-lane groups of a 32-lane
+//    pass at eight: no bank conflicts with 128- or 256-byte passes.
 //  * The tile plan (per-group prefix of tile counts) is computed by every
 //    workgroup from the device-resident row offsets: no planner launch and no
 //    host synchronisation.  Rows past a group's end are clamped to its last
-//    row on load and never stored.
+//    row on load and never stored; K rows past a group's end (weight
+//    gradients) are loaded from a zero block.
 //  * Workgroups are dealt round-robin to the 8 XCDs; block b takes logical
 //    tile (b % 8) * ceil(tiles / 8) + b / 8, so each XCD works through a
 //    contiguous run of tiles (same expert, consecutive n-tiles, m-tiles
 //    fastest) and its L2 holds the shared A rows and weight panels.
-//  * NP = 2 (SwiGLU): the gate rows n0.. and up rows up_off+n0.. of W13 are
-//    two B panels multiplied against one A tile; the epilogue forms
+//  * NP = 2 (SwiGLU forward): the gate rows n0.. and up rows up_off+n0.. of
+//    W13 are two B panels multiplied against one A tile; the epilogue forms
 //    silu(gate) * up directly.
 #include "gemm_common.hpp"
 
 namespace moe {
 
 constexpr int GB_BK = 64;
+
+// 16 zero bytes: the load source of K rows past the end of a group.
+__device__ uint4 g_zero16;
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
 // lane l writes lds_wave_base + 16*l; the LDS pointer must be wave-uniform.  (A
@@ -43,18 +60,41 @@ __device__ __forceinline__ void lds_load16(const void* src, void* lds_wave_base)
   __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
 }
 
-// Row mode: ts[g] = tiles of the groups before g (ceil(M_g/BM) * N/BN each).
-// K mode: ts[g] = padded rows of the groups before g (koff_g); the tile count
-// is G * (M_fixed/BM) * (N/BN).  Returns the number of tiles.
-template <int BM, int BN, int KG>
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// LDS transpose read of 16-bit data: within each 16-lane group, lane b+i
+// receives element i%4 of the four values addressed by lane b+4q+i/4, for
+// q = 0..3.  When lane b+4q+t points at row r0+q, columns c0+4t.. of a [k][x]
+// tile, lane b+i receives column c0+i of rows r0..r0+3.
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const char* p0, const char* p1) {
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Segment swizzle of K-major rows: distinct in the low two bits and in bits
+// 1..2 over any four consecutive rows.
+__device__ __forceinline__ int kswz(int r) { return (r & 3) ^ ((r & 3) << 1); }
+
+// K-major staging: lane l of load instruction q fills row q*(512/X) + l/(X/8)
+// (a k row of X columns, 2*X bytes), physical 16-byte chunk p = l % (X/8),
+// which holds logical chunk 2*((p >> 1) ^ kswz(row)) + (p & 1).
+template <int X>
+__device__ __forceinline__ void kmajor_slot(int q, int l, int& row, int& col) {
+  row = q * (512 / X) + l / (X / 8);
+  const int p = l % (X / 8);
+  col = 8 * (2 * ((p >> 1) ^ kswz(row)) + (p & 1));
+}
+
+// Row-grouped modes: ts[g] = tiles of the groups before g (ceil(M_g/BM) * N/BN
+// each).  Returns the number of tiles.
+template <int BM, int BN>
 __device__ __forceinline__ int32_t plan_tiles(const GemmArgs& g, int32_t* ts) {
   const int tid = threadIdx.x;
   const int NT = g.N / BN;
-  if constexpr (KG) {
-    ts[tid + 1] = tid < g.G ? ((g.offsets[tid + 1] - g.offsets[tid] + 63) & ~63) : 0;
-  } else {
-    ts[tid + 1] = tid < g.G ? int32_t(cdiv(g.offsets[tid + 1] - g.offsets[tid], BM)) * NT : 0;
-  }
+  ts[tid + 1] = tid < g.G ? int32_t(cdiv(g.offsets[tid + 1] - g.offsets[tid], BM)) * NT : 0;
   if (tid == 0) ts[0] = 0;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
@@ -63,22 +103,30 @@ __device__ __forceinline__ int32_t plan_tiles(const GemmArgs& g, int32_t* ts) {
     ts[tid + 1] += v;
     __syncthreads();
   }
-  if constexpr (KG) return g.G * (g.M_fixed / BM) * NT;
   return ts[g.G];
 }
 
-template <int BM, int BN, int NP, int EPI, int KG>
+template <int BM, int BN, int NP, int EPI, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gg_bf16_kernel(GemmArgs g) {
+  constexpr bool AK = MODE == GM_KGROUP;    // A staged K-major
+  constexpr bool BKM = MODE != GM_NT;       // B staged K-major
+  static_assert(NP == 1 || MODE == GM_NT, "two B panels only in the forward layout");
+  static_assert(BM >= 128 && BN >= 128, "K-major staging needs at least 8 segments per row");
   constexpr int ROWS = BM + NP * BN;     // 128-byte LDS rows per stage
   constexpr int STAGE = ROWS * 8;        // uint4 per stage
   constexpr int MI = BM / 64, NI = BN / 64;
   constexpr int A_INS = BM / 32, B_INS = BN / 32;  // load instructions per wave per panel
-  // Two stages of (BM + NP*BN) rows x 128 bytes: up to 128 KB, dynamic LDS.
+  // Two stages of (BM + NP*BN) x 128 bytes: up to 128 KB, dynamic LDS.
   extern __shared__ uint4 lds[];
   __shared__ int32_t ts[257];
 
-  const int32_t total = plan_tiles<BM, BN, KG>(g, ts);
+  int32_t total;
+  if constexpr (MODE == GM_KGROUP) {
+    total = g.G * (g.M_fixed / BM) * (g.N / BN);
+  } else {
+    total = plan_tiles<BM, BN>(g, ts);
+  }
   const int per = (total + 7) >> 3;
   const int bid = blockIdx.x;
   const int tile = (bid & 7) * per + (bid >> 3);
@@ -87,18 +135,19 @@ void gg_bf16_kernel(GemmArgs g) {
   int K;                                     // reduction length of this tile
   const uint16_t* A;
   const uint16_t* B;
-  if constexpr (KG) {
+  if constexpr (MODE == GM_KGROUP) {
     const int MT = g.M_fixed / BM;
     const int tpg = MT * (g.N / BN);
     tc.grp = tile / tpg;
     const int local = tile - tc.grp * tpg;
     tc.m0 = (local % MT) * BM;
     tc.n0 = (local / MT) * BN;
-    tc.row0 = 0;
+    tc.row0 = 0;                             // output rows of group grp
     tc.M = g.M_fixed;
-    K = ts[tc.grp + 1] - ts[tc.grp];
-    A = static_cast<const uint16_t*>(g.A) + int64_t(g.M_fixed) * ts[tc.grp];
-    B = static_cast<const uint16_t*>(g.B) + int64_t(g.N) * ts[tc.grp];
+    const int32_t r0 = g.offsets[tc.grp];
+    K = g.offsets[tc.grp + 1] - r0;
+    A = static_cast<const uint16_t*>(g.A) + int64_t(r0) * g.M_fixed;
+    B = static_cast<const uint16_t*>(g.B) + int64_t(r0) * g.N;
   } else {
     locate_tile(ts, g.offsets, g.G, tile, BM, BN, tc);
     K = g.K;
@@ -109,32 +158,70 @@ void gg_bf16_kernel(GemmArgs g) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wm = w >> 1, wn = w & 1;
 
-  // Lane l of a load instruction fills LDS slot l of an 8-row group: row l/8,
-  // physical chunk l%8, which holds logical chunk (l%8) ^ swz(row).  Every
-  // 8-row group this wave fills starts at a row with (row >> 3) & 1 == w & 1.
+  // ---- load sources.  K-contiguous: lane l of an instruction fills LDS slot l
+  // of an 8-row group: row l/8, physical chunk l%8, which holds logical chunk
+  // (l%8) ^ swz(row); every 8-row group this wave fills starts at a row with
+  // (row >> 3) & 1 == w & 1.
   const int lrow = l >> 3;
   const int lchunk = (l & 7) ^ lrow ^ (w & 1);
   const uint16_t* a_src[A_INS];
+  int a_krow[A_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
-    const int mr = min(tc.m0 + 8 * (w + 4 * i) + lrow, tc.M - 1);
-    a_src[i] = A + int64_t(tc.row0 + mr) * K + 8 * lchunk;
+    if constexpr (AK) {
+      int col;
+      kmajor_slot<BM>(w + 4 * i, l, a_krow[i], col);
+      a_src[i] = A + int64_t(a_krow[i]) * g.M_fixed + tc.m0 + col;
+    } else {
+      const int mr = min(tc.m0 + 8 * (w + 4 * i) + lrow, tc.M - 1);
+      a_src[i] = A + int64_t(tc.row0 + mr) * K + 8 * lchunk;
+      a_krow[i] = 0;
+    }
   }
-  const uint16_t* b_src[NP];
+  constexpr int NBS = BKM ? B_INS : NP;
+  const uint16_t* b_src[NBS];
+  int b_krow[NBS];
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
-    b_src[p] = B + int64_t(p * g.up_off + tc.n0 + 8 * w + lrow) * K + 8 * lchunk;
-  const int64_t b_step = int64_t(32) * K;   // 32 rows between a wave's B instructions
+  for (int i = 0; i < NBS; ++i) {
+    if constexpr (BKM) {
+      int col;
+      kmajor_slot<BN>(w + 4 * i, l, b_krow[i], col);
+      b_src[i] = B + int64_t(b_krow[i]) * g.N + tc.n0 + col;
+    } else {
+      b_src[i] = B + int64_t(i * g.up_off + tc.n0 + 8 * w + lrow) * K + 8 * lchunk;
+      b_krow[i] = 0;
+    }
+  }
+  const int64_t b_step = int64_t(32) * K;   // K-contiguous B: 32 rows between a wave's instructions
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(&g_zero16);
 
   auto issue = [&](int stage, int k0) {
     uint4* base = lds + stage * STAGE;
+    if constexpr (AK) {
+      const int64_t koff = int64_t(k0) * g.M_fixed;
 #pragma unroll
-    for (int i = 0; i < A_INS; ++i) lds_load16(a_src[i] + k0, base + (w + 4 * i) * 64);
+      for (int i = 0; i < A_INS; ++i)
+        lds_load16(k0 + a_krow[i] < K ? a_src[i] + koff : zero, base + (w + 4 * i) * 64);
+    } else {
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+      for (int i = 0; i < A_INS; ++i) lds_load16(a_src[i] + k0, base + (w + 4 * i) * 64);
+    }
+    uint4* bbase = base + BM * 8;
+    if constexpr (BKM) {
+      const int64_t koff = int64_t(k0) * g.N;
 #pragma unroll
-      for (int i = 0; i < B_INS; ++i)
-        lds_load16(b_src[p] + i * b_step + k0, base + (BM + p * BN) * 8 + (w + 4 * i) * 64);
+      for (int i = 0; i < B_INS; ++i) {
+        const uint16_t* s = b_src[i] + koff;
+        if constexpr (MODE == GM_KGROUP) s = k0 + b_krow[i] < K ? s : zero;
+        lds_load16(s, bbase + (w + 4 * i) * 64);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < B_INS; ++i)
+          lds_load16(b_src[p] + i * b_step + k0, bbase + p * BN * 8 + (w + 4 * i) * 64);
+    }
   };
 
   floatx16 acc[NP][MI][NI];
@@ -147,8 +234,22 @@ void gg_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[p][mi][ni][r] = 0.0f;
 
+  // ---- fragment addressing.  K-contiguous: lane l reads row fr = l%32,
+  // logical chunk 2s + fg (k = 16s + 8fg ..).  K-major: in 16-lane group gq,
+  // lane j reads row 16s + 8(gq >> 1) + 4h + j/4 at column xf + 16(gq & 1) + 4(j%4)
+  // for h = 0, 1; the segment (xf/16) ^ (gq & 1) ^ kswz(j/4) holds it.
   const int fr = l & 31, fg = l >> 5;
-  const int KT = K / GB_BK;
+  const int gq = l >> 4, jq = l & 15;
+  const int t32 = 32 * ((gq & 1) ^ kswz(jq >> 2));
+  int a_xo[MI], b_xo[NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) a_xo[mi] = (2 * (wm * (BM / 2) + mi * 32)) ^ t32;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) b_xo[ni] = (2 * (wn * (BN / 2) + ni * 32)) ^ t32;
+  const int a_lane = (8 * (gq >> 1) + (jq >> 2)) * (2 * BM) + 8 * (jq & 3);
+  const int b_lane = (8 * (gq >> 1) + (jq >> 2)) * (2 * BN) + 8 * (jq & 3);
+
+  const int KT = int(cdiv(K, GB_BK));
   // Each tile walks the K stages starting at its own offset (tile mod KT):
   // concurrent tiles read different K columns, which spreads their requests
   // over the L2 channels instead of having every CU hit the same channel with
@@ -157,6 +258,7 @@ void gg_bf16_kernel(GemmArgs g) {
   if (KT > 0) issue(0, krot * GB_BK);
   __syncthreads();
   // Fragments of K-step s+1 are read from LDS while the MFMAs of step s run.
+  constexpr int DS_PER_STEP = MI * (AK ? 2 : 1) + NP * NI * (BKM ? 2 : 1);
   bf16x8 af[2][MI], bfr[2][NP][NI];
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
@@ -165,19 +267,33 @@ void gg_bf16_kernel(GemmArgs g) {
       issue(cur ^ 1, (kn < KT ? kn : kn - KT) * GB_BK);
     }
     const uint4* As = lds + cur * STAGE;
+    const char* Ab = reinterpret_cast<const char*>(As);
+    const char* Bb = Ab + BM * 128;
 #pragma unroll
     for (int s = 0; s <= 4; ++s) {
       if (s < 4) {
         const int pc = (2 * s + fg) ^ (fr & 7) ^ ((fr >> 3) & 1);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          af[s & 1][mi] = __builtin_bit_cast(bf16x8, As[(wm * (BM / 2) + mi * 32 + fr) * 8 + pc]);
+        for (int mi = 0; mi < MI; ++mi) {
+          if constexpr (AK) {
+            const char* p = Ab + a_lane + a_xo[mi] + 16 * s * (2 * BM);
+            af[s & 1][mi] = lds_read_tr_pair(p, p + 4 * (2 * BM));
+          } else {
+            af[s & 1][mi] = __builtin_bit_cast(bf16x8, As[(wm * (BM / 2) + mi * 32 + fr) * 8 + pc]);
+          }
+        }
 #pragma unroll
         for (int p = 0; p < NP; ++p)
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            bfr[s & 1][p][ni] = __builtin_bit_cast(
-                bf16x8, As[(BM + p * BN + wn * (BN / 2) + ni * 32 + fr) * 8 + pc]);
+          for (int ni = 0; ni < NI; ++ni) {
+            if constexpr (BKM) {
+              const char* q = Bb + b_lane + b_xo[ni] + 16 * s * (2 * BN);
+              bfr[s & 1][p][ni] = lds_read_tr_pair(q, q + 4 * (2 * BN));
+            } else {
+              bfr[s & 1][p][ni] = __builtin_bit_cast(
+                  bf16x8, As[(BM + p * BN + wn * (BN / 2) + ni * 32 + fr) * 8 + pc]);
+            }
+          }
       }
       if (s > 0) {
         const int q = (s - 1) & 1;
@@ -193,7 +309,7 @@ void gg_bf16_kernel(GemmArgs g) {
       // Keep this order in the schedule: the LDS reads of step s, then the
       // MFMAs of step s-1 (otherwise the scheduler sinks every read next to
       // its use and each MFMA group waits on LDS latency).
-      if (s < 4) __builtin_amdgcn_sched_group_barrier(0x100, MI + NP * NI, 0);
+      if (s < 4) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_STEP, 0);
       if (s > 0) __builtin_amdgcn_sched_group_barrier(0x008, NP * MI * NI, 0);
     }
     __syncthreads();
@@ -228,7 +344,8 @@ void gg_bf16_kernel(GemmArgs g) {
         const int64_t row = tc.row0 + mr;
         const float4 v0 = *reinterpret_cast<const float4*>(cw + rl * CST + c4);
         if constexpr (EPI == EPI_STORE_F32) {
-          float* outp = static_cast<float*>(g.out) + (KG ? int64_t(tc.grp) * g.M_fixed * g.N : 0);
+          float* outp = static_cast<float*>(g.out) +
+                        (MODE == GM_KGROUP ? int64_t(tc.grp) * g.M_fixed * g.N : 0);
           *reinterpret_cast<float4*>(outp + row * g.N + n) = v0;
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           // v0 = dA[row, n..n+3]; h_in row = [gate | up]; out row = [dgate | dup]
@@ -274,56 +391,64 @@ void gg_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NP, int EPI, int KG>
+template <int BM, int BN, int NP, int EPI, int MODE>
 void launch_cfg(const GemmArgs& g, hipStream_t st) {
-  const int64_t bound = KG ? int64_t(g.G) * (g.M_fixed / BM) * (g.N / BN)
-                           : (cdiv(g.max_rows, BM) + g.G) * (g.N / BN);
+  const int64_t bound = MODE == GM_KGROUP ? int64_t(g.G) * (g.M_fixed / BM) * (g.N / BN)
+                                          : (cdiv(g.max_rows, BM) + g.G) * (g.N / BN);
   const unsigned grid = unsigned(cdiv(bound, 8) * 8);
   constexpr size_t lds_bytes = size_t(2) * (BM + NP * BN) * 128;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gg_bf16_kernel<BM, BN, NP, EPI, KG>),
+      reinterpret_cast<const void*>(&gg_bf16_kernel<BM, BN, NP, EPI, MODE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
   (void)attr;
-  gg_bf16_kernel<BM, BN, NP, EPI, KG><<<dim3(grid), dim3(256), lds_bytes, st>>>(g);
+  gg_bf16_kernel<BM, BN, NP, EPI, MODE><<<dim3(grid), dim3(256), lds_bytes, st>>>(g);
 }
 
-template <int EPI>
+template <int EPI, int MODE>
 static void launch_rows_np1(const GemmArgs& g, bool bm256, bool bn256, hipStream_t st) {
   if (bm256) {
-    if (bn256) launch_cfg<256, 256, 1, EPI, 0>(g, st); else launch_cfg<256, 128, 1, EPI, 0>(g, st);
+    if (bn256) launch_cfg<256, 256, 1, EPI, MODE>(g, st); else launch_cfg<256, 128, 1, EPI, MODE>(g, st);
   } else {
-    if (bn256) launch_cfg<128, 256, 1, EPI, 0>(g, st); else launch_cfg<128, 128, 1, EPI, 0>(g, st);
+    if (bn256) launch_cfg<128, 256, 1, EPI, MODE>(g, st); else launch_cfg<128, 128, 1, EPI, MODE>(g, st);
   }
 }
 
-// Tile shape (row mode): 256-row tiles when groups average at least 192 rows
+// Tile shape (row modes): 256-row tiles when groups average at least 192 rows
 // (fewer re-reads of each weight panel), else 128; 256-column tiles when that
-// still gives a tile per CU, else 128.  K mode: 256 x 256 when the output
-// dimensions allow it.
+// still gives a tile per CU, else 128.  K-grouped mode: 256 x 256 when the
+// output dimensions allow it.
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.G == 0) return hipSuccess;
-  if (g.kgroup) {
-    if (g.epi != EPI_STORE_F32) return hipErrorInvalidValue;
+  if (g.mode == GM_KGROUP) {
+    if (g.epi != EPI_STORE_F32 || g.M_fixed % 128 || g.N % 128) return hipErrorInvalidValue;
     const bool m256 = g.M_fixed % 256 == 0, n256 = g.N % 256 == 0;
-    if (m256 && n256) launch_cfg<256, 256, 1, EPI_STORE_F32, 1>(g, st);
-    else if (m256) launch_cfg<256, 128, 1, EPI_STORE_F32, 1>(g, st);
-    else if (n256) launch_cfg<128, 256, 1, EPI_STORE_F32, 1>(g, st);
-    else launch_cfg<128, 128, 1, EPI_STORE_F32, 1>(g, st);
+    if (m256 && n256) launch_cfg<256, 256, 1, EPI_STORE_F32, GM_KGROUP>(g, st);
+    else if (m256) launch_cfg<256, 128, 1, EPI_STORE_F32, GM_KGROUP>(g, st);
+    else if (n256) launch_cfg<128, 256, 1, EPI_STORE_F32, GM_KGROUP>(g, st);
+    else launch_cfg<128, 128, 1, EPI_STORE_F32, GM_KGROUP>(g, st);
     return hipGetLastError();
   }
   if (g.max_rows == 0) return hipSuccess;
+  if (g.N % 128 || g.K % GB_BK) return hipErrorInvalidValue;
   const int64_t avg = g.max_rows / g.G;
   const bool bm256 = avg >= 192;
   const int64_t mt = cdiv(g.max_rows, bm256 ? 256 : 128);
   const bool bn256 = (g.N % 256 == 0) && mt * (g.N / 256) >= 256;
+  if (g.mode == GM_NN) {
+    switch (g.epi) {
+      case EPI_STORE_F32: launch_rows_np1<EPI_STORE_F32, GM_NN>(g, bm256, bn256, st); break;
+      case EPI_SWIGLU_BWD: launch_rows_np1<EPI_SWIGLU_BWD, GM_NN>(g, bm256, bn256, st); break;
+      case EPI_GELU_BWD: launch_rows_np1<EPI_GELU_BWD, GM_NN>(g, bm256, bn256, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (g.epi) {
-    case EPI_STORE_F32: launch_rows_np1<EPI_STORE_F32>(g, bm256, bn256, st); break;
-    case EPI_GELU: launch_rows_np1<EPI_GELU>(g, bm256, bn256, st); break;
-    case EPI_SWIGLU_BWD: launch_rows_np1<EPI_SWIGLU_BWD>(g, bm256, bn256, st); break;
-    case EPI_GELU_BWD: launch_rows_np1<EPI_GELU_BWD>(g, bm256, bn256, st); break;
+    case EPI_STORE_F32: launch_rows_np1<EPI_STORE_F32, GM_NT>(g, bm256, bn256, st); break;
+    case EPI_GELU: launch_rows_np1<EPI_GELU, GM_NT>(g, bm256, bn256, st); break;
     case EPI_SWIGLU:
-      if (bm256) launch_cfg<256, 128, 2, EPI_SWIGLU, 0>(g, st);
-      else launch_cfg<128, 128, 2, EPI_SWIGLU, 0>(g, st);
+      if (bm256) launch_cfg<256, 128, 2, EPI_SWIGLU, GM_NT>(g, st);
+      else launch_cfg<128, 128, 2, EPI_SWIGLU, GM_NT>(g, st);
       break;
     default:
       return hipErrorInvalidValue;

@@ -52,29 +52,30 @@ hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int6
 // backward through the activation using the saved pre-activation h_in.
 enum Epi { EPI_STORE_F32 = 0, EPI_GELU = 1, EPI_SWIGLU = 2, EPI_SWIGLU_BWD = 3, EPI_GELU_BWD = 4 };
 
-// Row-grouped mode (kgroup = 0): group g owns rows offsets[g]..offsets[g+1]-1
-// of A and of out; out[rows] = epi(A[rows] . B[g]^T), A [rows, K], B [g][n, K].
-// K-grouped mode (kgroup = 1, weight gradients): group g reduces over its
-// Kp_g = roundup(M_g, 64) padded rows; A and B hold group-padded transposes
-// (A_g [M_fixed][Kp_g] at element M_fixed * koff_g, B_g [N][Kp_g] at N * koff_g)
-// and out_g [M_fixed][N] at g * M_fixed * N.  Empty groups write zeros.
+// Operand layouts of the grouped GEMM (group g owns rows offsets[g]..offsets[g+1]-1):
+//  GM_NT     out[rows] = epi(A[rows] . B[g]^T); A [rows, K], B [g][n, K]
+//  GM_NN     out[rows] = epi(A[rows] . B[g]);   A [rows, K], B [g][K, n]
+//  GM_KGROUP out[g] = A_g^T . B_g over the M_g rows of group g; A [rows, M_fixed],
+//            B [rows, N], out [g][M_fixed, N] fp32 (weight gradients; empty
+//            groups write zeros).
+enum GemmMode { GM_NT = 0, GM_KGROUP = 1, GM_NN = 2 };
 struct GemmArgs {
   const void* A;
   const void* B;
-  int64_t b_group_stride;   // row mode: elements between groups of B
+  int64_t b_group_stride;   // row modes: elements between groups of B
   const int32_t* offsets;   // [G+1] row offsets of the groups
   int G;
-  int64_t max_rows;         // row mode: upper bound of offsets[G] (launch size)
+  int64_t max_rows;         // row modes: upper bound of offsets[G] (launch size)
   int N;                    // output columns
-  int K;                    // row mode: reduction length
+  int K;                    // row modes: reduction length
   int up_off;               // SwiGLU: column offset of the up half (= F)
   int epi;
-  void* out;                // row mode [rows, N] (bf16 activations or fp32); K mode fp32
+  void* out;                // row modes [rows, N] (bf16 activations or fp32); K mode fp32
   void* h_save;             // nullable [rows, n_b] pre-activation (forward epilogues)
   const void* h_in;         // [rows, n_b] saved pre-activation (backward epilogues)
   int n_b;                  // row length of h_save / h_in (2F SwiGLU, F GELU)
   int32_t* tile_start;      // [G+1] scratch for the fp32 planner
-  int kgroup;               // 0: row-grouped, 1: K-grouped
+  int mode;                 // GemmMode
   int M_fixed;              // K mode: rows of each group's output
 };
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st);
@@ -88,13 +89,6 @@ hipError_t launch_fill_i32(int32_t* out, int n, int32_t v0, int32_t v1, int32_t 
 hipError_t launch_zero_i32(int32_t* out, int64_t n, hipStream_t st);
 hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, float target,
                               float gamma, hipStream_t st);
-
-// ------------------------------------------------------------------ transposes
-hipError_t launch_batched_transpose(const void* in, int batch, int R, int Cc, int elem_bytes,
-                                    void* out, hipStream_t st);
-// rows padded per group to multiples of 64; out needs Cc * (roundup(max_rows,64) + 64*G) elements
-hipError_t launch_group_transpose(const void* in, int Cc, const int32_t* offsets, int G,
-                                  int64_t max_rows, int elem_bytes, void* out, hipStream_t st);
 
 // ------------------------------------------------------------------ backward
 hipError_t launch_combine_bwd(const float* dy, const float* o, const int32_t* ros, const float* gate,
