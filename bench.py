@@ -32,6 +32,9 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--stage-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="finally run a plain device copy of this many MB (a known-size reference "
+                         "for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -191,6 +194,15 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+    if args.copy_mb > 0:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_mb} MB twice")
 
 
 if __name__ == "__main__":

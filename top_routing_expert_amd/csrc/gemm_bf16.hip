@@ -48,6 +48,7 @@
 namespace moe {
 
 constexpr int GB_BK = 64;
+constexpr int GB_WAVES = 8;   // waves per workgroup (one workgroup per CU)
 
 // 16 zero bytes: the load source of K rows past the end of a group.
 __device__ uint4 g_zero16;
@@ -89,34 +90,40 @@ __device__ __forceinline__ void kmajor_slot(int q, int l, int& row, int& col) {
 }
 
 // Row-grouped modes: ts[g] = tiles of the groups before g (ceil(M_g/BM) * N/BN
-// each).  Returns the number of tiles.
+// each), an inclusive scan by the first 256 threads (G <= 256).  Returns the
+// number of tiles.
 template <int BM, int BN>
 __device__ __forceinline__ int32_t plan_tiles(const GemmArgs& g, int32_t* ts) {
   const int tid = threadIdx.x;
+  const bool scan = tid < 256;
   const int NT = g.N / BN;
-  ts[tid + 1] = tid < g.G ? int32_t(cdiv(g.offsets[tid + 1] - g.offsets[tid], BM)) * NT : 0;
+  if (scan) ts[tid + 1] = tid < g.G ? int32_t(cdiv(g.offsets[tid + 1] - g.offsets[tid], BM)) * NT : 0;
   if (tid == 0) ts[0] = 0;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
-    const int32_t v = tid >= o ? ts[tid + 1 - o] : 0;
+    const int32_t v = scan && tid >= o ? ts[tid + 1 - o] : 0;
     __syncthreads();
-    ts[tid + 1] += v;
+    if (scan) ts[tid + 1] += v;
     __syncthreads();
   }
   return ts[g.G];
 }
 
-template <int BM, int BN, int NP, int EPI, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int NP, int EPI, int MODE, int WV>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(WV / 4, WV / 4)))
 void gg_bf16_kernel(GemmArgs g) {
   constexpr bool AK = MODE == GM_KGROUP;    // A staged K-major
   constexpr bool BKM = MODE != GM_NT;       // B staged K-major
   static_assert(NP == 1 || MODE == GM_NT, "two B panels only in the forward layout");
   static_assert(BM >= 128 && BN >= 128, "K-major staging needs at least 8 segments per row");
+  static_assert(WV == 4 || WV == 8, "4 or 8 waves");
+  constexpr int NWN = WV / 2;            // waves along n (2 along m)
+  constexpr int WTN = BN / NWN;          // wave tile width
   constexpr int ROWS = BM + NP * BN;     // 128-byte LDS rows per stage
   constexpr int STAGE = ROWS * 8;        // uint4 per stage
-  constexpr int MI = BM / 64, NI = BN / 64;
-  constexpr int A_INS = BM / 32, B_INS = BN / 32;  // load instructions per wave per panel
+  constexpr int MI = BM / 64, NI = WTN / 32;
+  constexpr int A_INS = BM / (8 * WV), B_INS = BN / (8 * WV);  // load instructions per wave per panel
+  static_assert(NI >= 1 && A_INS >= 1 && B_INS >= 1, "tile too small for the wave count");
   // Two stages of (BM + NP*BN) x 128 bytes: up to 128 KB, dynamic LDS.
   extern __shared__ uint4 lds[];
   __shared__ int32_t ts[257];
@@ -156,12 +163,12 @@ void gg_bf16_kernel(GemmArgs g) {
   }
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / NWN, wn = w % NWN;
 
-  // ---- load sources.  K-contiguous: lane l of an instruction fills LDS slot l
-  // of an 8-row group: row l/8, physical chunk l%8, which holds logical chunk
-  // (l%8) ^ swz(row); every 8-row group this wave fills starts at a row with
-  // (row >> 3) & 1 == w & 1.
+  // ---- load sources.  Instruction i of wave w fills the 1 KB LDS block
+  // q = w + WV*i of its panel.  K-contiguous: lane l fills slot l of the
+  // 8-row group q: row l/8, physical chunk l%8, which holds logical chunk
+  // (l%8) ^ swz(row); the group starts at a row with (row >> 3) & 1 == w & 1.
   const int lrow = l >> 3;
   const int lchunk = (l & 7) ^ lrow ^ (w & 1);
   const uint16_t* a_src[A_INS];
@@ -170,10 +177,10 @@ void gg_bf16_kernel(GemmArgs g) {
   for (int i = 0; i < A_INS; ++i) {
     if constexpr (AK) {
       int col;
-      kmajor_slot<BM>(w + 4 * i, l, a_krow[i], col);
+      kmajor_slot<BM>(w + WV * i, l, a_krow[i], col);
       a_src[i] = A + int64_t(a_krow[i]) * g.M_fixed + tc.m0 + col;
     } else {
-      const int mr = min(tc.m0 + 8 * (w + 4 * i) + lrow, tc.M - 1);
+      const int mr = min(tc.m0 + 8 * (w + WV * i) + lrow, tc.M - 1);
       a_src[i] = A + int64_t(tc.row0 + mr) * K + 8 * lchunk;
       a_krow[i] = 0;
     }
@@ -185,14 +192,14 @@ void gg_bf16_kernel(GemmArgs g) {
   for (int i = 0; i < NBS; ++i) {
     if constexpr (BKM) {
       int col;
-      kmajor_slot<BN>(w + 4 * i, l, b_krow[i], col);
+      kmajor_slot<BN>(w + WV * i, l, b_krow[i], col);
       b_src[i] = B + int64_t(b_krow[i]) * g.N + tc.n0 + col;
     } else {
       b_src[i] = B + int64_t(i * g.up_off + tc.n0 + 8 * w + lrow) * K + 8 * lchunk;
       b_krow[i] = 0;
     }
   }
-  const int64_t b_step = int64_t(32) * K;   // K-contiguous B: 32 rows between a wave's instructions
+  const int64_t b_step = int64_t(8 * WV) * K;   // K-contiguous B: rows between a wave's instructions
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(&g_zero16);
 
   auto issue = [&](int stage, int k0) {
@@ -201,10 +208,10 @@ void gg_bf16_kernel(GemmArgs g) {
       const int64_t koff = int64_t(k0) * g.M_fixed;
 #pragma unroll
       for (int i = 0; i < A_INS; ++i)
-        lds_load16(k0 + a_krow[i] < K ? a_src[i] + koff : zero, base + (w + 4 * i) * 64);
+        lds_load16(k0 + a_krow[i] < K ? a_src[i] + koff : zero, base + (w + WV * i) * 64);
     } else {
 #pragma unroll
-      for (int i = 0; i < A_INS; ++i) lds_load16(a_src[i] + k0, base + (w + 4 * i) * 64);
+      for (int i = 0; i < A_INS; ++i) lds_load16(a_src[i] + k0, base + (w + WV * i) * 64);
     }
     uint4* bbase = base + BM * 8;
     if constexpr (BKM) {
@@ -213,14 +220,14 @@ void gg_bf16_kernel(GemmArgs g) {
       for (int i = 0; i < B_INS; ++i) {
         const uint16_t* s = b_src[i] + koff;
         if constexpr (MODE == GM_KGROUP) s = k0 + b_krow[i] < K ? s : zero;
-        lds_load16(s, bbase + (w + 4 * i) * 64);
+        lds_load16(s, bbase + (w + WV * i) * 64);
       }
     } else {
 #pragma unroll
       for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
-          lds_load16(b_src[p] + i * b_step + k0, bbase + p * BN * 8 + (w + 4 * i) * 64);
+          lds_load16(b_src[p] + i * b_step + k0, bbase + p * BN * 8 + (w + WV * i) * 64);
     }
   };
 
@@ -245,7 +252,7 @@ void gg_bf16_kernel(GemmArgs g) {
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) a_xo[mi] = (2 * (wm * (BM / 2) + mi * 32)) ^ t32;
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni) b_xo[ni] = (2 * (wn * (BN / 2) + ni * 32)) ^ t32;
+  for (int ni = 0; ni < NI; ++ni) b_xo[ni] = (2 * (wn * WTN + ni * 32)) ^ t32;
   const int a_lane = (8 * (gq >> 1) + (jq >> 2)) * (2 * BM) + 8 * (jq & 3);
   const int b_lane = (8 * (gq >> 1) + (jq >> 2)) * (2 * BN) + 8 * (jq & 3);
 
@@ -291,7 +298,7 @@ void gg_bf16_kernel(GemmArgs g) {
               bfr[s & 1][p][ni] = lds_read_tr_pair(q, q + 4 * (2 * BN));
             } else {
               bfr[s & 1][p][ni] = __builtin_bit_cast(
-                  bf16x8, As[(BM + p * BN + wn * (BN / 2) + ni * 32 + fr) * 8 + pc]);
+                  bf16x8, As[(BM + p * BN + wn * WTN + ni * 32 + fr) * 8 + pc]);
             }
           }
       }
@@ -312,16 +319,20 @@ void gg_bf16_kernel(GemmArgs g) {
       if (s < 4) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_STEP, 0);
       if (s > 0) __builtin_amdgcn_sched_group_barrier(0x008, NP * MI * NI, 0);
     }
+    // Every MFMA of this stage is issued before the wait for the next stage's
+    // loads (the compiler would otherwise sink half of them past the barrier,
+    // where no load is in flight).
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
 
   // Epilogue through LDS (free after the last barrier).  Per 32-row block mi,
   // each wave writes its accumulators (register r of lane l holds row
   // 8*(r/4) + 4*(l/32) + r%4, column l%32 of a 32x32 block) into its own
-  // [NP][32][BN/2 + 4] fp32 region, then reads rows back four columns per lane
+  // [NP][32][WTN + 4] fp32 region, then reads rows back four columns per lane
   // and stores 16 bytes (fp32) or 8 bytes (bf16) per lane, row-contiguous.
-  constexpr int CST = BN / 2 + 4;
-  constexpr int LPR = (BN / 2) / 4;   // lanes per row
+  constexpr int CST = WTN + 4;
+  constexpr int LPR = WTN / 4;        // lanes per row
   constexpr int RPI = 64 / LPR;       // rows per read-back step
   float* cw = reinterpret_cast<float*>(lds) + w * (NP * 32 * CST);
 #pragma unroll
@@ -335,7 +346,7 @@ void gg_bf16_kernel(GemmArgs g) {
           cw[(p * 32 + 8 * (r >> 2) + 4 * fg + (r & 3)) * CST + ni * 32 + fr] = acc[p][mi][ni][r];
     __syncthreads();
     const int c4 = (l % LPR) * 4;
-    const int n = tc.n0 + wn * (BN / 2) + c4;
+    const int n = tc.n0 + wn * WTN + c4;
 #pragma unroll 4
     for (int it = 0; it < 32 / RPI; ++it) {
       const int rl = it * RPI + l / LPR;
@@ -391,17 +402,17 @@ void gg_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int NP, int EPI, int MODE>
+template <int BM, int BN, int NP, int EPI, int MODE, int WV = GB_WAVES>
 void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int64_t bound = MODE == GM_KGROUP ? int64_t(g.G) * (g.M_fixed / BM) * (g.N / BN)
                                           : (cdiv(g.max_rows, BM) + g.G) * (g.N / BN);
   const unsigned grid = unsigned(cdiv(bound, 8) * 8);
   constexpr size_t lds_bytes = size_t(2) * (BM + NP * BN) * 128;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gg_bf16_kernel<BM, BN, NP, EPI, MODE>),
+      reinterpret_cast<const void*>(&gg_bf16_kernel<BM, BN, NP, EPI, MODE, WV>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
   (void)attr;
-  gg_bf16_kernel<BM, BN, NP, EPI, MODE><<<dim3(grid), dim3(256), lds_bytes, st>>>(g);
+  gg_bf16_kernel<BM, BN, NP, EPI, MODE, WV><<<dim3(grid), dim3(64 * WV), lds_bytes, st>>>(g);
 }
 
 template <int EPI, int MODE>
