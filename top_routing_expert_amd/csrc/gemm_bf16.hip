@@ -75,6 +75,23 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const char* p0, const char* p
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Ring depth: as many 64-deep K stages as fit in 144 KB of LDS, at most 4.
+__host__ __device__ constexpr int gb_stages(int BM, int BN, int NP) {
+  return (BM + NP * BN) * 128 <= 32768 ? 4 : ((BM + NP * BN) * 128 <= 49152 ? 3 : 2);
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding load); LDS accesses are not moved across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Segment swizzle of K-major rows: distinct in the low two bits and in bits
 // 1..2 over any four consecutive rows.
 __device__ __forceinline__ int kswz(int r) { return (r & 3) ^ ((r & 3) << 1); }
@@ -124,7 +141,9 @@ void gg_bf16_kernel(GemmArgs g) {
   constexpr int MI = BM / 64, NI = WTN / 32;
   constexpr int A_INS = BM / (8 * WV), B_INS = BN / (8 * WV);  // load instructions per wave per panel
   static_assert(NI >= 1 && A_INS >= 1 && B_INS >= 1, "tile too small for the wave count");
-  // Two stages of (BM + NP*BN) x 128 bytes: up to 128 KB, dynamic LDS.
+  constexpr int NS = gb_stages(BM, BN, NP);
+  constexpr int INS = A_INS + NP * B_INS;   // load instructions per wave per stage
+  // NS stages of (BM + NP*BN) x 128 bytes (at most 144 KB), dynamic LDS.
   extern __shared__ uint4 lds[];
   __shared__ int32_t ts[257];
 
@@ -262,17 +281,31 @@ void gg_bf16_kernel(GemmArgs g) {
   // over the L2 channels instead of having every CU hit the same channel with
   // the same power-of-two row stride.  The sum order depends only on the tile.
   const int krot = KT > 0 ? tile % KT : 0;
-  if (KT > 0) issue(0, krot * GB_BK);
-  __syncthreads();
+  auto kcol = [&](int j) {
+    const int kn = j + krot;
+    return (kn < KT ? kn : kn - KT) * GB_BK;
+  };
+  // NS-stage ring: the loads of K steps kt+1 .. kt+NS-2 are in flight while
+  // step kt multiplies, and step kt+NS-1 is issued into the slot step kt-1
+  // has just released.
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < KT) issue(j, kcol(j));
   // Fragments of K-step s+1 are read from LDS while the MFMAs of step s run.
   constexpr int DS_PER_STEP = MI * (AK ? 2 : 1) + NP * NI * (BKM ? 2 : 1);
   bf16x8 af[2][MI], bfr[2][NP][NI];
+  int cur = 0, nxt = NS - 1;
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) {
-      const int kn = kt + 1 + krot;
-      issue(cur ^ 1, (kn < KT ? kn : kn - KT) * GB_BK);
-    }
+    // This wave's loads of step kt have landed once no more than the loads of
+    // the steps issued after it are outstanding (loads complete in order).
+    const int after = min(NS - 2, KT - 1 - kt);
+    if (NS >= 4 && after >= 2) wait_vmcnt<(NS >= 4 ? 2 : 0) * INS>();
+    else if (NS >= 3 && after >= 1) wait_vmcnt<(NS >= 3 ? 1 : 0) * INS>();
+    else wait_vmcnt<0>();
+    // Every wave's loads of step kt have landed and every wave has finished
+    // reading step kt-1 (its MFMAs were issued before this point).
+    lds_barrier();
+    if (kt + NS - 1 < KT) issue(nxt, kcol(kt + NS - 1));
     const uint4* As = lds + cur * STAGE;
     const char* Ab = reinterpret_cast<const char*>(As);
     const char* Bb = Ab + BM * 128;
@@ -319,12 +352,12 @@ void gg_bf16_kernel(GemmArgs g) {
       if (s < 4) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_STEP, 0);
       if (s > 0) __builtin_amdgcn_sched_group_barrier(0x008, NP * MI * NI, 0);
     }
-    // Every MFMA of this stage is issued before the wait for the next stage's
-    // loads (the compiler would otherwise sink half of them past the barrier,
-    // where no load is in flight).
+    // Every MFMA of this stage is issued before the next wait and barrier.
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    cur = cur + 1 == NS ? 0 : cur + 1;
+    nxt = nxt + 1 == NS ? 0 : nxt + 1;
   }
+  __syncthreads();
 
   // Epilogue through LDS (free after the last barrier).  Per 32-row block mi,
   // each wave writes its accumulators (register r of lane l holds row
@@ -407,7 +440,7 @@ void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int64_t bound = MODE == GM_KGROUP ? int64_t(g.G) * (g.M_fixed / BM) * (g.N / BN)
                                           : (cdiv(g.max_rows, BM) + g.G) * (g.N / BN);
   const unsigned grid = unsigned(cdiv(bound, 8) * 8);
-  constexpr size_t lds_bytes = size_t(2) * (BM + NP * BN) * 128;
+  constexpr size_t lds_bytes = size_t(gb_stages(BM, BN, NP)) * (BM + NP * BN) * 128;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&gg_bf16_kernel<BM, BN, NP, EPI, MODE, WV>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
