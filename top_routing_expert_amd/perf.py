@@ -11,6 +11,9 @@ FP32 instructions.
 
 from __future__ import annotations
 
+import hashlib
+import os
+
 from .presets import Preset
 
 PEAK_HBM_GBS = 8000.0
@@ -64,3 +67,17 @@ def combine_bytes(p: Preset, R: int) -> float:
     if p.F_shared:
         b += p.T * p.d * 4
     return float(b)
+
+
+# Sources of the grouped-GEMM kernels: measured hardware byte counts of the
+# expert FFN are valid only for the sources they were taken on.
+GEMM_SOURCES = ("gemm_bf16.hip", "gemm_common.hpp", "common.hpp", "kernels.hpp")
+
+
+def gemm_source_sha256() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for f in GEMM_SOURCES:
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
