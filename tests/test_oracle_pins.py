@@ -375,14 +375,15 @@ def _objective(p, inp, dy):
     return float(np.sum(dy * f["y"]) + f["aux"] + f["zloss"]), f
 
 
-@pytest.mark.parametrize("kind,act,cf,shared", [
-    ("softmax", "swiglu", 0.0, 0), ("sigmoid", "swiglu", 0.0, 6),
-    ("sqrt_softplus", "swiglu", 0.0, 6), ("softmax", "gelu", 0.75, 0),
-    ("sqrt_softplus", "gelu", 0.75, 6)])
-def test_backward_finite_differences(kind, act, cf, shared):
+@pytest.mark.parametrize("kind,act,cf,shared,routing", [
+    ("softmax", "swiglu", 0.0, 0, "topk"), ("sigmoid", "swiglu", 0.0, 6, "topk"),
+    ("sqrt_softplus", "swiglu", 0.0, 6, "topk"), ("softmax", "gelu", 0.75, 0, "topk"),
+    ("sqrt_softplus", "gelu", 0.75, 6, "topk"), ("sigmoid", "swiglu", 0.0, 6, "uniform")])
+def test_backward_finite_differences(kind, act, cf, shared, routing):
     p = tiny(T=24, d=10, E=5, k=2, F=6, score=kind, act=act, capacity_factor=cf,
              F_shared=shared, gate_scale=math.sqrt(2.0), aux_coef=0.3, z_coef=0.2,
-             sel_bias_std=0.05, zipf_s=1.1, renorm=kind != "softmax" or act == "swiglu")
+             sel_bias_std=0.05, zipf_s=1.1, renorm=kind != "softmax" or act == "swiglu",
+             routing=routing)
     inp = synth.make_inputs(p, seed=17, with_dy=True)
     inp = {k_: (None if v is None else np.asarray(v, np.float64)) for k_, v in inp.items()}
     dy = inp["dy"]
@@ -411,3 +412,55 @@ def test_backward_finite_differences(kind, act, cf, shared):
             fd = (Jp - Jm) / (2 * eps)
             an = grads[gname].reshape(-1)[i]
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (pname, i, fd, an)
+
+
+# ---------------------------------------------------------------------------
+# forced-uniform routing (the handbook's balanced baseline)
+# ---------------------------------------------------------------------------
+def test_uniform_routing_round_robin_balanced_distinct():
+    """Read slot by slot (token-major), the experts cycle 0..E-1; every expert
+    gets T*k/E slots and a token's k experts are distinct."""
+    p = tiny(T=48, E=6, k=4, routing="uniform")
+    inp = synth.make_inputs(p, seed=21)
+    r = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, routing="uniform")
+    flat = r["idx"].reshape(-1)
+    assert np.array_equal(flat[:p.E], np.arange(p.E))
+    assert np.array_equal(flat[p.E:], flat[:-p.E])
+    assert (r["counts"] == p.T * p.k // p.E).all()
+    assert all(len(set(row)) == p.k for row in r["idx"].tolist())
+    assert not r["near_tie"].any()
+
+
+def test_uniform_routing_aux_loss_is_coefficient():
+    """f_e = 1/E for every expert, so L_aux = a * E * sum_e P_e / E = a."""
+    p = tiny(T=60, E=5, k=2, routing="uniform", aux_coef=0.37)
+    inp = synth.make_inputs(p, seed=22)
+    for kind in ("softmax", "sigmoid", "sqrt_softplus"):
+        r = orc.route(inp["x"], inp["Wg"], p.k, kind, True, 1.0, aux_coef=p.aux_coef,
+                      routing="uniform")
+        assert abs(r["aux"] - float(np.float32(p.aux_coef))) < 1e-14   # coefficients are fp32
+
+
+@pytest.mark.parametrize("kind,renorm", [("softmax", True), ("sigmoid", False)])
+def test_uniform_routing_layer_equals_dense_bruteforce(kind, renorm):
+    """y_t = sum_e G_te E_e(x_t) with G the scores on the forced experts only."""
+    p = tiny(T=30, E=5, k=2, score=kind, renorm=renorm, gate_scale=1.5, routing="uniform",
+             capacity_factor=0.0)
+    inp = synth.make_inputs(p, seed=23)
+    f = orc.layer_fwd(p, inp)
+    z = inp["x"].astype(np.float64) @ inp["Wg"]
+    s = sps.softmax(z, axis=1) if kind == "softmax" else sps.expit(z)
+    mask = np.zeros((p.T, p.E), bool)
+    e = 0
+    for t in range(p.T):          # hand the slots out one by one, cycling over experts
+        for _ in range(p.k):
+            mask[t, e] = True
+            e = (e + 1) % p.E
+    G = np.where(mask, s, 0.0)
+    if renorm:
+        G = G / G.sum(axis=1, keepdims=True)
+    G = G * np.float32(1.5)
+    y = np.zeros((p.T, p.d))
+    for e in range(p.E):
+        y = y + G[:, e:e + 1] * _torch_ffn(inp["x"], inp["W13"][e], inp["W2"][e], p.act)
+    np.testing.assert_allclose(f["y"], y, rtol=1e-11, atol=1e-12)
