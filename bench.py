@@ -31,6 +31,10 @@ def parse():
     ap.add_argument("--config", default="c2", help="preset name (c1..c5)")
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--stage-iters", type=int, default=20)
+    ap.add_argument("--routing", default="topk", choices=["topk", "uniform"],
+                    help="expert choice: learned top-k, or the forced-uniform assignment")
+    ap.add_argument("--k", type=int, default=None,
+                    help="experts per token (serve the layer with fewer experts than its preset)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="finally run a plain device copy of this many MB (a known-size reference "
@@ -51,6 +55,9 @@ def measured_traffic(p, perf):
         d = json.load(fh)
     if d.get("source_sha256") != perf.gemm_source_sha256() or d.get("workload") != p.name:
         return None
+    from top_routing_expert_amd import presets
+    if p != presets.get(p.name):          # a modified workload (routing, k)
+        return None
     return d["hbm_bytes_per_launch"]
 
 
@@ -67,7 +74,10 @@ def main():
     import torch
     from top_routing_expert_amd import binding as B, perf, presets, synth
 
-    p = presets.get(args.config)
+    over = dict(routing=args.routing)
+    if args.k is not None:
+        over["k"] = args.k
+    p = presets.get(args.config, **over)
     train = p.train or not args.fwd_only
     dev = torch.device("cuda:0")
     log(f"[bench] generating {p.name} inputs")
@@ -213,7 +223,8 @@ def main():
         "dtype": "bf16" if p.dtype == "bf16" else "f32",
         "data": "synthetic (seeded Gaussian inputs and weights)",
         "config": {"workload": f"{p.name}: T={p.T} d={p.d} E={p.E} top-{p.k} F={p.F} {p.act} "
-                               f"{p.score} CF={p.capacity_factor} shared={p.F_shared}",
+                               f"{p.score} CF={p.capacity_factor} shared={p.F_shared}"
+                               + ("" if p.routing == "topk" else f" routing={p.routing}"),
                    "step": "forward+backward" if train else "forward",
                    "global_batch": p.T, "parallelism": "single GPU"},
         "roofline": roof,

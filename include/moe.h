@@ -73,13 +73,23 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
  * bf16: d, F and F_shared multiples of 128; fp32: d, F, F_shared multiples of 4. */
 typedef struct { int64_t T, d, E, k, F, F_shared; } moe_dims;
 
+/* How the k experts of a token are chosen.
+ * MOE_ROUTING_TOPK: the k largest selection scores (score + selection bias), ties to
+ *   the lower expert index ("Mixture of Experts Explained", "What is sparsity?", KeepTopK).
+ * MOE_ROUTING_UNIFORM: forced-uniform assignment, slot j of token t to expert
+ *   (t*k + j) mod E, the balanced baseline of the Ultimate MoE Training Handbook digest
+ *   ("the three hard parts", 2); gates and losses still come from the router's scores. */
+typedef enum { MOE_ROUTING_TOPK = 0, MOE_ROUTING_UNIFORM = 1 } moe_routing;
+
 /* score: moe_score; act: moe_act; dtype: moe_dtype;
  * renorm != 0: kept gates are divided by their sum, then multiplied by gate_scale;
  * capacity_factor <= 0: no capacity limit, else C = ceil(cf * T * k / E) slots per expert;
- * aux_coef, z_coef: load-balance and z-loss coefficients (0 = not computed). */
+ * aux_coef, z_coef: load-balance and z-loss coefficients (0 = not computed);
+ * routing: moe_routing (0 = top-k). */
 typedef struct {
   int32_t score, act, dtype, renorm;
   float gate_scale, capacity_factor, aux_coef, z_coef;
+  int32_t routing;
 } moe_opts;
 
 typedef struct {

@@ -79,7 +79,8 @@ def _route_status(p, **kw):
     ("k", 0, B.MOE_ERR_INVALID_ARG), ("k", 65, B.MOE_ERR_INVALID_ARG), ("k", 17, B.MOE_ERR_UNSUPPORTED),
     ("E", 300, B.MOE_ERR_UNSUPPORTED), ("T", -1, B.MOE_ERR_INVALID_ARG),
     ("d", 100, B.MOE_ERR_UNSUPPORTED), ("score", 7, B.MOE_ERR_INVALID_ARG),
-    ("dtype", 5, B.MOE_ERR_INVALID_ARG), ("capacity_factor", float("nan"), B.MOE_ERR_INVALID_ARG)])
+    ("dtype", 5, B.MOE_ERR_INVALID_ARG), ("capacity_factor", float("nan"), B.MOE_ERR_INVALID_ARG),
+    ("routing", 2, B.MOE_ERR_INVALID_ARG), ("routing", -1, B.MOE_ERR_INVALID_ARG)])
 def test_argument_errors_are_synchronous(L, field, value, status):
     p = presets.get("c4")
     assert _route_status(p, **{field: value}) == status

@@ -272,6 +272,51 @@ def test_layer_fwd_parity(name):
     print(f"{name}: layer y max-abs/rms {r:.2e} on {len(tokens)} tokens; drops {drops}")
 
 
+# --------------------------------------------------------------------------- routing studies
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_uniform_routing_parity(name):
+    """Forced-uniform routing: indices and counts exact, gates and losses to
+    1e-5, the layer on sampled tokens to the bf16 bar."""
+    p, inp, x, w = case(name, routing="uniform")
+    out = B.route(p, x, w.Wg, w.offset, w.sel_bias)
+    torch.cuda.synchronize()
+    ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                    inp["sel_bias"], p.aux_coef, p.z_coef, routing="uniform")
+    np.testing.assert_array_equal(out["idx"].cpu().numpy(), ref["idx"])
+    np.testing.assert_array_equal(out["counts"].cpu().numpy(), ref["counts"])
+    np.testing.assert_allclose(out["gate"].cpu().numpy(), ref["g"], rtol=1e-5, atol=1e-12)
+    np.testing.assert_allclose(out["losses"].cpu().numpy(), [ref["aux"], ref["zloss"]], rtol=1e-5,
+                               atol=0)
+    saved = B.alloc_saved(p, DEV)
+    y = B.layer_fwd(p, w, x, saved=saved)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(saved["topk_idx"].cpu().numpy(), ref["idx"])
+    rng = np.random.default_rng(4)
+    tokens = np.unique(np.concatenate([[0, p.T - 1], rng.integers(0, p.T, size=32)]))
+    r = _assert_bf16_close(y.cpu().numpy()[tokens], _layer_ref_sampled(p, inp, saved, tokens),
+                           f"{name} uniform y")
+    print(f"{name} uniform: layer y max-abs/rms {r:.2e}")
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_reduced_k_serving(k):
+    """The c4 layer served with fewer experts per token than it was built for."""
+    p, inp, x, w = case("c4", k=k)
+    out = B.route(p, x, w.Wg, w.offset, w.sel_bias)
+    torch.cuda.synchronize()
+    ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                    inp["sel_bias"])
+    check_route(p, out, ref)
+    saved = B.alloc_saved(p, DEV)
+    y = B.layer_fwd(p, w, x, saved=saved)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    tokens = np.unique(np.concatenate([[0, p.T - 1], rng.integers(0, p.T, size=32)]))
+    r = _assert_bf16_close(y.cpu().numpy()[tokens], _layer_ref_sampled(p, inp, saved, tokens),
+                           f"c4 k={k} y")
+    print(f"c4 served at k={k}: layer y max-abs/rms {r:.2e}")
+
+
 @pytest.mark.parametrize("over", [dict(T=200), dict(T=1), dict(k=8, renorm=False),
                                   dict(E=1, k=1, renorm=False), dict(score="sigmoid", F_shared=64),
                                   dict(score="sqrt_softplus", act="gelu", T=333, capacity_factor=0.7)])

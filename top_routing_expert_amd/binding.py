@@ -23,6 +23,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
 ACT = {"swiglu": 0, "gelu": 1}
 DTYPE = {"f32": 0, "bf16": 1}
+ROUTING = {"topk": 0, "uniform": 1}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -39,7 +40,8 @@ class Dims(C.Structure):
 class Opts(C.Structure):
     _fields_ = [("score", C.c_int32), ("act", C.c_int32), ("dtype", C.c_int32),
                 ("renorm", C.c_int32), ("gate_scale", C.c_float),
-                ("capacity_factor", C.c_float), ("aux_coef", C.c_float), ("z_coef", C.c_float)]
+                ("capacity_factor", C.c_float), ("aux_coef", C.c_float), ("z_coef", C.c_float),
+                ("routing", C.c_int32)]
 
 
 class Weights(C.Structure):
@@ -114,7 +116,7 @@ def dims_of(p: Preset, T: Optional[int] = None) -> Dims:
 
 def opts_of(p: Preset) -> Opts:
     return Opts(SCORE[p.score], ACT[p.act], DTYPE[p.dtype], int(p.renorm), p.gate_scale,
-                p.capacity_factor, p.aux_coef, p.z_coef)
+                p.capacity_factor, p.aux_coef, p.z_coef, ROUTING[p.routing])
 
 
 def capacity(p: Preset, T: Optional[int] = None) -> int:

@@ -38,6 +38,7 @@ int check_dims(const moe_dims* d, const moe_opts* o) {
   if (!d || !o) return MOE_ERR_INVALID_ARG;
   if (o->dtype != MOE_DTYPE_F32 && o->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (o->score < MOE_SCORE_SOFTMAX || o->score > MOE_SCORE_SQRT_SOFTPLUS) return MOE_ERR_INVALID_ARG;
+  if (o->routing < MOE_ROUTING_TOPK || o->routing > MOE_ROUTING_UNIFORM) return MOE_ERR_INVALID_ARG;
   if (o->act != MOE_ACT_SWIGLU && o->act != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
   if (d->T < 0 || d->E < 1 || d->k < 1 || d->k > d->E || d->F_shared < 0) return MOE_ERR_INVALID_ARG;
   if (!isfinite(o->gate_scale) || !isfinite(o->capacity_factor) || !isfinite(o->aux_coef) ||
@@ -162,6 +163,7 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
   a.k = int(d->k);
   a.EP = rw.EP;
   a.score = o->score;
+  a.routing = o->routing;
   a.renorm = o->renorm != 0;
   a.gate_scale = o->gate_scale;
   a.idx = idx;

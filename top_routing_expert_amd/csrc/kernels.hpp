@@ -16,6 +16,7 @@ struct RouteArgs {
   const float* bias;        // nullable [E]
   int T, d, E, k, EP;
   int score, renorm;
+  int routing;              // 0 top-k, 1 forced-uniform (slot j of token t -> (t*k + j) mod E)
   float gate_scale;
   int32_t* idx;             // [T, k]
   float* gate;              // [T, k]

@@ -129,11 +129,16 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
       isel[j] = 0;
       gsel[j] = 0.0f;
       if (j < k) {
-        uint64_t best = 0;
+        int e;
+        if (a.routing == 1) {
+          e = int((int64_t(t) * k + j) % E);
+        } else {
+          uint64_t best = 0;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-        best = group_max_u64<LG>(best);
-        const int e = int(~uint32_t(best));
+          for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+          best = group_max_u64<LG>(best);
+          e = int(~uint32_t(best));
+        }
         float sv = 0.0f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
