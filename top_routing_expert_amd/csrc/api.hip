@@ -248,10 +248,21 @@ int dwg_split(const moe_dims* d) {
   return int(s < by_t ? s : by_t);
 }
 
+// Token chunks of the shared expert's weight-gradient reduction over T: enough
+// 256x256 output tiles x chunks for one per CU, at most 16 chunks of at least
+// 256 tokens.
+int shared_split(const moe_dims* d, int64_t M, int64_t N) {
+  const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
+  int64_t s = cdiv(256, tiles);
+  s = s < 1 ? 1 : (s > 16 ? 16 : s);
+  const int64_t by_t = d->T / 256 > 0 ? d->T / 256 : 1;
+  return int(s < by_t ? s : by_t);
+}
+
 struct BwdWs {
   FfnWs ffn, ffn_s;
   size_t dO, dg, dH, dXp, dz, dwg_part, dxr;
-  size_t dyx, dHs, dxs, soff;
+  size_t dyx, dHs, dxs, soff, ssplit_off, spart;
 };
 BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   BwdWs b;
@@ -271,6 +282,10 @@ BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   b.dHs = c.take(size_t(d->T) * 2 * Fs * eb);
   b.dxs = c.take(Fs ? size_t(d->T) * d->d * 4 : 0);
   b.soff = c.take(2 * 4);
+  b.ssplit_off = c.take(Fs ? size_t(17) * 4 : 0);
+  b.spart = c.take(Fs ? size_t(std::max(shared_split(d, 2 * Fs, d->d) * 2 * Fs * d->d,
+                                         shared_split(d, d->d, Fs) * d->d * Fs)) * 4
+                      : 0);
   return b;
 }
 
@@ -539,9 +554,17 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
     MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dHs), w->Ws13, 0, soff, 1, T, D, 2 * fs,
                                   EPI_STORE_F32, dxs, nullptr, 0, 0),
                     ts_s, st));
-    MOE_TRY(gemm_on(o, gemm_wgrad(dyx, sv->a_shared, soff, 1, D, fs, grads->dWs2), ts_s, st));
-    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dHs), x, soff, 1, 2 * fs, D, grads->dWs13),
-                    ts_s, st));
+    // weight gradients: the T-reduction split into equal token chunks (one
+    // K-grouped GEMM over the chunks), then the chunk partials summed in order
+    int32_t* coff = at<int32_t>(ws, b.ssplit_off);
+    float* part = at<float>(ws, b.spart);
+    const int s2 = shared_split(d, D, fs), s13 = shared_split(d, 2 * fs, D);
+    MOE_TRY(launch_fill_seq_i32(coff, s2 + 1, int32_t(cdiv(T, s2)), int32_t(T), st));
+    MOE_TRY(gemm_on(o, gemm_wgrad(dyx, sv->a_shared, coff, s2, D, fs, part), ts_s, st));
+    MOE_TRY(launch_sum_partials(part, s2, int64_t(D) * fs, grads->dWs2, st));
+    MOE_TRY(launch_fill_seq_i32(coff, s13 + 1, int32_t(cdiv(T, s13)), int32_t(T), st));
+    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dHs), x, coff, s13, 2 * fs, D, part), ts_s, st));
+    MOE_TRY(launch_sum_partials(part, s13, int64_t(2) * fs * D, grads->dWs13, st));
   }
   // router: dz from the kept gates' gradient and the two losses; dWg = x^T dz;
   // dx_router = dz Wg^T

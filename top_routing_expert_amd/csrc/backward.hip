@@ -339,6 +339,11 @@ hipError_t launch_strided_gemm(const void* A, bool a_bf16, int64_t sam, int64_t 
   return hipGetLastError();
 }
 
+hipError_t launch_sum_partials(const float* P, int nz, int64_t n, float* out, hipStream_t st) {
+  sum_partials_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(P, nz, n, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_unpermute_sum(const float* dxp, const int32_t* ros, const float* e1,
                                 const float* e2, int T, int k, int d, float* dx, hipStream_t st) {
   unpermute_sum_kernel<<<unsigned(cdiv(T, 4)), 256, 0, st>>>(dxp, ros, e1, e2, T, k, d, dx);

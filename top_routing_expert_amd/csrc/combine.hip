@@ -59,9 +59,20 @@ __global__ void fill_i32_kernel(int32_t* out, int n, int32_t v0, int32_t v1, int
   if (i < n) out[i] = i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3;
 }
 
+// out[i] = min(i * step, cap), i = 0..n-1 (row offsets of equal chunks)
+__global__ void fill_seq_i32_kernel(int32_t* out, int n, int32_t step, int32_t cap) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = int32_t(min(int64_t(i) * step, int64_t(cap)));
+}
+
 __global__ void zero_i32_kernel(int32_t* out, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) out[i] = 0;
+}
+
+hipError_t launch_fill_seq_i32(int32_t* out, int n, int32_t step, int32_t cap, hipStream_t st) {
+  fill_seq_i32_kernel<<<dim3(unsigned(cdiv(n, 256))), dim3(256), 0, st>>>(out, n, step, cap);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_i32(int32_t* out, int n, int32_t v0, int32_t v1, int32_t v2, int32_t v3,

@@ -148,15 +148,35 @@ void gg_bf16_kernel(GemmArgs g) {
   __shared__ int32_t ts[257];
 
   int32_t total;
+  int tile;
   if constexpr (MODE == GM_KGROUP) {
+    // A tile's work grows with its group's rows, so groups are taken heaviest
+    // first (ts[r] = the group of rank r by rows, descending, ties to the
+    // lower index; G <= 256) and tiles go round-robin over the XCDs in that
+    // order: the longest tiles start first and spread over the whole chip.
+    const int tid = threadIdx.x;
+    const int32_t mine = tid < g.G ? g.offsets[tid + 1] - g.offsets[tid] : -1;
+    if (tid < 256) ts[tid] = mine;
+    __syncthreads();
+    int rank = 0;
+    if (tid < g.G)
+      for (int h = 0; h < g.G; ++h) {
+        const int32_t o = ts[h];
+        rank += (o > mine) || (o == mine && h < tid);
+      }
+    __syncthreads();
+    if (tid < g.G) ts[rank] = tid;
+    __syncthreads();
     total = g.G * (g.M_fixed / BM) * (g.N / BN);
+    tile = blockIdx.x;
+    if (tile >= total) return;
   } else {
     total = plan_tiles<BM, BN>(g, ts);
+    const int per = (total + 7) >> 3;
+    const int bid = blockIdx.x;
+    tile = (bid & 7) * per + (bid >> 3);
+    if ((bid >> 3) >= per || tile >= total) return;
   }
-  const int per = (total + 7) >> 3;
-  const int bid = blockIdx.x;
-  const int tile = (bid & 7) * per + (bid >> 3);
-  if ((bid >> 3) >= per || tile >= total) return;
   TileCoord tc;
   int K;                                     // reduction length of this tile
   const uint16_t* A;
@@ -164,8 +184,8 @@ void gg_bf16_kernel(GemmArgs g) {
   if constexpr (MODE == GM_KGROUP) {
     const int MT = g.M_fixed / BM;
     const int tpg = MT * (g.N / BN);
-    tc.grp = tile / tpg;
-    const int local = tile - tc.grp * tpg;
+    tc.grp = ts[tile / tpg];
+    const int local = tile % tpg;
     tc.m0 = (local % MT) * BM;
     tc.n0 = (local / MT) * BN;
     tc.row0 = 0;                             // output rows of group grp

@@ -88,6 +88,8 @@ hipError_t launch_combine(const float* o, const int32_t* row_of_slot, const floa
 hipError_t launch_fill_i32(int32_t* out, int n, int32_t v0, int32_t v1, int32_t v2, int32_t v3,
                            hipStream_t st);
 hipError_t launch_zero_i32(int32_t* out, int64_t n, hipStream_t st);
+// out[i] = min(i * step, cap) for i < n
+hipError_t launch_fill_seq_i32(int32_t* out, int n, int32_t step, int32_t cap, hipStream_t st);
 hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, float target,
                               float gamma, hipStream_t st);
 
@@ -102,6 +104,8 @@ hipError_t launch_router_bwd(const float* z, const int32_t* idx, const float* dg
 hipError_t launch_strided_gemm(const void* A, bool a_bf16, int64_t sam, int64_t sak, const float* B,
                                int64_t sbk, int64_t sbn, int M, int N, int K, int nsplit, float* P,
                                float* out, hipStream_t st);
+// out[i] = sum over z of P[z * n + i], z = 0..nz-1 in order
+hipError_t launch_sum_partials(const float* P, int nz, int64_t n, float* out, hipStream_t st);
 hipError_t launch_unpermute_sum(const float* dxp, const int32_t* ros, const float* e1,
                                 const float* e2, int T, int k, int d, float* dx, hipStream_t st);
 
