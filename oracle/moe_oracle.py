@@ -62,7 +62,7 @@ __all__ = [
     "capacity", "router_logits", "score", "select_topk", "near_tie_flags", "gates",
     "logsumexp_rows", "router_losses", "route", "dispatch", "permute", "silu", "gelu",
     "expert_ffn", "shared_expert", "combine", "bias_update", "layer_fwd", "layer_bwd",
-    "router_bwd", "expert_bwd",
+    "router_bwd", "expert_bwd", "uniform_assignment", "hash_assignment", "fmix32", "softplus",
     "NEAR_TIE_REL",
 ]
 
@@ -200,58 +200,122 @@ def uniform_assignment(T: int, E: int, k: int):
     return (t * k + j) % E
 
 
+def fmix32(v):
+    """The 32-bit finalizer of Appleby's MurmurHash3 (public domain): xor-shift
+    16, multiply by 0x85ebca6b, xor-shift 13, multiply by 0xc2b2ae35, xor-shift
+    16, all modulo 2^32.  A bijection of the 32-bit integers."""
+    h = np.asarray(v).astype(np.uint64) & 0xFFFFFFFF
+    h ^= h >> 16
+    h = (h * 0x85EBCA6B) & 0xFFFFFFFF
+    h ^= h >> 13
+    h = (h * 0xC2B2AE35) & 0xFFFFFFFF
+    h ^= h >> 16
+    return h
+
+
+def hash_assignment(token_ids, E: int, k: int):
+    """Token-id hash routing [Handbook news, DeepSeek-V4: the first MoE layers
+    pick experts by a fixed hash of the token id]: the token's experts are the
+    k consecutive experts (fmix32(id) + j) mod E, j = 0..k-1 (distinct for
+    k <= E; the same for every occurrence of the id)."""
+    h = fmix32(np.asarray(token_ids).astype(np.int64) & 0xFFFFFFFF).astype(np.int64)
+    return (h[:, None] + np.arange(k, dtype=np.int64)[None, :]) % E
+
+
+def softplus(v):
+    return np.logaddexp(0.0, np.asarray(v, F64))
+
+
 def route(x, Wg, k, score_kind, renorm, gate_scale, offset=None, sel_bias=None,
-          aux_coef=0.0, z_coef=0.0, routing="topk"):
+          aux_coef=0.0, z_coef=0.0, routing="topk", W_noise=None, noise=None, uniform=None,
+          token_ids=None):
     """The FP32-router step of the layer in float64 [Handbook-digest, "the three
     hard parts", 1: routing in full precision].  Returns a dict with z, s, sel,
-    idx [T,k], g [T,k], counts [E] (pre-drop), losses and near-tie flags.
-    routing="uniform" replaces the top-k choice by the forced-uniform
-    assignment; gates and losses are computed from the scores as usual."""
+    idx [T,k], g [T,k], active [T,k], counts [E] (pre-drop, active slots),
+    losses and near-tie flags.
+
+    routing:
+      "topk"      KeepTopK of the selection scores;
+      "uniform"   the forced-uniform assignment;
+      "noisy_topk" noisy top-k gating [MoE-Explained, "What is sparsity?", the
+                  H(x) equation]: the logits become H = z + noise * softplus(x W_noise)
+                  (noise: the caller's standard-normal draws [T,E]); scores,
+                  selection, gates and losses all use H (returned as z; the
+                  projection x W_noise as zn);
+      "gshard"    random routing [MoE-Explained, "MoEs and Transformers", GShard]:
+                  top-2, the first expert always kept, the second kept iff
+                  uniform[t] < 2 * g2 / (g1 + g2) (probability proportional to its
+                  weight, 1 when the two weights are equal); a skipped slot is
+                  inactive (no output, not counted) but stays in the gate
+                  normalisation;
+      "hash"      the token-id hash assignment.
+    Gates are always the scores of the chosen experts (renormalised and scaled
+    as configured)."""
     z = router_logits(x, Wg, offset)
+    zn = None
+    if routing == "noisy_topk":
+        zn = np.asarray(x, F64) @ np.asarray(W_noise, F64)
+        z = z + np.asarray(noise, F64) * softplus(zn)
     s = score(z, score_kind)
     sel = s + (np.asarray(sel_bias, F64)[None, :] if sel_bias is not None else 0.0)
-    E = z.shape[1]
+    T, E = z.shape
     if routing == "uniform":
-        idx = uniform_assignment(z.shape[0], E, k)
-    elif routing == "topk":
+        idx = uniform_assignment(T, E, k)
+    elif routing == "hash":
+        idx = hash_assignment(token_ids, E, k)
+    elif routing in ("topk", "noisy_topk", "gshard"):
+        if routing == "gshard" and k != 2:
+            raise ValueError("random routing is a top-2 scheme")
         idx = select_topk(sel, k)
     else:
         raise ValueError(f"unknown routing {routing!r}")
     g = gates(s, idx, renorm, gate_scale)
-    counts = np.bincount(idx.reshape(-1), minlength=E).astype(np.int64)
+    active = np.ones((T, k), bool)
+    if routing == "gshard":
+        s1 = np.take_along_axis(s, idx[:, :1], axis=1)[:, 0]
+        s2 = np.take_along_axis(s, idx[:, 1:], axis=1)[:, 0]
+        active[:, 1] = np.asarray(uniform, F64) < 2.0 * s2 / (s1 + s2)
+    counts = np.bincount(idx[active], minlength=E).astype(np.int64)
     aux, zl = router_losses(z, s, counts, k, aux_coef, z_coef)
     boundary, order = near_tie_flags(sel, k)
-    if routing != "topk":
+    if routing in ("uniform", "hash"):
         boundary, order = np.zeros_like(boundary), np.zeros_like(order)
-    return dict(z=z, s=s, sel=sel, idx=idx, g=g, counts=counts, aux=aux, zloss=zl,
-                near_tie=boundary, near_tie_order=order)
+    return dict(z=z, zn=zn, s=s, sel=sel, idx=idx, g=g, active=active, counts=counts, aux=aux,
+                zloss=zl, near_tie=boundary, near_tie_order=order)
 
 
 # ---------------------------------------------------------------------------
 # Dispatch: capacity, drop set, expert-contiguous permutation
 # ---------------------------------------------------------------------------
-def dispatch(idx, E: int, C):
+def dispatch(idx, E: int, C, active=None, priority: str = "token"):
     """Group routed slots by expert [MoE-Explained, "MoEs and Transformers",
     expert capacity and overflow].
 
-    counts_e = slots that chose e (pre-drop); each expert keeps its first C
-    slots in ascending token order; kept rows are laid out expert by expert:
-    row = offsets[e] + position, offsets = exclusive scan of min(counts, C).
-    Returns counts [E], offsets [E+1], row_of_slot [T,k] (-1 = dropped) and
-    token_of_row [T*k] (-1 past the last kept row).
+    counts_e = active slots that chose e (pre-drop); each expert keeps its
+    first C slots in ascending token order (priority "token"), or with every
+    token's first choices ahead of any second choice (priority "slot": order by
+    slot, then token; GShard's overflow priority in the same section); kept
+    rows are laid out expert by expert: row = offsets[e] + position, offsets =
+    exclusive scan of min(counts, C).  Inactive slots are skipped.
+    Returns counts [E], offsets [E+1], row_of_slot [T,k] (-1 = dropped or
+    inactive) and token_of_row [T*k] (-1 past the last kept row).
     """
     idx = np.asarray(idx)
     T, k = idx.shape
+    act = np.ones((T, k), bool) if active is None else np.asarray(active, bool)
     counts = np.zeros(E, np.int64)
     for e in range(E):
-        counts[e] = int(np.count_nonzero(idx == e))
+        counts[e] = int(np.count_nonzero((idx == e) & act))
     kept = counts.copy() if C is None else np.minimum(counts, C)
     offsets = np.zeros(E + 1, np.int64)
     offsets[1:] = np.cumsum(kept)
     row_of_slot = np.full((T, k), -1, np.int64)
     token_of_row = np.full(T * k, -1, np.int64)
     for e in range(E):
-        ts, js = np.nonzero(idx == e)          # row-major: ascending token index
+        if priority == "slot":
+            js, ts = np.nonzero(((idx == e) & act).T)   # slot-major, then ascending token
+        else:
+            ts, js = np.nonzero((idx == e) & act)       # row-major: ascending token index
         n = int(kept[e])
         rows = offsets[e] + np.arange(n)
         row_of_slot[ts[:n], js[:n]] = rows
@@ -352,9 +416,11 @@ def layer_fwd(p, inp, keep_hidden: bool = False):
     from the seeded generator).  Steps in order: route, capacity, dispatch,
     permute, expert FFN, shared expert, combine."""
     r = route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale,
-              inp.get("offset"), inp.get("sel_bias"), p.aux_coef, p.z_coef, p.routing)
+              inp.get("offset"), inp.get("sel_bias"), p.aux_coef, p.z_coef, p.routing,
+              inp.get("W_noise"), inp.get("noise"), inp.get("uniform"), inp.get("token_ids"))
     C = capacity(p.T, p.E, p.k, p.capacity_factor)
-    counts, offsets, row_of_slot, token_of_row = dispatch(r["idx"], p.E, C)
+    counts, offsets, row_of_slot, token_of_row = dispatch(r["idx"], p.E, C, r["active"],
+                                                          p.priority)
     R = int(offsets[-1])
     x_perm = permute(inp["x"], token_of_row, R)
     res = expert_ffn(x_perm, offsets, inp["W13"], inp["W2"], p.act, keep_hidden)
@@ -484,5 +550,11 @@ def layer_bwd(p, inp, fwd, dy):
     dz = router_bwd(p, fwd["s"], fwd["z"], fwd["idx"], fwd["counts"], dg)
     dWg = x.T @ dz
     dx += dz @ np.asarray(inp["Wg"], F64).T
-    return dict(dx=dx, dWg=dWg, dW13=dW13, dW2=dW2, dWs13=dWs13, dWs2=dWs2,
+    dW_noise = None
+    if p.routing == "noisy_topk":
+        # H = z + noise * softplus(zn): dH/dzn = noise * sigmoid(zn)
+        dzn = dz * np.asarray(inp["noise"], F64) / (1.0 + np.exp(-fwd["zn"]))
+        dW_noise = x.T @ dzn
+        dx += dzn @ np.asarray(inp["W_noise"], F64).T
+    return dict(dx=dx, dWg=dWg, dW13=dW13, dW2=dW2, dWs13=dWs13, dWs2=dWs2, dW_noise=dW_noise,
                 dO=dO, dg=dg, dz=dz, dXp=dXp)

@@ -378,7 +378,9 @@ def _objective(p, inp, dy):
 @pytest.mark.parametrize("kind,act,cf,shared,routing", [
     ("softmax", "swiglu", 0.0, 0, "topk"), ("sigmoid", "swiglu", 0.0, 6, "topk"),
     ("sqrt_softplus", "swiglu", 0.0, 6, "topk"), ("softmax", "gelu", 0.75, 0, "topk"),
-    ("sqrt_softplus", "gelu", 0.75, 6, "topk"), ("sigmoid", "swiglu", 0.0, 6, "uniform")])
+    ("sqrt_softplus", "gelu", 0.75, 6, "topk"), ("sigmoid", "swiglu", 0.0, 6, "uniform"),
+    ("softmax", "swiglu", 0.75, 6, "noisy_topk"), ("softmax", "gelu", 0.0, 0, "gshard"),
+    ("sqrt_softplus", "swiglu", 0.0, 0, "hash")])
 def test_backward_finite_differences(kind, act, cf, shared, routing):
     p = tiny(T=24, d=10, E=5, k=2, F=6, score=kind, act=act, capacity_factor=cf,
              F_shared=shared, gate_scale=math.sqrt(2.0), aux_coef=0.3, z_coef=0.2,
@@ -392,6 +394,8 @@ def test_backward_finite_differences(kind, act, cf, shared, routing):
     fk = orc.layer_fwd(p, inp, keep_hidden=True)
     grads = orc.layer_bwd(p, inp, fk, dy)
     names = [("x", "dx"), ("Wg", "dWg"), ("W13", "dW13"), ("W2", "dW2")]
+    if routing == "noisy_topk":
+        names += [("W_noise", "dW_noise")]
     if shared:
         names += [("Ws13", "dWs13"), ("Ws2", "dWs2")]
     rng = np.random.default_rng(18)
@@ -464,3 +468,149 @@ def test_uniform_routing_layer_equals_dense_bruteforce(kind, renorm):
     for e in range(p.E):
         y = y + G[:, e:e + 1] * _torch_ffn(inp["x"], inp["W13"][e], inp["W2"][e], p.act)
     np.testing.assert_allclose(f["y"], y, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# variant routers: noisy top-k, random second expert, token-id hash; overflow priority
+# ---------------------------------------------------------------------------
+def _dense_y(p, inp, G):
+    y = np.zeros((p.T, p.d))
+    for e in range(p.E):
+        y = y + G[:, e:e + 1] * _torch_ffn(inp["x"], inp["W13"][e], inp["W2"][e], p.act)
+    return y
+
+
+def test_noisy_topk_without_noise_is_topk():
+    p = tiny(routing="noisy_topk", k=2)
+    inp = synth.make_inputs(p, seed=31)
+    a = orc.route(inp["x"], inp["Wg"], 2, "softmax", True, 1.0, routing="noisy_topk",
+                  W_noise=inp["W_noise"], noise=np.zeros_like(inp["noise"]))
+    b = orc.route(inp["x"], inp["Wg"], 2, "softmax", True, 1.0)
+    assert np.array_equal(a["idx"], b["idx"]) and np.allclose(a["g"], b["g"], rtol=0, atol=0)
+
+
+def test_noisy_topk_large_draw_wins():
+    """A large positive draw on expert e makes it the first choice."""
+    p = tiny(routing="noisy_topk", k=2)
+    inp = synth.make_inputs(p, seed=32)
+    noise = inp["noise"].copy()
+    want = np.arange(p.T) % p.E
+    noise[np.arange(p.T), want] = 1e4
+    r = orc.route(inp["x"], inp["Wg"], 2, "softmax", True, 1.0, routing="noisy_topk",
+                  W_noise=inp["W_noise"], noise=noise)
+    assert np.array_equal(r["idx"][:, 0], want)
+
+
+def test_noisy_topk_layer_equals_dense_bruteforce():
+    """G = Softmax(KeepTopK(H, k)) with H = x Wg + eps * log(1 + exp(x Wn)),
+    summed densely over all experts."""
+    p = tiny(T=40, E=6, k=2, routing="noisy_topk", renorm=True, gate_scale=1.0)
+    inp = synth.make_inputs(p, seed=33)
+    f = orc.layer_fwd(p, inp)
+    x = inp["x"].astype(np.float64)
+    H = x @ inp["Wg"] + inp["noise"] * np.log1p(np.exp(x @ inp["W_noise"]))
+    keep = np.array([[np.sum(H[t] > H[t, e]) < p.k for e in range(p.E)] for t in range(p.T)])
+    Hk = np.where(keep, H, -np.inf)
+    G = np.exp(Hk - Hk.max(axis=1, keepdims=True))
+    G = G / G.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(f["y"], _dense_y(p, inp, G), rtol=1e-11, atol=1e-12)
+
+
+def _top2_by_hand(s):
+    out = []
+    for row in s:
+        order = sorted(range(len(row)), key=lambda e: (-row[e], e))
+        out.append(order[:2])
+    return np.array(out)
+
+
+def test_random_second_expert_rule():
+    """First expert always; second kept iff u < 2 g2 / (g1 + g2); u = 0 keeps all."""
+    p = tiny(T=200, E=6, k=2, routing="gshard")
+    inp = synth.make_inputs(p, seed=34)
+    r = orc.route(inp["x"], inp["Wg"], 2, "softmax", True, 1.0, routing="gshard",
+                  uniform=inp["uniform"])
+    s = sps.softmax(inp["x"].astype(np.float64) @ inp["Wg"], axis=1)
+    top = _top2_by_hand(s)
+    assert np.array_equal(r["idx"], top)
+    s1, s2 = s[np.arange(p.T), top[:, 0]], s[np.arange(p.T), top[:, 1]]
+    assert r["active"][:, 0].all()
+    np.testing.assert_array_equal(r["active"][:, 1], inp["uniform"] < 2 * s2 / (s1 + s2))
+    assert 0 < r["active"][:, 1].sum() < p.T
+    np.testing.assert_array_equal(r["counts"], np.bincount(r["idx"][r["active"]], minlength=p.E))
+    r0 = orc.route(inp["x"], inp["Wg"], 2, "softmax", True, 1.0, routing="gshard",
+                   uniform=np.zeros(p.T, np.float32))
+    assert r0["active"].all()
+
+
+def test_random_second_expert_layer_dense():
+    """y = g1 E1 + [second kept] g2 E2, gates normalised over both experts."""
+    p = tiny(T=50, E=5, k=2, routing="gshard", renorm=True)
+    inp = synth.make_inputs(p, seed=35)
+    f = orc.layer_fwd(p, inp)
+    s = sps.softmax(inp["x"].astype(np.float64) @ inp["Wg"], axis=1)
+    top = _top2_by_hand(s)
+    s1, s2 = s[np.arange(p.T), top[:, 0]], s[np.arange(p.T), top[:, 1]]
+    keep2 = inp["uniform"] < 2 * s2 / (s1 + s2)
+    G = np.zeros((p.T, p.E))
+    G[np.arange(p.T), top[:, 0]] = s1 / (s1 + s2)
+    G[np.arange(p.T), top[:, 1]] = np.where(keep2, s2 / (s1 + s2), 0.0)
+    np.testing.assert_allclose(f["y"], _dense_y(p, inp, G), rtol=1e-11, atol=1e-12)
+
+
+def test_slot_priority_dispatch_bruteforce():
+    """Top-1-first overflow: walk the slots in (slot, token) order, each expert
+    filling its C places in that order."""
+    rng = np.random.default_rng(36)
+    T, k, E, C = 40, 3, 5, 9
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    active = rng.random((T, k)) < 0.85
+    counts, offsets, ros, tor = orc.dispatch(idx, E, C, active, "slot")
+    fill = np.zeros(E, np.int64)
+    want = np.full((T, k), -1)
+    kept = np.minimum(np.bincount(idx[active], minlength=E), C)
+    base = np.concatenate([[0], np.cumsum(kept)])
+    for j in range(k):
+        for t in range(T):
+            e = idx[t, j]
+            if active[t, j] and fill[e] < C:
+                want[t, j] = base[e] + fill[e]
+                fill[e] += 1
+    np.testing.assert_array_equal(ros, want)
+    np.testing.assert_array_equal(offsets, base)
+    np.testing.assert_array_equal(counts, np.bincount(idx[active], minlength=E))
+    R = int(offsets[-1])
+    assert sorted(ros[ros >= 0].tolist()) == list(range(R))
+    assert all(tor[ros[t, j]] == t for t in range(T) for j in range(k) if ros[t, j] >= 0)
+
+
+def test_fmix32_is_a_bijection():
+    v = np.arange(1 << 18, dtype=np.int64)
+    h = orc.fmix32(v)
+    assert len(np.unique(h)) == v.size and int(orc.fmix32(np.array([0]))[0]) == 0
+    # invert it: undo each xor-shift and multiply by the inverse constants mod 2^32
+    def unshift(x, s):
+        y = x.copy()
+        for _ in range(32 // s + 1):
+            y = x ^ (y >> s)
+        return y
+    y = unshift(h, 16)
+    y = (y * pow(0xC2B2AE35, -1, 1 << 32)) & 0xFFFFFFFF
+    y = unshift(y, 13)
+    y = (y * pow(0x85EBCA6B, -1, 1 << 32)) & 0xFFFFFFFF
+    y = unshift(y, 16)
+    assert np.array_equal(y.astype(np.int64), v)
+
+
+def test_hash_routing_fixed_per_id_distinct_balanced():
+    p = tiny(T=4000, E=8, k=3, routing="hash")
+    inp = synth.make_inputs(p, seed=37)
+    ids = inp["token_ids"].copy()
+    ids[100:200] = ids[0]                     # repeated ids route identically
+    r = orc.route(inp["x"], inp["Wg"], p.k, "softmax", True, 1.0, routing="hash", token_ids=ids)
+    assert (r["idx"][100:200] == r["idx"][0]).all()
+    assert all(len(set(row)) == p.k for row in r["idx"].tolist())
+    # experts are k consecutive ones (mod E) from a start that depends only on the id
+    assert ((r["idx"][:, 1:] - r["idx"][:, :-1]) % p.E == 1).all()
+    c = r["counts"] / r["counts"].sum()
+    assert np.max(np.abs(c - 1 / p.E)) < 0.02

@@ -43,7 +43,8 @@ class Preset:
     aux_coef: float = 0.0       # load-balance loss coefficient (0 = off)
     z_coef: float = 0.0         # router z-loss coefficient (0 = off)
     bias_gamma: float = 0.0     # fixed step of the loss-free bias update (0 = off)
-    routing: str = "topk"       # "topk" | "uniform" (forced-uniform assignment)
+    routing: str = "topk"       # "topk" | "uniform" | "noisy_topk" | "gshard" | "hash"
+    priority: str = "token"     # capacity overflow order: "token" (index) | "slot" (top-1 first)
     # ---- synthetic input recipe (all standard deviations) ----
     x_std: float = 1.0
     wg_std: float = 0.02        # router weight W_g [d, E], fp32

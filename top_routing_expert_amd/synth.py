@@ -28,7 +28,9 @@ import numpy as np
 
 from .presets import Preset
 
-_STREAMS = ("x", "Wg", "zipf_perm", "sel_bias", "W13", "W2", "shared", "dy")
+_STREAMS = ("x", "Wg", "zipf_perm", "sel_bias", "W13", "W2", "shared", "dy",
+            "W_noise", "noise", "uniform", "token_ids")
+VOCAB = 65536   # token-id range of the hash-routing inputs
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
@@ -90,6 +92,17 @@ def make_inputs(p: Preset, seed: int = 0, with_dy: bool | None = None,
             out["Ws2"] = _normal(sh[1], (p.d, p.F_shared), p.w_std, bf16)
         else:
             out["Ws13"] = out["Ws2"] = None
+    # inputs of the variant routers: the noise projection and its standard-normal
+    # draws (noisy top-k), one uniform draw per token (random second expert),
+    # token ids (hash routing)
+    out["W_noise"] = out["noise"] = out["uniform"] = out["token_ids"] = None
+    if p.routing == "noisy_topk":
+        out["W_noise"] = _normal(rng["W_noise"], (p.d, p.E), p.wg_std, False)
+        out["noise"] = rng["noise"].standard_normal((p.T, p.E), dtype=np.float32)
+    elif p.routing == "gshard":
+        out["uniform"] = rng["uniform"].random(p.T, dtype=np.float32)
+    elif p.routing == "hash":
+        out["token_ids"] = rng["token_ids"].integers(0, VOCAB, p.T, dtype=np.int32)
     if with_dy is None:
         with_dy = p.train
     out["dy"] = _normal(rng["dy"], (p.T, p.d), 1.0, False) if with_dy else None
