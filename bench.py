@@ -31,8 +31,12 @@ def parse():
     ap.add_argument("--config", default="c2", help="preset name (c1..c5)")
     ap.add_argument("--fwd-only", action="store_true")
     ap.add_argument("--stage-iters", type=int, default=20)
-    ap.add_argument("--routing", default="topk", choices=["topk", "uniform"],
-                    help="expert choice: learned top-k, or the forced-uniform assignment")
+    ap.add_argument("--routing", default="topk",
+                    choices=["topk", "uniform", "noisy_topk", "gshard", "hash"],
+                    help="expert choice: learned top-k, forced-uniform, noisy top-k, random "
+                         "second expert (top-2), or token-id hash")
+    ap.add_argument("--priority", default="token", choices=["token", "slot"],
+                    help="capacity overflow order: token index, or first choices first")
     ap.add_argument("--k", type=int, default=None,
                     help="experts per token (serve the layer with fewer experts than its preset)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,7 +78,7 @@ def main():
     import torch
     from top_routing_expert_amd import binding as B, perf, presets, synth
 
-    over = dict(routing=args.routing)
+    over = dict(routing=args.routing, priority=args.priority)
     if args.k is not None:
         over["k"] = args.k
     p = presets.get(args.config, **over)
@@ -85,7 +89,8 @@ def main():
     x = torch.from_numpy(inp["x"]).to(dev).to(B.TORCH_DTYPE[p.dtype]).contiguous()
     w = B.weights_to_device(p, inp, dev)
     dy = torch.from_numpy(inp["dy"]).to(dev) if train else None
-    layer = B.Layer(p, w, dev, train=train)
+    ri = B.router_inputs_to_device(inp, dev)
+    layer = B.Layer(p, w, dev, train=train, ri=ri)
 
     def step():
         layer.fwd(x)
@@ -99,7 +104,7 @@ def main():
         if train and e.status == B.MOE_ERR_UNSUPPORTED:
             log("[bench] backward not available; timing the forward only")
             train = False
-            layer = B.Layer(p, w, dev, train=False)
+            layer = B.Layer(p, w, dev, train=False, ri=ri)
         else:
             raise
     for _ in range(args.warmup):
@@ -116,8 +121,8 @@ def main():
 
     # ---- per-step rates, HIP events on the current stream (the library's stream)
     ws = B.Workspace(dev)
-    y, st = B.layer_fwd(p, w, x, stats=True, ws=ws)
-    r = B.route(p, x, w.Wg, w.offset, w.sel_bias, ws=ws)
+    y, st = B.layer_fwd(p, w, x, stats=True, ri=ri, ws=ws)
+    r = B.route(p, x, w.Wg, w.offset, w.sel_bias, ri=ri, ws=ws)
     pm = B.permute(p, x, r["idx"], ws=ws)
     torch.cuda.synchronize()
     offsets = pm["offsets"].cpu().numpy()
@@ -139,7 +144,7 @@ def main():
 
     it = args.stage_iters
     ffn_out = torch.empty(p.T * p.k, p.d, dtype=torch.float32, device=dev)
-    t_route = timed(lambda: B.route(p, x, w.Wg, w.offset, w.sel_bias, ws=ws), it)
+    t_route = timed(lambda: B.route(p, x, w.Wg, w.offset, w.sel_bias, ri=ri, ws=ws), it)
     t_perm = timed(lambda: B.permute(p, x, r["idx"], ws=ws), it)
     t_ffn = timed(lambda: B.expert_ffn(p, pm["x_perm"], pm["offsets"], w.W13, w.W2,
                                        max_rows=p.T * p.k, ws=ws), it)
@@ -190,7 +195,8 @@ def main():
         ps, sub = p, inp
         if Ts < p.T:
             ps = p.with_(T=Ts)
-            sub = dict(inp, x=inp["x"][:Ts], dy=None if inp.get("dy") is None else inp["dy"][:Ts])
+            sub = dict(inp, **{n: inp[n][:Ts] for n in ("x", "dy", "noise", "uniform", "token_ids")
+                               if inp.get(n) is not None})
         t0 = time.perf_counter()
         passes = 0
         while True:
@@ -224,7 +230,8 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and weights)",
         "config": {"workload": f"{p.name}: T={p.T} d={p.d} E={p.E} top-{p.k} F={p.F} {p.act} "
                                f"{p.score} CF={p.capacity_factor} shared={p.F_shared}"
-                               + ("" if p.routing == "topk" else f" routing={p.routing}"),
+                               + ("" if p.routing == "topk" else f" routing={p.routing}")
+                               + ("" if p.priority == "token" else f" priority={p.priority}"),
                    "step": "forward+backward" if train else "forward",
                    "global_batch": p.T, "parallelism": "single GPU"},
         "roofline": roof,

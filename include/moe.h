@@ -73,24 +73,58 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
  * bf16: d, F and F_shared multiples of 128; fp32: d, F, F_shared multiples of 4. */
 typedef struct { int64_t T, d, E, k, F, F_shared; } moe_dims;
 
-/* How the k experts of a token are chosen.
+/* How the k experts of a token are chosen.  Gates are always the router scores of
+ * the chosen experts (renormalised and scaled as configured).
  * MOE_ROUTING_TOPK: the k largest selection scores (score + selection bias), ties to
  *   the lower expert index ("Mixture of Experts Explained", "What is sparsity?", KeepTopK).
  * MOE_ROUTING_UNIFORM: forced-uniform assignment, slot j of token t to expert
  *   (t*k + j) mod E, the balanced baseline of the Ultimate MoE Training Handbook digest
- *   ("the three hard parts", 2); gates and losses still come from the router's scores. */
-typedef enum { MOE_ROUTING_TOPK = 0, MOE_ROUTING_UNIFORM = 1 } moe_routing;
+ *   ("the three hard parts", 2).
+ * MOE_ROUTING_NOISY_TOPK: noisy top-k gating ("What is sparsity?", the H(x) equation):
+ *   the logits become H = z + noise * softplus(x . W_noise) (moe_router_inputs.W_noise,
+ *   .noise) and everything downstream (scores, selection, gates, losses) uses H.
+ * MOE_ROUTING_RANDOM_SECOND: GShard's random routing ("MoEs and Transformers"): top-2
+ *   (k = 2), the first expert always kept, the second kept iff uniform[t] <
+ *   2 * s2 / (s1 + s2) of the two chosen scores; a skipped second slot is reported in
+ *   topk_idx as E + expert (permute treats it as not routed; its gate stays in the
+ *   normalisation).
+ * MOE_ROUTING_HASH: experts fixed by the token id (Handbook news, DeepSeek-V4):
+ *   slot j of token t to (fmix32(token_ids[t]) + j) mod E, fmix32 the 32-bit
+ *   finalizer of MurmurHash3. */
+typedef enum {
+  MOE_ROUTING_TOPK = 0,
+  MOE_ROUTING_UNIFORM = 1,
+  MOE_ROUTING_NOISY_TOPK = 2,
+  MOE_ROUTING_RANDOM_SECOND = 3,
+  MOE_ROUTING_HASH = 4
+} moe_routing;
+
+/* Which slots an expert keeps when more than its capacity choose it.
+ * MOE_PRIORITY_TOKEN: ascending token index.  MOE_PRIORITY_SLOT: every token's
+ * first choice before any second choice, then by token (GShard's overflow
+ * priority, "MoEs and Transformers"). */
+typedef enum { MOE_PRIORITY_TOKEN = 0, MOE_PRIORITY_SLOT = 1 } moe_priority;
 
 /* score: moe_score; act: moe_act; dtype: moe_dtype;
  * renorm != 0: kept gates are divided by their sum, then multiplied by gate_scale;
  * capacity_factor <= 0: no capacity limit, else C = ceil(cf * T * k / E) slots per expert;
  * aux_coef, z_coef: load-balance and z-loss coefficients (0 = not computed);
- * routing: moe_routing (0 = top-k). */
+ * routing: moe_routing (0 = top-k); priority: moe_priority (0 = token order). */
 typedef struct {
   int32_t score, act, dtype, renorm;
   float gate_scale, capacity_factor, aux_coef, z_coef;
-  int32_t routing;
+  int32_t routing, priority;
 } moe_opts;
+
+/* Per-call inputs of the variant routers (device pointers, fp32 unless noted).
+ * Only the ones opts.routing uses are read; the rest may be NULL.  Random draws
+ * are inputs so that a call is reproducible. */
+typedef struct {
+  const float* W_noise;      /* [d, E] noise projection (noisy top-k) */
+  const float* noise;        /* [T, E] standard-normal draws (noisy top-k) */
+  const float* uniform;      /* [T] draws in [0, 1) (random second expert) */
+  const int32_t* token_ids;  /* [T] int32 token ids (hash routing) */
+} moe_router_inputs;
 
 typedef struct {
   const float* Wg;            /* [d, E] */
@@ -119,6 +153,7 @@ typedef struct {
   void* h_shared;        /* [T, 2*F_shared] (when F_shared > 0) */
   void* a_shared;        /* [T, F_shared]   (when F_shared > 0) */
   float* losses;         /* [2] aux loss, z-loss */
+  float* noise_logits;   /* [T, E] x . W_noise (noisy top-k training only) */
 } moe_saved;
 
 typedef struct {
@@ -127,6 +162,7 @@ typedef struct {
   float* dW2;    /* [E, d, F] */
   float* dWs13;  /* [2*F_shared, d] (when F_shared > 0) */
   float* dWs2;   /* [d, F_shared]   (when F_shared > 0) */
+  float* dW_noise; /* [d, E] (noisy top-k) */
 } moe_grads;
 
 /* Router monitoring outputs, every field nullable. */
@@ -153,16 +189,17 @@ int moe_workspace_size(const moe_dims* dims, const moe_opts* opts, int with_bwd,
  * s = score(z); top-k of s + sel_bias by (value desc, index asc), NaN lowest;
  * gate_j = s[idx_j], renormalised over the kept experts if opts.renorm, times
  * gate_scale.  Outputs: topk_idx [T,k], topk_gate [T,k]; nullable: scores
- * [T,E] (s), logits [T,E] (z), counts [E] (pre-capacity histogram), losses [2]
- * (aux, z-loss; zero when the coefficient is 0). */
+ * [T,E] (s), logits [T,E] (z), counts [E] (pre-capacity histogram of the routed
+ * slots), losses [2] (aux, z-loss; zero when the coefficient is 0).  ri: the
+ * variant routers' inputs (nullable for top-k and uniform routing). */
 int moe_route(const moe_dims* dims, const moe_opts* opts, const void* x, const float* Wg,
               const float* logit_offset, const float* sel_bias, int32_t* topk_idx,
               float* topk_gate, float* scores, float* logits, int32_t* counts, float* losses,
-              void* ws, size_t ws_bytes, void* stream);
+              const moe_router_inputs* ri, void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch ("MoEs and Transformers": expert capacity, overflow to the residual).
  * counts[e] = slots choosing e; expert e keeps its first C slots in ascending
- * token order; rows are expert-contiguous from offsets (exclusive scan of
+ * token order (opts.priority = MOE_PRIORITY_SLOT: first choices first); rows are expert-contiguous from offsets (exclusive scan of
  * min(counts, C)); row_of_slot[t,j] = row or -1; token_of_row[row] = t;
  * x_perm[row] = x[t].  topk_idx entries outside [0,E) are ignored (dropped)
  * and never index memory. */
@@ -190,18 +227,22 @@ int moe_combine(const moe_dims* dims, const float* out_perm, const int32_t* row_
                 const float* topk_gate, const float* shared_out, float* y, void* stream);
 
 /* Whole forward: route, dispatch, routed expert FFNs, shared expert, combine.
- * y [T,d] fp32 (the caller adds the residual x).  saved and stats nullable. */
+ * y [T,d] fp32 (the caller adds the residual x).  ri, saved and stats nullable
+ * (ri as for moe_route). */
 int moe_layer_fwd(const moe_dims* dims, const moe_opts* opts, const moe_weights* w,
-                  const void* x, float* y, moe_saved* saved, moe_stats* stats,
-                  void* ws, size_t ws_bytes, void* stream);
+                  const moe_router_inputs* ri, const void* x, float* y, moe_saved* saved,
+                  moe_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
 /* Whole backward of J = <dy, y> + L_aux + L_z from the state saved by
  * moe_layer_fwd.  Routing decisions and load fractions are constants; the
  * selection bias and logit offset get no gradient.  dx [T,d] fp32; grads
- * overwritten (not accumulated), fp32. */
+ * overwritten (not accumulated), fp32.  Noisy top-k also yields
+ * dW_noise = x^T (dH * noise * sigmoid(x . W_noise)) and the matching dx term,
+ * from saved.noise_logits and ri (W_noise, noise). */
 int moe_layer_bwd(const moe_dims* dims, const moe_opts* opts, const moe_weights* w,
-                  const void* x, const moe_saved* saved, const float* dy, float* dx,
-                  moe_grads* grads, void* ws, size_t ws_bytes, void* stream);
+                  const moe_router_inputs* ri, const void* x, const moe_saved* saved,
+                  const float* dy, float* dx, moe_grads* grads, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /* Fixed-step loss-free bias update (news digest: the fixed-step baseline;
  * handbook digest: loss-free bias): bias[e] += gamma * sign(target - counts[e]),

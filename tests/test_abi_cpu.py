@@ -72,7 +72,7 @@ def _route_status(p, **kw):
             setattr(o, k, v)
     dummy = C.c_void_p(256)
     return B.lib().moe_route(C.byref(d), C.byref(o), dummy, dummy, None, None, dummy, dummy, None,
-                             None, None, None, dummy, 1 << 40, None)
+                             None, None, None, None, dummy, 1 << 40, None)
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -80,7 +80,11 @@ def _route_status(p, **kw):
     ("E", 300, B.MOE_ERR_UNSUPPORTED), ("T", -1, B.MOE_ERR_INVALID_ARG),
     ("d", 100, B.MOE_ERR_UNSUPPORTED), ("score", 7, B.MOE_ERR_INVALID_ARG),
     ("dtype", 5, B.MOE_ERR_INVALID_ARG), ("capacity_factor", float("nan"), B.MOE_ERR_INVALID_ARG),
-    ("routing", 2, B.MOE_ERR_INVALID_ARG), ("routing", -1, B.MOE_ERR_INVALID_ARG)])
+    ("routing", 5, B.MOE_ERR_INVALID_ARG), ("routing", -1, B.MOE_ERR_INVALID_ARG),
+    ("routing", 2, B.MOE_ERR_INVALID_ARG),      # noisy top-k without its inputs
+    ("routing", 3, B.MOE_ERR_INVALID_ARG),      # random second expert needs k = 2
+    ("routing", 4, B.MOE_ERR_INVALID_ARG),      # hash routing without token ids
+    ("priority", 2, B.MOE_ERR_INVALID_ARG)])
 def test_argument_errors_are_synchronous(L, field, value, status):
     p = presets.get("c4")
     assert _route_status(p, **{field: value}) == status
@@ -92,12 +96,12 @@ def test_null_and_misaligned_pointers(L):
     ok = C.c_void_p(256)
     bad = C.c_void_p(258)
     r = B.lib().moe_route
-    assert r(C.byref(d), C.byref(o), None, ok, None, None, ok, ok, None, None, None, None, ok, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
-    assert r(C.byref(d), C.byref(o), bad, ok, None, None, ok, ok, None, None, None, None, ok, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert r(C.byref(d), C.byref(o), None, ok, None, None, ok, ok, None, None, None, None, None, ok, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert r(C.byref(d), C.byref(o), bad, ok, None, None, ok, ok, None, None, None, None, None, ok, 1 << 40, None) == B.MOE_ERR_INVALID_ARG
     # workspace too small
-    assert r(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None, None, ok, 16, None) == B.MOE_ERR_WORKSPACE
+    assert r(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None, None, None, ok, 16, None) == B.MOE_ERR_WORKSPACE
     # workspace misaligned
-    assert r(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None, None, C.c_void_p(272), 1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    assert r(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None, None, None, C.c_void_p(272), 1 << 40, None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_zero_tokens_is_a_noop(L):
@@ -105,5 +109,5 @@ def test_zero_tokens_is_a_noop(L):
     d, o = B.dims_of(p, T=0), B.opts_of(p)
     ok = C.c_void_p(256)
     assert B.lib().moe_route(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None,
-                             None, ok, 1 << 40, None) == B.MOE_OK
+                             None, None, ok, 1 << 40, None) == B.MOE_OK
     assert B.lib().moe_combine(C.byref(d), ok, ok, ok, None, ok, None) == B.MOE_OK

@@ -35,11 +35,12 @@ BF16_BOUND = 2.0 ** -6
 def _train(p, inp):
     x = torch.from_numpy(inp["x"]).to(DEV).to(B.TORCH_DTYPE[p.dtype]).contiguous()
     w = B.weights_to_device(p, inp, DEV)
+    ri = B.router_inputs_to_device(inp, DEV)
     saved = B.alloc_saved(p, DEV)
     ws = B.Workspace(DEV)
-    y = B.layer_fwd(p, w, x, saved=saved, ws=ws)
+    y = B.layer_fwd(p, w, x, saved=saved, ri=ri, ws=ws)
     dy = torch.from_numpy(inp["dy"]).to(DEV)
-    g = B.layer_bwd(p, w, x, saved, dy, ws=ws)
+    g = B.layer_bwd(p, w, x, saved, dy, ri=ri, ws=ws)
     torch.cuda.synchronize()
     return x, w, saved, y, g
 
@@ -73,6 +74,9 @@ def _bounded(got, ref, cond, what):
          gate_scale=math.sqrt(2.0)),
     dict(T=333, k=3, aux_coef=0.05),
     dict(renorm=False, k=1, z_coef=0.2),
+    dict(routing="noisy_topk", aux_coef=0.1, z_coef=0.05, F_shared=64),
+    dict(routing="gshard", priority="slot", capacity_factor=0.9, aux_coef=0.1),
+    dict(routing="hash", score="sigmoid", aux_coef=0.1),
 ])
 def test_layer_bwd_fp32(over):
     p = presets.get("c1", train=True, **over)
@@ -81,8 +85,12 @@ def test_layer_bwd_fp32(over):
     assert not (fk["near_tie"].any() or fk["near_tie_order"].any())
     ref = orc.layer_bwd(p, inp, fk, inp["dy"])
     _, _, saved, y, g = _train(p, inp)
-    np.testing.assert_array_equal(saved["topk_idx"].cpu().numpy(), fk["idx"])
-    for name in ("dx", "dWg", "dW13", "dW2") + (("dWs13", "dWs2") if p.F_shared else ()):
+    np.testing.assert_array_equal(saved["topk_idx"].cpu().numpy(),
+                                  np.where(fk["active"], fk["idx"], fk["idx"] + p.E))
+    names = ("dx", "dWg", "dW13", "dW2") + (("dWs13", "dWs2") if p.F_shared else ())
+    if p.routing == "noisy_topk":
+        names += ("dW_noise",)
+    for name in names:
         _close(g[name].cpu().numpy(), ref[name], 1e-4, name)
 
 

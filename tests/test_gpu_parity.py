@@ -317,6 +317,117 @@ def test_reduced_k_serving(k):
     print(f"c4 served at k={k}: layer y max-abs/rms {r:.2e}")
 
 
+VARIANTS = [("c4", dict(routing="noisy_topk")), ("c3", dict(routing="gshard")),
+            ("c3", dict(routing="gshard", priority="slot", capacity_factor=0.8)),
+            ("c4", dict(routing="hash")), ("c1", dict(routing="noisy_topk")),
+            ("c1", dict(routing="gshard", priority="slot"))]
+
+
+def _variant_case(name, over):
+    p, inp, x, w = case(name, **over)
+    key = ("ri", name, tuple(sorted(over.items())))
+    if key not in _cache:
+        _cache[key] = B.router_inputs_to_device(inp, DEV)
+    return p, inp, x, w, _cache[key]
+
+
+def _oracle_route(p, inp, x_rows=None):
+    sl = slice(None) if x_rows is None else x_rows
+    g = lambda n: None if inp.get(n) is None else inp[n][sl]
+    return orc.route(inp["x"][sl], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                     inp["sel_bias"], p.aux_coef, p.z_coef, p.routing, inp.get("W_noise"),
+                     g("noise"), g("uniform"), g("token_ids"))
+
+
+def _keep_flags(p, inp, ref):
+    """Tokens whose random keep decision sits within fp32 rounding of its
+    threshold (the GPU decides in fp32, the oracle in fp64): either is valid."""
+    if p.routing != "gshard":
+        return np.zeros(p.T, bool)
+    s1 = np.take_along_axis(ref["s"], ref["idx"][:, :1], 1)[:, 0]
+    s2 = np.take_along_axis(ref["s"], ref["idx"][:, 1:], 1)[:, 0]
+    thr = 2 * s2 / (s1 + s2)
+    return np.abs(inp["uniform"] - thr) <= 1e-5 * np.maximum(thr, 1e-30)
+
+
+@pytest.mark.parametrize("name,over", VARIANTS)
+def test_variant_router_parity(name, over):
+    """Noisy top-k, random second expert, token-id hash: indices exact (skipped
+    second slots reported as E + expert) away from near-ties, gates to 1e-5,
+    counts of the routed slots exact, dispatch (token or slot priority) exact
+    on the GPU's own indices."""
+    p, inp, x, w, ri = _variant_case(name, over)
+    out = B.route(p, x, w.Wg, w.offset, w.sel_bias, want_logits=True, ri=ri)
+    torch.cuda.synchronize()
+    ref = _oracle_route(p, inp)
+    idx_g = out["idx"].cpu().numpy().astype(np.int64)
+    active_g = idx_g < p.E
+    experts_g = np.where(active_g, idx_g, idx_g - p.E)
+    want = np.where(ref["active"], ref["idx"], ref["idx"] + p.E)
+    flag = ref["near_tie"] | ref["near_tie_order"]
+    kflag = _keep_flags(p, inp, ref)
+    bad = np.any(idx_g != want, axis=1) & ~flag & ~kflag
+    assert not bad.any(), f"{int(bad.sum())} index mismatches away from near-ties"
+    ok = ~(flag | kflag)
+    np.testing.assert_allclose(out["gate"].cpu().numpy()[ok], ref["g"][ok], rtol=1e-5, atol=1e-12)
+    if p.routing == "noisy_topk":
+        cond = np.abs(inp["x"]).astype(np.float64) @ np.abs(inp["Wg"]).astype(np.float64)
+        cond += np.abs(inp["noise"]) * (np.abs(inp["x"]).astype(np.float64) @
+                                        np.abs(inp["W_noise"]).astype(np.float64))
+        dz = np.abs(out["logits"].cpu().numpy() - ref["z"])
+        assert np.all(dz <= 2e-6 * cond + 1e-6), float(np.max(dz / (cond + 1e-30)))
+    np.testing.assert_array_equal(out["counts"].cpu().numpy(),
+                                  np.bincount(experts_g[active_g], minlength=p.E))
+    # dispatch of the GPU's routing
+    C = orc.capacity(p.T, p.E, p.k, p.capacity_factor)
+    pm = B.permute(p, x, out["idx"])
+    torch.cuda.synchronize()
+    counts, offsets, ros, tor = orc.dispatch(experts_g, p.E, C, active_g, p.priority)
+    np.testing.assert_array_equal(pm["counts"].cpu().numpy(), counts)
+    np.testing.assert_array_equal(pm["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(pm["row_of_slot"].cpu().numpy(), ros)
+    R = int(offsets[-1])
+    np.testing.assert_array_equal(pm["token_of_row"].cpu().numpy()[:R], tor[:R])
+    print(f"{name} {over}: near-ties {int(flag.sum())}, keep-threshold ties {int(kflag.sum())}, "
+          f"skipped {int((~active_g).sum())}, kept rows {R}")
+
+
+@pytest.mark.parametrize("name,over", VARIANTS)
+def test_variant_router_layer(name, over):
+    p, inp, x, w, ri = _variant_case(name, over)
+    saved = B.alloc_saved(p, DEV)
+    y = B.layer_fwd(p, w, x, saved=saved, ri=ri)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    if p.dtype == "f32":
+        ref = orc.layer_fwd(p, inp)
+        idx_g = saved["topk_idx"].cpu().numpy()
+        assert np.array_equal(idx_g, np.where(ref["active"], ref["idx"], ref["idx"] + p.E))
+        err = np.max(np.abs(y - ref["y"]))
+        rms = np.sqrt(np.mean(ref["y"] ** 2))
+        assert err <= 1e-4 and err <= 1e-4 * rms, (err, rms)
+        return
+    rng = np.random.default_rng(6)
+    tokens = np.unique(np.concatenate([[0, p.T - 1], rng.integers(0, p.T, size=32)]))
+    ref = _oracle_route(p, inp, tokens)
+    idx = saved["topk_idx"].cpu().numpy()[tokens].astype(np.int64)
+    ros = saved["row_of_slot"].cpu().numpy()[tokens]
+    experts = np.where(idx < p.E, idx, idx - p.E)
+    g = orc.gates(ref["s"], experts, p.renorm, p.gate_scale)
+    X = inp["x"][tokens].astype(np.float64)
+    y_ref = np.zeros((len(tokens), p.d))
+    for i in range(len(tokens)):
+        for j in range(p.k):
+            if ros[i, j] >= 0:
+                e = experts[i, j]
+                y_ref[i] += g[i, j] * orc.expert_ffn(X[i:i + 1], np.array([0, 1]),
+                                                     inp["W13"][e:e + 1], inp["W2"][e:e + 1], p.act)[0]
+    if p.F_shared:
+        y_ref += orc.shared_expert(X, inp["Ws13"], inp["Ws2"])
+    r = _assert_bf16_close(y[tokens], y_ref, f"{name} {over} y")
+    print(f"{name} {over}: layer y max-abs/rms {r:.2e}")
+
+
 @pytest.mark.parametrize("over", [dict(T=200), dict(T=1), dict(k=8, renorm=False),
                                   dict(E=1, k=1, renorm=False), dict(score="sigmoid", F_shared=64),
                                   dict(score="sqrt_softplus", act="gelu", T=333, capacity_factor=0.7)])

@@ -12,6 +12,7 @@ import os
 from dataclasses import dataclass
 from typing import Optional
 
+import numpy as np
 import torch
 
 from .presets import Preset
@@ -23,7 +24,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
 ACT = {"swiglu": 0, "gelu": 1}
 DTYPE = {"f32": 0, "bf16": 1}
-ROUTING = {"topk": 0, "uniform": 1}
+ROUTING = {"topk": 0, "uniform": 1, "noisy_topk": 2, "gshard": 3, "hash": 4}
+PRIORITY = {"token": 0, "slot": 1}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -41,7 +43,11 @@ class Opts(C.Structure):
     _fields_ = [("score", C.c_int32), ("act", C.c_int32), ("dtype", C.c_int32),
                 ("renorm", C.c_int32), ("gate_scale", C.c_float),
                 ("capacity_factor", C.c_float), ("aux_coef", C.c_float), ("z_coef", C.c_float),
-                ("routing", C.c_int32)]
+                ("routing", C.c_int32), ("priority", C.c_int32)]
+
+
+class RouterInputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("W_noise", "noise", "uniform", "token_ids")]
 
 
 class Weights(C.Structure):
@@ -52,11 +58,11 @@ class Weights(C.Structure):
 class Saved(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("topk_idx", "topk_gate", "logits", "counts", "offsets",
                                           "row_of_slot", "token_of_row", "x_perm", "h", "a", "o",
-                                          "h_shared", "a_shared", "losses")]
+                                          "h_shared", "a_shared", "losses", "noise_logits")]
 
 
 class Grads(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("dWg", "dW13", "dW2", "dWs13", "dWs2")]
+    _fields_ = [(n, C.c_void_p) for n in ("dWg", "dW13", "dW2", "dWs13", "dWs2", "dW_noise")]
 
 
 class Stats(C.Structure):
@@ -82,12 +88,15 @@ def lib() -> C.CDLL:
     D, O = P(Dims), P(Opts)
     L.moe_capacity.argtypes = [D, O, P(I64)]
     L.moe_workspace_size.argtypes = [D, O, C.c_int, P(C.c_size_t)]
-    L.moe_route.argtypes = [D, O, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, C.c_size_t, VP]
+    L.moe_route.argtypes = [D, O, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, P(RouterInputs), VP,
+                            C.c_size_t, VP]
     L.moe_permute.argtypes = [D, O, VP, VP, VP, VP, VP, VP, VP, VP, C.c_size_t, VP]
     L.moe_expert_ffn.argtypes = [D, O, I64, I64, I64, VP, VP, VP, VP, VP, VP, VP, VP, C.c_size_t, VP]
     L.moe_combine.argtypes = [D, VP, VP, VP, VP, VP, VP]
-    L.moe_layer_fwd.argtypes = [D, O, P(Weights), VP, VP, P(Saved), P(Stats), VP, C.c_size_t, VP]
-    L.moe_layer_bwd.argtypes = [D, O, P(Weights), VP, P(Saved), VP, VP, P(Grads), VP, C.c_size_t, VP]
+    L.moe_layer_fwd.argtypes = [D, O, P(Weights), P(RouterInputs), VP, VP, P(Saved), P(Stats), VP,
+                                C.c_size_t, VP]
+    L.moe_layer_bwd.argtypes = [D, O, P(Weights), P(RouterInputs), VP, P(Saved), VP, VP, P(Grads),
+                                VP, C.c_size_t, VP]
     L.moe_bias_update.argtypes = [VP, VP, I64, F32, F32, VP]
     L.moe_strerror.argtypes = [C.c_int]
     L.moe_strerror.restype = C.c_char_p
@@ -116,7 +125,7 @@ def dims_of(p: Preset, T: Optional[int] = None) -> Dims:
 
 def opts_of(p: Preset) -> Opts:
     return Opts(SCORE[p.score], ACT[p.act], DTYPE[p.dtype], int(p.renorm), p.gate_scale,
-                p.capacity_factor, p.aux_coef, p.z_coef, ROUTING[p.routing])
+                p.capacity_factor, p.aux_coef, p.z_coef, ROUTING[p.routing], PRIORITY[p.priority])
 
 
 def capacity(p: Preset, T: Optional[int] = None) -> int:
@@ -153,7 +162,7 @@ class Workspace:
 
 # --------------------------------------------------------------------------- steps
 def route(p: Preset, x, Wg, offset=None, sel_bias=None, *, want_scores=False, want_logits=False,
-          ws: Optional[Workspace] = None):
+          ri: Optional["LayerRouterInputs"] = None, ws: Optional[Workspace] = None):
     """moe_route: returns dict(idx [T,k] i32, gate [T,k] f32, counts [E], losses [2], ...)."""
     dev = x.device
     T = x.shape[0]
@@ -171,7 +180,7 @@ def route(p: Preset, x, Wg, offset=None, sel_bias=None, *, want_scores=False, wa
     _check("moe_route", lib().moe_route(
         C.byref(dims_of(p, T)), C.byref(opts_of(p)), _ptr(x), _ptr(Wg), _ptr(offset), _ptr(sel_bias),
         _ptr(out["idx"]), _ptr(out["gate"]), _ptr(out["scores"]), _ptr(out["logits"]),
-        _ptr(out["counts"]), _ptr(out["losses"]), _ptr(buf), nb, _stream()))
+        _ptr(out["counts"]), _ptr(out["losses"]), _ri_c(ri), _ptr(buf), nb, _stream()))
     return out
 
 
@@ -251,6 +260,29 @@ class LayerWeights:
                           self.Ws2)))
 
 
+@dataclass
+class LayerRouterInputs:
+    """The variant routers' per-call inputs on the device (see moe_router_inputs)."""
+    W_noise: Optional[torch.Tensor] = None
+    noise: Optional[torch.Tensor] = None
+    uniform: Optional[torch.Tensor] = None
+    token_ids: Optional[torch.Tensor] = None
+
+    def c(self) -> RouterInputs:
+        return RouterInputs(*(None if t is None else t.data_ptr() for t in
+                              (self.W_noise, self.noise, self.uniform, self.token_ids)))
+
+
+def _ri_c(ri: Optional[LayerRouterInputs]):
+    return None if ri is None else C.byref(ri.c())
+
+
+def router_inputs_to_device(inp: dict, device) -> LayerRouterInputs:
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return LayerRouterInputs(W_noise=t(inp.get("W_noise")), noise=t(inp.get("noise")),
+                             uniform=t(inp.get("uniform")), token_ids=t(inp.get("token_ids")))
+
+
 def weights_to_device(p: Preset, inp: dict, device) -> LayerWeights:
     wd = TORCH_DTYPE[p.dtype]
     # upload fp32 and convert on the device (values are already representable in dt)
@@ -272,7 +304,8 @@ def alloc_saved(p: Preset, device, T: Optional[int] = None) -> dict:
              row_of_slot=e(T, p.k, dt=torch.int32), token_of_row=e(Tk, dt=torch.int32),
              x_perm=e(Tk, p.d, dt=xd), h=e(Tk, nu, dt=xd), a=e(Tk, p.F, dt=xd), o=e(Tk, p.d),
              h_shared=e(T, 2 * p.F_shared, dt=xd) if p.F_shared else None,
-             a_shared=e(T, p.F_shared, dt=xd) if p.F_shared else None, losses=e(2))
+             a_shared=e(T, p.F_shared, dt=xd) if p.F_shared else None, losses=e(2),
+             noise_logits=e(T, p.E) if p.routing == "noisy_topk" else None)
     return s
 
 
@@ -283,7 +316,8 @@ def _saved_c(s: Optional[dict]):
 
 
 def layer_fwd(p: Preset, w: LayerWeights, x, *, saved: Optional[dict] = None, stats: bool = False,
-              ws: Optional[Workspace] = None, y: Optional[torch.Tensor] = None):
+              ri: Optional[LayerRouterInputs] = None, ws: Optional[Workspace] = None,
+              y: Optional[torch.Tensor] = None):
     """moe_layer_fwd; returns y (and the stats dict when asked)."""
     dev = x.device
     T = x.shape[0]
@@ -302,27 +336,29 @@ def layer_fwd(p: Preset, w: LayerWeights, x, *, saved: Optional[dict] = None, st
     nb = workspace_size(p, with_bwd=saved is not None, T=T)
     buf = ws.get(nb)
     _check("moe_layer_fwd", lib().moe_layer_fwd(
-        C.byref(dims_of(p, T)), C.byref(opts_of(p)), C.byref(w.c()), _ptr(x), _ptr(y),
+        C.byref(dims_of(p, T)), C.byref(opts_of(p)), C.byref(w.c()), _ri_c(ri), _ptr(x), _ptr(y),
         _saved_c(saved), st_c, _ptr(buf), nb, _stream()))
     return (y, st) if stats else y
 
 
-def layer_bwd(p: Preset, w: LayerWeights, x, saved: dict, dy, *, ws: Optional[Workspace] = None):
-    """moe_layer_bwd; returns dict(dx, dWg, dW13, dW2, dWs13, dWs2)."""
+def layer_bwd(p: Preset, w: LayerWeights, x, saved: dict, dy, *,
+              ri: Optional[LayerRouterInputs] = None, ws: Optional[Workspace] = None):
+    """moe_layer_bwd; returns dict(dx, dWg, dW13, dW2, dWs13, dWs2, dW_noise)."""
     dev = x.device
     T = x.shape[0]
     e = lambda *s: torch.empty(*s, dtype=torch.float32, device=dev)
     nu = 2 * p.F if p.act == "swiglu" else p.F
     g = dict(dx=e(T, p.d), dWg=e(p.d, p.E), dW13=e(p.E, nu, p.d), dW2=e(p.E, p.d, p.F),
              dWs13=e(2 * p.F_shared, p.d) if p.F_shared else None,
-             dWs2=e(p.d, p.F_shared) if p.F_shared else None)
+             dWs2=e(p.d, p.F_shared) if p.F_shared else None,
+             dW_noise=e(p.d, p.E) if p.routing == "noisy_topk" else None)
     gc = Grads(*(None if g[n] is None else g[n].data_ptr() for n, _ in Grads._fields_))
     ws = ws or Workspace(dev)
     nb = workspace_size(p, with_bwd=True, T=T)
     buf = ws.get(nb)
     _check("moe_layer_bwd", lib().moe_layer_bwd(
-        C.byref(dims_of(p, T)), C.byref(opts_of(p)), C.byref(w.c()), _ptr(x), _saved_c(saved),
-        _ptr(dy), _ptr(g["dx"]), C.byref(gc), _ptr(buf), nb, _stream()))
+        C.byref(dims_of(p, T)), C.byref(opts_of(p)), C.byref(w.c()), _ri_c(ri), _ptr(x),
+        _saved_c(saved), _ptr(dy), _ptr(g["dx"]), C.byref(gc), _ptr(buf), nb, _stream()))
     return g
 
 
@@ -332,8 +368,10 @@ class Layer:
     forward or backward call is a single C call that only enqueues kernels."""
 
     def __init__(self, p: Preset, w: LayerWeights, device, T: Optional[int] = None,
-                 train: bool = False):
+                 train: bool = False, ri: Optional[LayerRouterInputs] = None):
         self.p, self.w, self.T = p, w, p.T if T is None else T
+        self.ri = ri
+        self._ri = ri.c() if ri is not None else None
         self.device = torch.device(device)
         self.train = train
         self._dims, self._opts, self._w = dims_of(p, self.T), opts_of(p), w.c()
@@ -349,7 +387,8 @@ class Layer:
 
     def fwd(self, x: torch.Tensor) -> torch.Tensor:
         _check("moe_layer_fwd", lib().moe_layer_fwd(
-            C.byref(self._dims), C.byref(self._opts), C.byref(self._w), C.c_void_p(x.data_ptr()),
+            C.byref(self._dims), C.byref(self._opts), C.byref(self._w),
+            C.byref(self._ri) if self._ri is not None else None, C.c_void_p(x.data_ptr()),
             C.c_void_p(self.y.data_ptr()), C.byref(self._saved_c) if self.train else None, None,
             C.c_void_p(self.ws.data_ptr()), self.ws_bytes, _stream()))
         return self.y
@@ -361,12 +400,14 @@ class Layer:
             nu = 2 * p.F if p.act == "swiglu" else p.F
             self.grads = dict(dWg=e(p.d, p.E), dW13=e(p.E, nu, p.d), dW2=e(p.E, p.d, p.F),
                               dWs13=e(2 * p.F_shared, p.d) if p.F_shared else None,
-                              dWs2=e(p.d, p.F_shared) if p.F_shared else None)
+                              dWs2=e(p.d, p.F_shared) if p.F_shared else None,
+                              dW_noise=e(p.d, p.E) if p.routing == "noisy_topk" else None)
             self.dx = e(self.T, p.d)
             self._grads_c = Grads(*(None if self.grads[n] is None else self.grads[n].data_ptr()
                                     for n, _ in Grads._fields_))
         _check("moe_layer_bwd", lib().moe_layer_bwd(
-            C.byref(self._dims), C.byref(self._opts), C.byref(self._w), C.c_void_p(x.data_ptr()),
+            C.byref(self._dims), C.byref(self._opts), C.byref(self._w),
+            C.byref(self._ri) if self._ri is not None else None, C.c_void_p(x.data_ptr()),
             C.byref(self._saved_c), C.c_void_p(dy.data_ptr()), C.c_void_p(self.dx.data_ptr()),
             C.byref(self._grads_c), C.c_void_p(self.ws.data_ptr()), self.ws_bytes, _stream()))
         return dict(self.grads, dx=self.dx)

@@ -38,7 +38,9 @@ int check_dims(const moe_dims* d, const moe_opts* o) {
   if (!d || !o) return MOE_ERR_INVALID_ARG;
   if (o->dtype != MOE_DTYPE_F32 && o->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (o->score < MOE_SCORE_SOFTMAX || o->score > MOE_SCORE_SQRT_SOFTPLUS) return MOE_ERR_INVALID_ARG;
-  if (o->routing < MOE_ROUTING_TOPK || o->routing > MOE_ROUTING_UNIFORM) return MOE_ERR_INVALID_ARG;
+  if (o->routing < MOE_ROUTING_TOPK || o->routing > MOE_ROUTING_HASH) return MOE_ERR_INVALID_ARG;
+  if (o->priority != MOE_PRIORITY_TOKEN && o->priority != MOE_PRIORITY_SLOT) return MOE_ERR_INVALID_ARG;
+  if (o->routing == MOE_ROUTING_RANDOM_SECOND && d && d->k != 2) return MOE_ERR_INVALID_ARG;
   if (o->act != MOE_ACT_SWIGLU && o->act != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
   if (d->T < 0 || d->E < 1 || d->k < 1 || d->k > d->E || d->F_shared < 0) return MOE_ERR_INVALID_ARG;
   if (!isfinite(o->gate_scale) || !isfinite(o->capacity_factor) || !isfinite(o->aux_coef) ||
@@ -65,9 +67,23 @@ bool route_mfma(const moe_dims* d, const moe_opts* o, int EP) {
   return o->dtype == MOE_DTYPE_BF16 && d->d % (64 * route_ks(EP)) == 0;
 }
 
+// The variant routers' inputs that opts->routing needs must be present.
+int check_router_inputs(const moe_opts* o, const moe_router_inputs* ri) {
+  switch (o->routing) {
+    case MOE_ROUTING_NOISY_TOPK:
+      return ri && ri->W_noise && ri->noise ? MOE_OK : MOE_ERR_INVALID_ARG;
+    case MOE_ROUTING_RANDOM_SECOND:
+      return ri && ri->uniform ? MOE_OK : MOE_ERR_INVALID_ARG;
+    case MOE_ROUTING_HASH:
+      return ri && ri->token_ids ? MOE_OK : MOE_ERR_INVALID_ARG;
+    default:
+      return MOE_OK;
+  }
+}
+
 // ---- workspace plans -------------------------------------------------------
-struct RouteWs { size_t wsplit, part_p, part_cnt, part_lse2, part_nf; int nblk, EP; };
-RouteWs plan_route(Carver& c, const moe_dims* d) {
+struct RouteWs { size_t wsplit, part_p, part_cnt, part_lse2, part_nf, zn; int nblk, EP; };
+RouteWs plan_route(Carver& c, const moe_dims* d, const moe_opts* o) {
   RouteWs r;
   r.EP = route_pad_experts(int(d->E));
   r.nblk = int(cdiv(d->T, ROUTE_BT));
@@ -76,13 +92,14 @@ RouteWs plan_route(Carver& c, const moe_dims* d) {
   r.part_cnt = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_lse2 = c.take(size_t(r.nblk) * 4);
   r.part_nf = c.take(size_t(r.nblk) * 4);
+  r.zn = c.take(o->routing == MOE_ROUTING_NOISY_TOPK ? size_t(d->T) * d->E * 4 : 0);
   return r;
 }
 
 struct PermWs { size_t blockcnt, blockbase; int nblk; };
-PermWs plan_perm(Carver& c, const moe_dims* d) {
+PermWs plan_perm(Carver& c, const moe_dims* d, const moe_opts* o) {
   PermWs p;
-  p.nblk = int(cdiv(d->T, DISP_TB));
+  p.nblk = dispatch_blocks(int(d->T), int(d->k), o->priority == MOE_PRIORITY_SLOT);
   p.blockcnt = c.take(size_t(p.nblk) * d->E * 4);
   p.blockbase = c.take(size_t(p.nblk) * d->E * 4);
   return p;
@@ -107,8 +124,8 @@ FwdWs plan_fwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   FwdWs f;
   const int eb = elem_bytes(o);
   const int64_t Tk = d->T * d->k;
-  f.route = plan_route(c, d);
-  f.perm = plan_perm(c, d);
+  f.route = plan_route(c, d, o);
+  f.perm = plan_perm(c, d, o);
   f.ffn = plan_ffn(c, d->E, Tk, d->F, eb, false);
   f.ffn_shared = plan_ffn(c, 1, d->T, d->F_shared, eb, false);
   f.idx = c.take(size_t(Tk) * 4);
@@ -146,10 +163,11 @@ int check_ws(const void* ws, size_t have, size_t need) {
 }
 
 // ---- the steps, with validated arguments --------------------------------
+// zn_out: where noisy top-k keeps x . W_noise (nullable: the workspace).
 int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* Wg,
-             const float* offset, const float* bias, int32_t* idx, float* gate, float* scores,
-             float* logits, int32_t* counts, float* losses, int32_t* n_nonfinite, void* ws,
-             const RouteWs& rw, hipStream_t st) {
+             const float* offset, const float* bias, const moe_router_inputs* ri, int32_t* idx,
+             float* gate, float* scores, float* logits, int32_t* counts, float* losses,
+             int32_t* n_nonfinite, float* zn_out, void* ws, const RouteWs& rw, hipStream_t st) {
   RouteArgs a{};
   a.x = x;
   a.x_bf16 = o->dtype == MOE_DTYPE_BF16;
@@ -175,6 +193,21 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
   a.part_lse2 = at<float>(ws, rw.part_lse2);
   a.part_nf = at<int32_t>(ws, rw.part_nf);
   const bool mfma = route_mfma(d, o, rw.EP);
+  if (o->routing == MOE_ROUTING_NOISY_TOPK) {
+    // first pass: zn = x . W_noise (raw logits of the noise projection)
+    float* zn = zn_out ? zn_out : at<float>(ws, rw.zn);
+    RouteArgs an = a;
+    an.Wg = ri->W_noise;
+    an.offset = nullptr;
+    an.logits = zn;
+    an.logits_only = 1;
+    if (mfma) MOE_TRY(launch_wg_split(ri->W_noise, a.d, a.E, a.EP, at<uint16_t>(ws, rw.wsplit), st));
+    MOE_TRY(launch_route(an, mfma, st));
+    a.noise = ri->noise;
+    a.noise_logit = zn;
+  }
+  if (o->routing == MOE_ROUTING_RANDOM_SECOND) a.uniform = ri->uniform;
+  if (o->routing == MOE_ROUTING_HASH) a.token_ids = ri->token_ids;
   if (mfma) MOE_TRY(launch_wg_split(Wg, a.d, a.E, a.EP, at<uint16_t>(ws, rw.wsplit), st));
   MOE_TRY(launch_route(a, mfma, st));
   if (counts || losses || n_nonfinite)
@@ -189,10 +222,11 @@ int do_permute(const moe_dims* d, const moe_opts* o, const void* x, const int32_
   const int64_t C = capacity_of(d, o);
   int32_t* bc = at<int32_t>(ws, pw.blockcnt);
   int32_t* bb = at<int32_t>(ws, pw.blockbase);
-  MOE_TRY(launch_dispatch_hist(idx, T, k, E, bc, st));
+  const bool slot_major = o->priority == MOE_PRIORITY_SLOT;
+  MOE_TRY(launch_dispatch_hist(idx, T, k, E, slot_major, bc, st));
   MOE_TRY(launch_dispatch_scan(bc, pw.nblk, E, C, bb, counts, offsets, n_dropped, st));
-  MOE_TRY(launch_dispatch_permute(idx, T, k, E, C, bb, offsets, x, int(d->d), elem_bytes(o), ros,
-                                  tor, xperm, st));
+  MOE_TRY(launch_dispatch_permute(idx, T, k, E, C, slot_major, bb, offsets, x, int(d->d),
+                                  elem_bytes(o), ros, tor, xperm, st));
   return MOE_OK;
 }
 
@@ -263,6 +297,7 @@ struct BwdWs {
   FfnWs ffn, ffn_s;
   size_t dO, dg, dH, dXp, dz, dwg_part, dxr;
   size_t dyx, dHs, dxs, soff, ssplit_off, spart;
+  size_t dzn, dwn_part;   // noisy top-k
 };
 BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   BwdWs b;
@@ -277,7 +312,11 @@ BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   b.dXp = c.take(size_t(R) * d->d * 4);
   b.dz = c.take(size_t(d->T) * d->E * 4);
   b.dwg_part = c.take(size_t(dwg_split(d)) * d->d * d->E * 4);
-  b.dxr = c.take(size_t(d->T) * d->d * 4);
+  const bool noisy = o->routing == MOE_ROUTING_NOISY_TOPK;
+  // noisy top-k: dx_router = dz Wg^T + dzn W_noise^T as two partials summed in order
+  b.dxr = c.take(size_t(noisy ? 2 : 1) * d->T * d->d * 4);
+  b.dzn = c.take(noisy ? size_t(d->T) * d->E * 4 : 0);
+  b.dwn_part = c.take(noisy ? size_t(dwg_split(d)) * d->d * d->E * 4 : 0);
   b.dyx = c.take(Fs ? size_t(d->T) * d->d * eb : 0);
   b.dHs = c.take(size_t(d->T) * 2 * Fs * eb);
   b.dxs = c.take(Fs ? size_t(d->T) * d->d * 4 : 0);
@@ -358,18 +397,18 @@ int moe_workspace_size(const moe_dims* d, const moe_opts* o, int with_bwd, size_
 int moe_route(const moe_dims* d, const moe_opts* o, const void* x, const float* Wg,
               const float* logit_offset, const float* sel_bias, int32_t* topk_idx,
               float* topk_gate, float* scores, float* logits, int32_t* counts, float* losses,
-              void* ws, size_t ws_bytes, void* stream) {
+              const moe_router_inputs* ri, void* ws, size_t ws_bytes, void* stream) {
   int s = check_dims(d, o);
   if (s) return s;
   if (d->T == 0) return MOE_OK;
   if (!x || !Wg || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x)) return MOE_ERR_INVALID_ARG;
+  if ((s = check_router_inputs(o, ri))) return s;
   Carver c;
-  const RouteWs rw = plan_route(c, d);
+  const RouteWs rw = plan_route(c, d, o);
   if ((s = check_ws(ws, ws_bytes, c.off))) return s;
-  if (d->T == 0) return MOE_OK;
-  return do_route(d, o, x, Wg, logit_offset, sel_bias, topk_idx, topk_gate, scores, logits, counts,
-                  losses, nullptr, ws, rw, static_cast<hipStream_t>(stream));
+  return do_route(d, o, x, Wg, logit_offset, sel_bias, ri, topk_idx, topk_gate, scores, logits,
+                  counts, losses, nullptr, nullptr, ws, rw, static_cast<hipStream_t>(stream));
 }
 
 int moe_permute(const moe_dims* d, const moe_opts* o, const void* x, const int32_t* topk_idx,
@@ -381,7 +420,7 @@ int moe_permute(const moe_dims* d, const moe_opts* o, const void* x, const int32
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
   Carver c;
-  const PermWs pw = plan_perm(c, d);
+  const PermWs pw = plan_perm(c, d, o);
   if ((s = check_ws(ws, ws_bytes, c.off))) return s;
   if (d->T == 0) {
     // no tokens: every expert is empty
@@ -424,13 +463,15 @@ int moe_combine(const moe_dims* d, const float* out_perm, const int32_t* row_of_
                                    int(d->k), int(d->d), y, static_cast<hipStream_t>(stream)));
 }
 
-int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, const void* x,
-                  float* y, moe_saved* sv, moe_stats* stats, void* ws, size_t ws_bytes,
-                  void* stream) {
+int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
+                  const moe_router_inputs* ri, const void* x, float* y, moe_saved* sv,
+                  moe_stats* stats, void* ws, size_t ws_bytes, void* stream) {
   int s = check_dims(d, o);
   if (s) return s;
   if (d->T == 0) return MOE_OK;
   if (!w || !x || !y || !w->Wg || !w->W13 || !w->W2) return MOE_ERR_INVALID_ARG;
+  if ((s = check_router_inputs(o, ri))) return s;
+  if (sv && o->routing == MOE_ROUTING_NOISY_TOPK && !sv->noise_logits) return MOE_ERR_INVALID_ARG;
   if (d->F_shared > 0 && (!w->Ws13 || !w->Ws2)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(y) || !aligned16(w->W13) || !aligned16(w->W2) ||
       (d->F_shared > 0 && (!aligned16(w->Ws13) || !aligned16(w->Ws2))))
@@ -463,9 +504,9 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
                      : (stats && stats->losses) ? stats->losses
                      : want_losses ? at<float>(ws, f.losses) : nullptr;
 
-  s = do_route(d, o, x, w->Wg, w->logit_offset, w->sel_bias, idx, gate, nullptr,
+  s = do_route(d, o, x, w->Wg, w->logit_offset, w->sel_bias, ri, idx, gate, nullptr,
                sv ? sv->logits : nullptr, nullptr, losses, stats ? stats->n_nonfinite : nullptr,
-               ws, f.route, st);
+               sv ? sv->noise_logits : nullptr, ws, f.route, st);
   if (s) return s;
   s = do_permute(d, o, x, idx, counts, offsets, ros, tor, xperm, stats ? stats->n_dropped : nullptr,
                  ws, f.perm, st);
@@ -493,13 +534,17 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
   return MOE_OK;
 }
 
-int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, const void* x,
-                  const moe_saved* sv, const float* dy, float* dx, moe_grads* grads, void* ws,
-                  size_t ws_bytes, void* stream) {
+int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
+                  const moe_router_inputs* ri, const void* x, const moe_saved* sv,
+                  const float* dy, float* dx, moe_grads* grads, void* ws, size_t ws_bytes,
+                  void* stream) {
   int s = check_dims(d, o);
   if (s) return s;
   if (d->T == 0) return MOE_OK;
   const int64_t Fs = d->F_shared;
+  const bool noisy = o->routing == MOE_ROUTING_NOISY_TOPK;
+  if ((s = check_router_inputs(o, ri))) return s;
+  if (noisy && (!sv || !sv->noise_logits || !grads || !grads->dW_noise)) return MOE_ERR_INVALID_ARG;
   if (!w || !x || !sv || !dy || !dx || !grads || !w->Wg || !w->W13 || !w->W2) return MOE_ERR_INVALID_ARG;
   if (!grads->dWg || !grads->dW13 || !grads->dW2) return MOE_ERR_INVALID_ARG;
   if (Fs > 0 && (!w->Ws13 || !w->Ws2 || !grads->dWs13 || !grads->dWs2 || !sv->h_shared ||
@@ -575,7 +620,20 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w, co
   MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
                               at<float>(ws, b.dwg_part), grads->dWg, st));
   float* dxr = at<float>(ws, b.dxr);
-  MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, st));
+  if (noisy) {
+    // H = z + noise * softplus(zn): dzn = dz * noise * sigmoid(zn);
+    // dW_noise = x^T dzn; dx_router = dz Wg^T + dzn W_noise^T
+    float* dzn = at<float>(ws, b.dzn);
+    float* part = dxr + int64_t(T) * D;
+    MOE_TRY(launch_noise_grad(dz, ri->noise, sv->noise_logits, int64_t(T) * E, dzn, st));
+    MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dzn, E, 1, D, E, T, dwg_split(d),
+                                at<float>(ws, b.dwn_part), grads->dW_noise, st));
+    MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, st));
+    MOE_TRY(launch_strided_gemm(dzn, false, E, 1, ri->W_noise, 1, E, T, D, E, 1, part, nullptr, st));
+    MOE_TRY(launch_sum_partials(dxr, 2, int64_t(T) * D, dxr, st));
+  } else {
+    MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, st));
+  }
   MOE_TRY(launch_unpermute_sum(at<float>(ws, b.dXp), sv->row_of_slot, dxs, dxr, T, k, D, dx, st));
   return MOE_OK;
 }

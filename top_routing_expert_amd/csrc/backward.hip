@@ -131,7 +131,10 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
   float S = 0.0f;
 #pragma unroll
   for (int j = 0; j < BWD_KMAX; ++j) {
+    // a slot skipped by the random second-expert rule reads E + expert: it has
+    // no gradient of its own (dg = 0) but stays in the gate normalisation
     ix[j] = j < k ? idx[int64_t(t) * k + j] : -1;
+    if (ix[j] >= E && ix[j] < 2 * E) ix[j] -= E;
     dgv[j] = j < k ? dg[int64_t(t) * k + j] : 0.0f;
     ssel[j] = 0.0f;
     if (j < k && unsigned(ix[j]) < unsigned(E)) {
@@ -260,6 +263,21 @@ __global__ __launch_bounds__(256) void strided_gemm_kernel(
       if (gn < N) Pz[int64_t(gm) * N + gn] = acc[i][j];
     }
   }
+}
+
+// Noisy top-k: the logits are H = z + noise * softplus(zn), zn = x . W_noise, so
+// dJ/dzn = dJ/dH * noise * sigmoid(zn).
+__global__ void noise_grad_kernel(const float* __restrict__ dz, const float* __restrict__ noise,
+                                  const float* __restrict__ zn, int64_t n, float* __restrict__ dzn) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  dzn[i] = dz[i] * noise[i] / (1.0f + expf(-zn[i]));
+}
+
+hipError_t launch_noise_grad(const float* dz, const float* noise, const float* zn, int64_t n,
+                             float* dzn, hipStream_t st) {
+  noise_grad_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(dz, noise, zn, n, dzn);
+  return hipGetLastError();
 }
 
 // out[i] = sum over z of P[z][i], z in order.

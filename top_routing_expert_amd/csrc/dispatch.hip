@@ -8,6 +8,10 @@
 // index, built from per-block counts (scanned in block order), per-wave counts
 // (scanned in wave order) and a ballot/popcount rank inside the wave.  No
 // global atomics decide any order.
+//
+// Slot priority (every token's first choice before any second choice, GShard's
+// overflow order): the same kernels run over the T*k slots in slot-major order,
+// as virtual tokens v = j*T + t with one slot each.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -18,13 +22,18 @@ constexpr int DISP_KMAX = 16;
 // Per-block histogram of the slots' experts.  LDS atomics only count, so the
 // result is order independent.  Entries outside [0, E) are skipped.
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ idx, int T,
-                                                            int k, int E,
+                                                            int k, int E, int slot_major,
                                                             int32_t* __restrict__ blockcnt) {
   __shared__ int32_t hist[256];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
   const int t = blockIdx.x * DISP_TB + threadIdx.x;
-  if (t < T) {
+  if (slot_major) {
+    if (int64_t(t) < int64_t(T) * k) {
+      const int e = idx[int64_t(t % T) * k + t / T];
+      if (unsigned(e) < unsigned(E)) atomicAdd(&hist[e], 1);
+    }
+  } else if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[int64_t(t) * k + j];
       if (unsigned(e) < unsigned(E)) atomicAdd(&hist[e], 1);
@@ -89,7 +98,9 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __res
 //   2. rank in expert = blockbase[b][e] + counts of lower waves + rank in wave;
 //      kept iff rank < C; row = offsets[e] + rank;
 // The row copy is a separate, token-parallel kernel (permute_copy_kernel).
-template <int KM>
+// SLOT: the block's "tokens" are the slot-major virtual tokens v = j*T + t
+// (KM = 1); their slot is (v % T, v / T).
+template <int KM, bool SLOT>
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int64_t C,
     const int32_t* __restrict__ blockbase, const int32_t* __restrict__ offsets,
@@ -97,8 +108,11 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
   __shared__ int32_t wavecnt[4][256];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   for (int i = tid; i < 4 * 256; i += blockDim.x) (&wavecnt[0][0])[i] = 0;
-  const int t = blockIdx.x * DISP_TB + tid;
-  const bool valid = t < T;
+  const int v = blockIdx.x * DISP_TB + tid;
+  const bool valid = SLOT ? int64_t(v) < int64_t(T) * k : v < T;
+  const int t = SLOT ? (valid ? v % T : 0) : v;                 // token of this lane's slots
+  const int64_t slot0 = SLOT ? int64_t(t) * k + (valid ? v / T : 0) : int64_t(t) * k;
+  const int kk = SLOT ? 1 : k;                                  // slots per lane
   int ex[KM];
   int rk[KM];
   uint32_t pending = 0;
@@ -106,8 +120,8 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
   for (int j = 0; j < KM; ++j) {
     ex[j] = -1;
     rk[j] = 0;
-    if (valid && j < k) {
-      const int e = idx[int64_t(t) * k + j];
+    if (valid && j < kk) {
+      const int e = idx[slot0 + j];
       if (unsigned(e) < unsigned(E)) {
         ex[j] = e;
         pending |= 1u << j;
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
-    if (j < k) {
+    if (j < kk) {
       int row = -1;
       const int e = ex[j];
       if (e >= 0) {
@@ -156,7 +170,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
           token_of_row[row] = t;
         }
       }
-      if (valid) row_of_slot[int64_t(t) * k + j] = row;
+      if (valid) row_of_slot[slot0 + j] = row;
     }
   }
 }
@@ -190,10 +204,15 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const int32_t* __rest
   }
 }
 
-hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, int32_t* blockcnt,
-                                hipStream_t st) {
-  const unsigned nblk = unsigned(cdiv(T, DISP_TB));
-  dispatch_hist_kernel<<<dim3(nblk), dim3(256), 0, st>>>(idx, T, k, E, blockcnt);
+int dispatch_blocks(int T, int k, bool slot_major) {
+  return int(cdiv(slot_major ? int64_t(T) * k : int64_t(T), DISP_TB));
+}
+
+hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, bool slot_major,
+                                int32_t* blockcnt, hipStream_t st) {
+  const unsigned nblk = unsigned(dispatch_blocks(T, k, slot_major));
+  dispatch_hist_kernel<<<dim3(nblk), dim3(256), 0, st>>>(idx, T, k, E, slot_major ? 1 : 0,
+                                                         blockcnt);
   return hipGetLastError();
 }
 
@@ -206,19 +225,27 @@ hipError_t launch_dispatch_scan(const int32_t* blockcnt, int nblk, int E, int64_
 }
 
 hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int64_t C,
-                                   const int32_t* blockbase, const int32_t* offsets,
-                                   const void* x, int d, int elem_bytes, int32_t* row_of_slot,
-                                   int32_t* token_of_row, void* x_perm, hipStream_t st) {
-  const unsigned nblk = unsigned(cdiv(T, DISP_TB));
+                                   bool slot_major, const int32_t* blockbase,
+                                   const int32_t* offsets, const void* x, int d, int elem_bytes,
+                                   int32_t* row_of_slot, int32_t* token_of_row, void* x_perm,
+                                   hipStream_t st) {
+  const unsigned nblk = unsigned(dispatch_blocks(T, k, slot_major));
   const unsigned ncopy = unsigned(cdiv(T, 4));
   const int row_bytes = d * elem_bytes;
   const auto* xs = static_cast<const uint8_t*>(x);
   auto* xp = static_cast<uint8_t*>(x_perm);
 #define MOE_PERMUTE(KM)                                                                        \
-  dispatch_rank_kernel<KM><<<dim3(nblk), dim3(256), 0, st>>>(idx, T, k, E, C, blockbase,        \
-                                                             offsets, row_of_slot, token_of_row); \
+  dispatch_rank_kernel<KM, false><<<dim3(nblk), dim3(256), 0, st>>>(                           \
+      idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);                         \
   permute_copy_kernel<KM><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp)
-  if (k <= 1) { MOE_PERMUTE(1); }
+  if (slot_major) {
+    dispatch_rank_kernel<1, true><<<dim3(nblk), dim3(256), 0, st>>>(
+        idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);
+    if (k <= 2) permute_copy_kernel<2><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
+    else if (k <= 4) permute_copy_kernel<4><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
+    else if (k <= 8) permute_copy_kernel<8><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
+    else permute_copy_kernel<16><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
+  } else if (k <= 1) { MOE_PERMUTE(1); }
   else if (k <= 2) { MOE_PERMUTE(2); }
   else if (k <= 4) { MOE_PERMUTE(4); }
   else if (k <= 8) { MOE_PERMUTE(8); }

@@ -16,7 +16,12 @@ struct RouteArgs {
   const float* bias;        // nullable [E]
   int T, d, E, k, EP;
   int score, renorm;
-  int routing;              // 0 top-k, 1 forced-uniform (slot j of token t -> (t*k + j) mod E)
+  int routing;              // moe_routing: 0 top-k, 1 uniform, 2 noisy top-k, 3 random second, 4 hash
+  int logits_only;          // write the raw logits x . Wg only (the noise projection pass)
+  const float* noise;       // noisy top-k: [T, E] standard-normal draws
+  const float* noise_logit; // noisy top-k: [T, E] x . W_noise
+  const float* uniform;     // random second expert: [T] draws in [0, 1)
+  const int32_t* token_ids; // hash routing: [T]
   float gate_scale;
   int32_t* idx;             // [T, k]
   float* gate;              // [T, k]
@@ -38,15 +43,19 @@ hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, flo
 
 // ------------------------------------------------------------------ dispatch
 constexpr int DISP_TB = 256;   // tokens per dispatch block
-hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, int32_t* blockcnt,
-                                hipStream_t st);
+// Blocks of the histogram / rank kernels (and rows of their per-block count
+// arrays): over tokens, or over the T*k slots in slot-major order.
+int dispatch_blocks(int T, int k, bool slot_major);
+hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, bool slot_major,
+                                int32_t* blockcnt, hipStream_t st);
 hipError_t launch_dispatch_scan(const int32_t* blockcnt, int nblk, int E, int64_t C,
                                 int32_t* blockbase, int32_t* counts, int32_t* offsets,
                                 int32_t* n_dropped, hipStream_t st);
 hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int64_t C,
-                                   const int32_t* blockbase, const int32_t* offsets,
-                                   const void* x, int d, int elem_bytes, int32_t* row_of_slot,
-                                   int32_t* token_of_row, void* x_perm, hipStream_t st);
+                                   bool slot_major, const int32_t* blockbase,
+                                   const int32_t* offsets, const void* x, int d, int elem_bytes,
+                                   int32_t* row_of_slot, int32_t* token_of_row, void* x_perm,
+                                   hipStream_t st);
 
 // ------------------------------------------------------------------ grouped GEMM
 // Epilogues: fp32 store; forward activations (GELU, SwiGLU of two panels);
@@ -104,6 +113,9 @@ hipError_t launch_router_bwd(const float* z, const int32_t* idx, const float* dg
 hipError_t launch_strided_gemm(const void* A, bool a_bf16, int64_t sam, int64_t sak, const float* B,
                                int64_t sbk, int64_t sbn, int M, int N, int K, int nsplit, float* P,
                                float* out, hipStream_t st);
+// dzn = dz * noise * sigmoid(zn), n elements
+hipError_t launch_noise_grad(const float* dz, const float* noise, const float* zn, int64_t n,
+                             float* dzn, hipStream_t st);
 // out[i] = sum over z of P[z * n + i], z = 0..nz-1 in order
 hipError_t launch_sum_partials(const float* P, int nz, int64_t n, float* out, hipStream_t st);
 hipError_t launch_unpermute_sum(const float* dxp, const int32_t* ros, const float* e1,

@@ -85,11 +85,23 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
 #pragma unroll
       for (int q = 0; q < KS; ++q) zz += zs[q][tl][e];
       zz += off[v];
+      if (a.noise && valid && e < E) {
+        // H = z + noise * softplus(x . W_noise)
+        const float zn = a.noise_logit[int64_t(t) * E + e];
+        zz += a.noise[int64_t(t) * E + e] * (fmaxf(zn, 0.0f) + log1pf(expf(-fabsf(zn))));
+      }
       z[v] = zz;
       if (e < E) {
         m = fmaxf(m, zz);
         finite = finite && isfinite(zz);
       }
+    }
+    if (a.logits_only) {
+      if (valid)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (lg + LG * v < E) a.logits[int64_t(t) * E + lg + LG * v] = z[v];
+      continue;
     }
     m = group_max<LG>(m);
     float sexp = 0.0f;
@@ -132,6 +144,8 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
         int e;
         if (a.routing == 1) {
           e = int((int64_t(t) * k + j) % E);
+        } else if (a.routing == 4) {
+          e = valid ? int((int64_t(fmix32(uint32_t(a.token_ids[t]))) + j) % E) : 0;
         } else {
           uint64_t best = 0;
 #pragma unroll
@@ -153,12 +167,22 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
         gs += ge;
       }
     }
+    // Random second expert (k = 2): keep it iff u < 2 s2 / (s1 + s2); a skipped
+    // slot is reported as E + expert and not counted.
+    bool skip2 = false;
+    if (a.routing == 3 && valid) {
+      skip2 = !(a.uniform[t] < 2.0f * gsel[1] / (gsel[0] + gsel[1]));
+      if (skip2)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (lg + LG * v == isel[1]) cacc[v] -= 1;
+    }
     if (valid) {
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (j < k && lg == j) {
           const float g = a.renorm ? (gsel[j] / gs) * a.gate_scale : gsel[j] * a.gate_scale;
-          a.idx[int64_t(t) * k + j] = isel[j];
+          a.idx[int64_t(t) * k + j] = isel[j] + ((j == 1 && skip2) ? E : 0);
           a.gate[int64_t(t) * k + j] = g;
         }
       }
