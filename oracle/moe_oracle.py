@@ -63,6 +63,7 @@ __all__ = [
     "logsumexp_rows", "router_losses", "route", "dispatch", "permute", "silu", "gelu",
     "expert_ffn", "shared_expert", "combine", "bias_update", "layer_fwd", "layer_bwd",
     "router_bwd", "expert_bwd", "uniform_assignment", "hash_assignment", "fmix32", "softplus",
+    "score_histogram", "quantile_bias", "load_report", "expert_output_norms",
     "NEAR_TIE_REL",
 ]
 
@@ -558,3 +559,77 @@ def layer_bwd(p, inp, fwd, dy):
         dx += dzn @ np.asarray(inp["W_noise"], F64).T
     return dict(dx=dx, dWg=dWg, dW13=dW13, dW2=dW2, dWs13=dWs13, dWs2=dWs2, dW_noise=dW_noise,
                 dO=dO, dg=dg, dz=dz, dXp=dXp)
+
+
+# ---------------------------------------------------------------------------
+# Load balance from score histograms; router monitoring
+# ---------------------------------------------------------------------------
+def score_histogram(s, lo: float, hi: float, nbins: int):
+    """Per-expert histogram of the scores s [T,E] over nbins equal bins of
+    [lo, hi): bin = floor((s - lo) * (nbins / (hi - lo))) clamped to
+    [0, nbins-1], evaluated in fp32 (the precision the scores have); NaN
+    scores are not counted.  This is the fixed-size summary a multi-GPU job
+    sums over GPUs before solving the bias [Handbook news, Kimi K3]."""
+    s32 = np.asarray(s, np.float32)
+    T, E = s32.shape
+    scale = np.float32(nbins) / (np.float32(hi) - np.float32(lo))
+    with np.errstate(invalid="ignore"):
+        b = np.floor((s32 - np.float32(lo)) * scale)
+    ok = ~np.isnan(b)
+    b = np.clip(np.where(ok, b, 0), 0, nbins - 1).astype(np.int64)
+    hist = np.zeros((E, nbins), np.int64)
+    for e in range(E):
+        hist[e] = np.bincount(b[ok[:, e], e], minlength=nbins)
+    return hist
+
+
+def quantile_bias(hist, lo: float, hi: float, target: float):
+    """Quantile balancing [Handbook news, Kimi K3: the bias solved from score
+    histograms instead of fixed steps].  For each expert e, q_e is the score
+    above which `target` of its tokens lie, read off its histogram (bins walked
+    from the top, linear within the bin where the count is reached; lo if the
+    expert has fewer tokens in all).  The bias b_e = mean(q) - q_e puts every
+    expert's target-th largest biased score at the same level, so a threshold
+    on s + b would give each expert exactly `target` tokens."""
+    hist = np.asarray(hist, np.int64)
+    E, nb = hist.shape
+    w = (float(hi) - float(lo)) / nb
+    q = np.full(E, float(lo))
+    for e in range(E):
+        c = 0
+        for i in range(nb - 1, -1, -1):
+            h = int(hist[e, i])
+            if h > 0 and c + h >= target:
+                q[e] = float(lo) + (i + 1 - (target - c) / h) * w
+                break
+            c += h
+    return q.mean() - q
+
+
+def load_report(counts, n_dropped: int):
+    """Router monitoring [Handbook explainer, "router and load balancing": max
+    expert load, drop rate, spread of expert utilisation]: max/mean load, the
+    coefficient of variation of the per-expert counts (population std / mean),
+    the dropped fraction of the routed slots and the number of empty experts."""
+    c = np.asarray(counts, F64)
+    mean = c.mean()
+    return dict(max_over_mean=float(c.max() / mean), cv=float(c.std() / mean),
+                drop_rate=float(n_dropped) / float(c.sum()), n_empty=int(np.sum(c == 0)))
+
+
+def expert_output_norms(o, offsets):
+    """Mean L2 norm of each expert's output rows (0 for an empty expert) and
+    max/median over the non-empty experts [Handbook digest, the failure case
+    where a layer's largest expert output norm grew from ~14x to 5700x the
+    median]."""
+    o = np.asarray(o, F64)
+    offsets = np.asarray(offsets, np.int64)
+    E = offsets.size - 1
+    n = np.zeros(E)
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            n[e] = np.mean(np.sqrt(np.sum(o[r0:r1] ** 2, axis=1)))
+    ne = n[np.diff(offsets) > 0]
+    ratio = float(ne.max() / np.median(ne)) if ne.size else 0.0
+    return n, ratio

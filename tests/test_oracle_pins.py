@@ -614,3 +614,86 @@ def test_hash_routing_fixed_per_id_distinct_balanced():
     assert ((r["idx"][:, 1:] - r["idx"][:, :-1]) % p.E == 1).all()
     c = r["counts"] / r["counts"].sum()
     assert np.max(np.abs(c - 1 / p.E)) < 0.02
+
+
+# ---------------------------------------------------------------------------
+# quantile balancing from score histograms; router monitoring
+# ---------------------------------------------------------------------------
+def test_score_histogram_matches_numpy_away_from_edges():
+    rng = np.random.default_rng(40)
+    nb, lo, hi = 64, 0.0, 1.0
+    centres = (rng.integers(0, nb, size=(500, 7)) + 0.5) / nb
+    s = centres + rng.uniform(-0.3, 0.3, size=centres.shape) / nb
+    h = orc.score_histogram(s, lo, hi, nb)
+    for e in range(7):
+        ref, _ = np.histogram(s[:, e], bins=nb, range=(lo, hi))
+        np.testing.assert_array_equal(h[e], ref)
+    s[0, 0], s[1, 0], s[2, 0] = -5.0, 7.0, np.nan          # clamped, clamped, skipped
+    h2 = orc.score_histogram(s, lo, hi, nb)
+    assert h2[0, 0] >= 1 and h2[0, -1] >= 1 and h2[0].sum() == 499
+
+
+def test_quantile_bias_closed_form_grid():
+    """One token per bin: expert e's L-th largest score is exactly lo + (nb - L) w."""
+    nb, E, L = 100, 3, 17
+    s = np.repeat(((np.arange(nb) + 0.5) / nb)[:, None], E, axis=1)
+    s[:, 1] = s[:, 1] * 0.5          # expert 1: bins 0..49 with two tokens in each of half of them
+    h = orc.score_histogram(s, 0.0, 1.0, nb)
+    b = orc.quantile_bias(h, 0.0, 1.0, L)
+    q0 = (nb - L) / nb
+    # expert 1: scores (i + 0.5) / 200 -> bin floor((i+0.5)/2): two tokens per bin 0..49
+    c, q1 = 0, None
+    for i in range(nb - 1, -1, -1):
+        hh = h[1, i]
+        if hh and c + hh >= L:
+            q1 = (i + 1 - (L - c) / hh) / nb
+            break
+        c += hh
+    q = np.array([q0, q1, q0])
+    np.testing.assert_allclose(b, q.mean() - q, rtol=0, atol=1e-12)
+    assert abs(q1 - (50 - 8.5) / nb) < 1e-12          # 8 full bins (16 tokens) + half a bin
+
+
+def test_quantile_bias_undoes_a_shift_and_balances():
+    rng = np.random.default_rng(41)
+    T, E, nb, k = 4000, 6, 400, 2
+    base = rng.uniform(0.1, 0.6, size=T)
+    shift = np.array([0.0, 0.05, 0.1, 0.15, 0.2, 0.25])          # multiples of the bin width 1/400
+    s = base[:, None] + shift[None, :]
+    L = T * k / E
+    b = orc.quantile_bias(orc.score_histogram(s, 0.0, 1.0, nb), 0.0, 1.0, L)
+    np.testing.assert_allclose(b - b[0], -shift, atol=1e-12)
+    # balance: with the bias, a common threshold gives every expert L tokens
+    # (to within one bin's tokens)
+    s2 = s + b[None, :]
+    tau = np.sort(s2[:, 0])[::-1][int(L) - 1]
+    counts = (s2 >= tau - 1e-12).sum(axis=0)
+    assert np.all(np.abs(counts - L) <= np.max(orc.score_histogram(s, 0.0, 1.0, nb)))
+    # q_e = mean(q) - b_e lies within a bin width of the exact empirical
+    # quantile, so mean(exact) - b_e lies within two
+    exact = np.sort(s, axis=0)[::-1][int(L) - 1]
+    assert np.all(np.abs(exact.mean() - b - exact) <= 2.0 / nb + 1e-12)
+
+
+def test_load_report_closed_forms():
+    E, T, k = 8, 64, 2
+    r = orc.load_report(np.full(E, T * k // E), 0)
+    assert r == dict(max_over_mean=1.0, cv=0.0, drop_rate=0.0, n_empty=0)
+    c = np.zeros(E, np.int64)
+    c[3] = T * k
+    r = orc.load_report(c, 100)
+    assert r["max_over_mean"] == E and abs(r["cv"] - math.sqrt(E - 1)) < 1e-12
+    assert r["drop_rate"] == 100 / (T * k) and r["n_empty"] == E - 1
+
+
+def test_expert_output_norms_bruteforce():
+    rng = np.random.default_rng(42)
+    offsets = np.array([0, 3, 3, 10, 11])
+    o = rng.normal(size=(11, 5))
+    n, ratio = orc.expert_output_norms(o, offsets)
+    want = [np.mean([np.linalg.norm(o[r]) for r in range(a, b)]) if b > a else 0.0
+            for a, b in zip(offsets[:-1], offsets[1:])]
+    np.testing.assert_allclose(n, want, rtol=1e-14)
+    import statistics
+    ne = [want[0], want[2], want[3]]
+    assert abs(ratio - max(ne) / statistics.median(ne)) < 1e-14
