@@ -250,6 +250,36 @@ int moe_layer_bwd(const moe_dims* dims, const moe_opts* opts, const moe_weights*
 int moe_bias_update(const int32_t* counts, float* bias, int64_t E, float target, float gamma,
                     void* stream);
 
+/* Quantile balancing, step 1 (Ultimate MoE Training Handbook news, Kimi K3: the
+ * selection bias solved from score histograms summed over GPUs instead of fixed
+ * steps).  scores [T, E] fp32 (moe_route's scores output); hist [E, nbins] int32,
+ * overwritten: hist[e][b] = tokens t with bin(scores[t,e]) = b, bin =
+ * floor((s - lo) * (nbins / (hi - lo))) in fp32 clamped to [0, nbins-1]; NaN
+ * scores are not counted.  Requires E <= 256, 1 <= nbins <= 65536, lo < hi. */
+int moe_score_histogram(const float* scores, int64_t T, int64_t E, float lo, float hi,
+                        int32_t nbins, int32_t* hist, void* stream);
+
+/* Quantile balancing, step 2: bias[e] = mean(q) - q[e], where q[e] is the score
+ * above which `target` (normally T*k/E) tokens of expert e lie, read from its
+ * histogram (bins walked from the top, linear within the bin reaching the
+ * count; lo when the expert has fewer tokens).  The result is a selection-only
+ * bias (moe_weights.sel_bias) that puts every expert's target-th largest biased
+ * score at the same level. */
+int moe_bias_from_histogram(const int32_t* hist, int64_t E, int32_t nbins, float lo, float hi,
+                            float target, float* bias, void* stream);
+
+/* Router monitoring (handbook explainer, "router and load balancing": max expert
+ * load, drop rate, spread of expert utilisation; handbook digest: a layer's
+ * largest expert output norm against the median).  counts [E] (pre-capacity),
+ * n_dropped [1] nullable; out_perm [R, d] fp32 and offsets [E+1] (nullable
+ * together) give expert_norm [E] (required with them) = mean L2 norm of each
+ * expert's output rows.  report [5] fp32 on the device: max/mean load,
+ * population std/mean of the loads, dropped/routed slots, max/median expert
+ * norm over the non-empty experts (0 without out_perm), empty experts. */
+int moe_router_report(int64_t E, int64_t d, const int32_t* counts, const int32_t* n_dropped,
+                      const float* out_perm, const int32_t* offsets, float* expert_norm,
+                      float* report, void* stream);
+
 /* Static text for a moe_status value. */
 const char* moe_strerror(int status);
 

@@ -111,3 +111,21 @@ def test_zero_tokens_is_a_noop(L):
     assert B.lib().moe_route(C.byref(d), C.byref(o), ok, ok, None, None, ok, ok, None, None, None,
                              None, None, ok, 1 << 40, None) == B.MOE_OK
     assert B.lib().moe_combine(C.byref(d), ok, ok, ok, None, ok, None) == B.MOE_OK
+
+
+def test_balance_entry_points_reject_bad_arguments(L):
+    ok = C.c_void_p(256)
+    h = B.lib().moe_score_histogram
+    assert h(ok, 10, 4, 0.0, 1.0, 16, None, None) == B.MOE_ERR_INVALID_ARG     # no output
+    assert h(ok, 10, 4, 1.0, 1.0, 16, ok, None) == B.MOE_ERR_INVALID_ARG       # lo == hi
+    assert h(ok, 10, 4, 0.0, float("nan"), 16, ok, None) == B.MOE_ERR_INVALID_ARG
+    assert h(ok, 10, 300, 0.0, 1.0, 16, ok, None) == B.MOE_ERR_UNSUPPORTED      # E > 256
+    assert h(ok, 10, 4, 0.0, 1.0, 0, ok, None) == B.MOE_ERR_INVALID_ARG        # no bins
+    s = B.lib().moe_bias_from_histogram
+    assert s(ok, 4, 16, 0.0, 1.0, float("nan"), ok, None) == B.MOE_ERR_INVALID_ARG
+    assert s(ok, 4, 16, 0.0, 1.0, -1.0, ok, None) == B.MOE_ERR_INVALID_ARG
+    assert s(None, 4, 16, 0.0, 1.0, 3.0, ok, None) == B.MOE_ERR_INVALID_ARG
+    r = B.lib().moe_router_report
+    assert r(4, 8, ok, None, ok, None, ok, ok, None) == B.MOE_ERR_INVALID_ARG  # out_perm w/o offsets
+    assert r(4, 8, None, None, None, None, None, ok, None) == B.MOE_ERR_INVALID_ARG
+    assert r(300, 8, ok, None, None, None, None, ok, None) == B.MOE_ERR_UNSUPPORTED

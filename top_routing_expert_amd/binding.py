@@ -71,7 +71,8 @@ class Stats(C.Structure):
 
 ABI_FUNCTIONS = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute",
                  "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd",
-                 "moe_bias_update", "moe_strerror")
+                 "moe_bias_update", "moe_score_histogram", "moe_bias_from_histogram",
+                 "moe_router_report", "moe_strerror")
 
 _lib: Optional[C.CDLL] = None
 
@@ -98,6 +99,9 @@ def lib() -> C.CDLL:
     L.moe_layer_bwd.argtypes = [D, O, P(Weights), P(RouterInputs), VP, P(Saved), VP, VP, P(Grads),
                                 VP, C.c_size_t, VP]
     L.moe_bias_update.argtypes = [VP, VP, I64, F32, F32, VP]
+    L.moe_score_histogram.argtypes = [VP, I64, I64, F32, F32, C.c_int32, VP, VP]
+    L.moe_bias_from_histogram.argtypes = [VP, I64, C.c_int32, F32, F32, F32, VP, VP]
+    L.moe_router_report.argtypes = [I64, I64, VP, VP, VP, VP, VP, VP, VP]
     L.moe_strerror.argtypes = [C.c_int]
     L.moe_strerror.restype = C.c_char_p
     for f in ABI_FUNCTIONS[:-1]:
@@ -411,3 +415,35 @@ class Layer:
             C.byref(self._saved_c), C.c_void_p(dy.data_ptr()), C.c_void_p(self.dx.data_ptr()),
             C.byref(self._grads_c), C.c_void_p(self.ws.data_ptr()), self.ws_bytes, _stream()))
         return dict(self.grads, dx=self.dx)
+
+
+# --------------------------------------------------------------------------- balance / monitoring
+def score_histogram(scores, lo: float, hi: float, nbins: int):
+    """moe_score_histogram: hist [E, nbins] int32 of the scores [T, E]."""
+    T, E = scores.shape
+    _need(scores, "scores", (T, E), torch.float32, scores.device)
+    hist = torch.empty(E, nbins, dtype=torch.int32, device=scores.device)
+    _check("moe_score_histogram", lib().moe_score_histogram(
+        _ptr(scores), T, E, lo, hi, nbins, _ptr(hist), _stream()))
+    return hist
+
+
+def bias_from_histogram(hist, lo: float, hi: float, target: float):
+    """moe_bias_from_histogram: the quantile-balancing selection bias [E]."""
+    E, nbins = hist.shape
+    bias = torch.empty(E, dtype=torch.float32, device=hist.device)
+    _check("moe_bias_from_histogram", lib().moe_bias_from_histogram(
+        _ptr(hist), E, nbins, lo, hi, target, _ptr(bias), _stream()))
+    return bias
+
+
+def router_report(counts, n_dropped=None, out_perm=None, offsets=None, d: int = 0):
+    """moe_router_report: dict(report [5] f32, expert_norm [E] or None)."""
+    E = counts.numel()
+    dev = counts.device
+    norm = torch.empty(E, dtype=torch.float32, device=dev) if out_perm is not None else None
+    rep = torch.empty(5, dtype=torch.float32, device=dev)
+    _check("moe_router_report", lib().moe_router_report(
+        E, d if out_perm is None else out_perm.shape[1], _ptr(counts), _ptr(n_dropped),
+        _ptr(out_perm), _ptr(offsets), _ptr(norm), _ptr(rep), _stream()))
+    return dict(report=rep, expert_norm=norm)

@@ -638,6 +638,36 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   return MOE_OK;
 }
 
+int moe_score_histogram(const float* scores, int64_t T, int64_t E, float lo, float hi,
+                        int32_t nbins, int32_t* hist, void* stream) {
+  if (!hist || T < 0 || E < 1 || nbins < 1 || !isfinite(lo) || !isfinite(hi) || !(lo < hi))
+    return MOE_ERR_INVALID_ARG;
+  if (T > 0 && !scores) return MOE_ERR_INVALID_ARG;
+  if (E > 256 || nbins > 65536 || T * E >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_score_hist(scores, T, int(E), lo, hi, nbins, hist,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int moe_bias_from_histogram(const int32_t* hist, int64_t E, int32_t nbins, float lo, float hi,
+                            float target, float* bias, void* stream) {
+  if (!hist || !bias || E < 1 || nbins < 1 || !isfinite(lo) || !isfinite(hi) || !(lo < hi) ||
+      !isfinite(target) || target < 0.0f)
+    return MOE_ERR_INVALID_ARG;
+  if (E > 256 || nbins > 65536) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_bias_solve(hist, int(E), nbins, lo, hi, target, bias,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int moe_router_report(int64_t E, int64_t d, const int32_t* counts, const int32_t* n_dropped,
+                      const float* out_perm, const int32_t* offsets, float* expert_norm,
+                      float* report, void* stream) {
+  if (!counts || !report || E < 1 || (out_perm && (!offsets || !expert_norm || d < 1)))
+    return MOE_ERR_INVALID_ARG;
+  if (E > 256 || d >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_router_report(int(E), int(d), counts, n_dropped, out_perm, offsets,
+                                         expert_norm, report, static_cast<hipStream_t>(stream)));
+}
+
 int moe_bias_update(const int32_t* counts, float* bias, int64_t E, float target, float gamma,
                     void* stream) {
   if (!counts || !bias || E < 1 || E > (int64_t(1) << 30) || !isfinite(target) || !isfinite(gamma))

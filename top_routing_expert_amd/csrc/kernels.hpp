@@ -121,4 +121,13 @@ hipError_t launch_sum_partials(const float* P, int nz, int64_t n, float* out, hi
 hipError_t launch_unpermute_sum(const float* dxp, const int32_t* ros, const float* e1,
                                 const float* e2, int T, int k, int d, float* dx, hipStream_t st);
 
+// ------------------------------------------------------------------ balance / monitoring
+hipError_t launch_score_hist(const float* s, int64_t T, int E, float lo, float hi, int nbins,
+                             int32_t* hist, hipStream_t st);
+hipError_t launch_bias_solve(const int32_t* hist, int E, int nbins, float lo, float hi, float target,
+                             float* bias, hipStream_t st);
+hipError_t launch_router_report(int E, int d, const int32_t* counts, const int32_t* n_dropped,
+                                const float* o, const int32_t* offsets, float* norm, float* report,
+                                hipStream_t st);
+
 }  // namespace moe
