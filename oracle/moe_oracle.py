@@ -64,6 +64,8 @@ __all__ = [
     "expert_ffn", "shared_expert", "combine", "bias_update", "layer_fwd", "layer_bwd",
     "router_bwd", "expert_bwd", "uniform_assignment", "hash_assignment", "fmix32", "softplus",
     "score_histogram", "quantile_bias", "load_report", "expert_output_norms",
+    "e2m1_decode", "e4m3_decode", "e2m1_encode", "e4m3_encode", "mx_quantize", "mx_dequantize",
+    "expert_ffn_mx",
     "NEAR_TIE_REL",
 ]
 
@@ -633,3 +635,124 @@ def expert_output_norms(o, offsets):
     ne = n[np.diff(offsets) > 0]
     ratio = float(ne.max() / np.median(ne)) if ne.size else 0.0
     return n, ratio
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 routed experts for inference [Handbook news: Kimi K3 quantises its
+# routed experts to MXFP4].  Element and scale formats are those of the OCP
+# Microscaling (MX) specification: FP4 E2M1 (1 sign, 2 exponent bits with bias
+# 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), FP8 E4M3 (bias 7,
+# 3 mantissa bits, largest 448, code S.1111.111 is NaN) and the E8M0 shared
+# scale 2^(code - 127).  A block's shared exponent is floor(log2(max|v|)) minus
+# the element type's largest exponent (2 for E2M1, 8 for E4M3); elements are
+# v / 2^X rounded to nearest, ties to even, saturating at the largest
+# magnitude.  Weights: FP4 with one scale per 32 consecutive k.  Activations:
+# FP8 with one scale per 64 consecutive k (the pairing of the CDNA4 FP8 x FP4
+# matrix instruction gives each activation lane halves of two 32-blocks).
+# ---------------------------------------------------------------------------
+def e2m1_decode(c):
+    c = np.asarray(c, np.int64)
+    e, m = (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(c & 8, -mag, mag)
+
+
+def e4m3_decode(c):
+    c = np.asarray(c, np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def _encode(v, mbits: int, emin: int, maxmag: float, bias: int):
+    """Round |v| to the nearest value of a sign-magnitude float grid with mbits
+    mantissa bits, smallest normal exponent emin (subnormals below), ties to
+    even, saturating at maxmag; returns codes with the sign at bit
+    1 + exponent bits + mbits."""
+    v = np.asarray(v, F64)
+    a = np.minimum(np.abs(v), maxmag)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, emin)
+    q = np.rint(a / np.ldexp(1.0, (e - mbits).astype(np.int64)))      # units of the grid step
+    # q in [0, 2^(mbits+1)]: q = 2^(mbits+1) moves to the next binade
+    normal = a >= np.ldexp(1.0, emin)
+    m = np.where(q >= 2 ** (mbits + 1), 0, q - np.where(normal, 2 ** mbits, 0))
+    ebits = np.where(q >= 2 ** (mbits + 1), e + 1 + bias,
+                     np.where(normal, e + bias, np.where(q >= 2 ** mbits, 1, 0)))
+    m = np.where(~normal & (q >= 2 ** mbits), q - 2 ** mbits, m)
+    code = (ebits.astype(np.int64) << mbits) | m.astype(np.int64)
+    sign = np.signbit(v).astype(np.int64) << (mbits + (4 if mbits == 3 else 2))
+    return code | sign
+
+
+def e2m1_encode(v):
+    return _encode(v, 1, 0, 6.0, 1)
+
+
+def e4m3_encode(v):
+    return _encode(v, 3, -6, 448.0, 7)
+
+
+def mx_quantize(w, block: int, fmt: str):
+    """Quantise the rows of w [rows, K] in blocks of `block` consecutive k.
+    Returns codes [rows, K] (int, one per element) and scale codes
+    [rows, K/block] (E8M0)."""
+    w = np.asarray(w, F64)
+    rows, K = w.shape
+    emax = {"e2m1": 2, "e4m3": 8}[fmt]
+    blk = w.reshape(rows, K // block, block)
+    amax = np.max(np.abs(blk), axis=2)
+    _, ex = np.frexp(amax)                        # amax = f * 2^ex, f in [0.5, 1)
+    X = np.where(amax > 0, ex - 1 - emax, -127)
+    scode = np.clip(X + 127, 0, 254).astype(np.int64)
+    scaled = blk / np.ldexp(1.0, (scode - 127))[:, :, None]
+    enc = e2m1_encode if fmt == "e2m1" else e4m3_encode
+    return enc(scaled).reshape(rows, K), scode
+
+
+def mx_dequantize(codes, scodes, block: int, fmt: str):
+    dec = e2m1_decode if fmt == "e2m1" else e4m3_decode
+    v = dec(codes)
+    rows, K = v.shape
+    return (v.reshape(rows, K // block, block) *
+            np.ldexp(1.0, np.asarray(scodes, np.int64) - 127)[:, :, None]).reshape(rows, K)
+
+
+def expert_ffn_mx(xq, xs, offsets, W13q, W13s, W2q, W2s, act: str, aq=None, as_=None):
+    """Grouped expert FFN with FP8 activations (64-blocks) and MXFP4 weights
+    (32-blocks): h = deq(x) deq(W13)^T, a = act(h), a quantised to FP8
+    (64-blocks), o = deq(a) deq(W2)^T.  With aq/as_ given (the GPU's quantised
+    activation), the down projection uses them (a step-wise check).  Returns
+    o [R,d], a (float64, before quantisation), aq, as."""
+    x = mx_dequantize(xq, xs, 64, "e4m3")
+    R = x.shape[0]
+    E = len(offsets) - 1
+    F = W2q.shape[2] if W2q.ndim == 3 else None
+    outs, acts = np.zeros((R, W2q.shape[1])), None
+    a_full = None
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        W13 = mx_dequantize(W13q[e], W13s[e], 32, "e2m1")
+        h = x[r0:r1] @ W13.T
+        if act == "swiglu":
+            Fh = W13.shape[0] // 2
+            a = silu(h[:, :Fh]) * h[:, Fh:]
+        else:
+            a = gelu(h)
+        if a_full is None:
+            a_full = np.zeros((R, a.shape[1]))
+        a_full[r0:r1] = a
+    if aq is None:
+        aq, as_ = mx_quantize(a_full, 64, "e4m3")
+    ad = mx_dequantize(aq, as_, 64, "e4m3")
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        W2 = mx_dequantize(W2q[e], W2s[e], 32, "e2m1")
+        outs[r0:r1] = ad[r0:r1] @ W2.T
+    return outs, a_full, aq, as_

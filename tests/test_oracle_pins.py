@@ -697,3 +697,96 @@ def test_expert_output_norms_bruteforce():
     import statistics
     ne = [want[0], want[2], want[3]]
     assert abs(ratio - max(ne) / statistics.median(ne)) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# MX formats (OCP Microscaling): FP4 E2M1, FP8 E4M3, E8M0 block scales
+# ---------------------------------------------------------------------------
+def test_mx_element_tables():
+    np.testing.assert_array_equal(orc.e2m1_decode(np.arange(8)), [0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    np.testing.assert_array_equal(orc.e2m1_decode(np.arange(8, 16)), -orc.e2m1_decode(np.arange(8)))
+    d = orc.e4m3_decode(np.array([0x01, 0x07, 0x08, 0x38, 0x3F, 0x7E, 0x7F, 0xFE]))
+    np.testing.assert_array_equal(d[[0, 1, 2, 3, 4, 5, 7]],
+                                  [2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.875, 448.0, -448.0])
+    assert np.isnan(d[6])
+
+
+def _nearest_even(v, table_codes, dec):
+    """Brute force: the representable value nearest to v (ties to the even
+    code, i.e. mantissa bit 0), saturating at the largest magnitude."""
+    vals = dec(table_codes)
+    out = []
+    for x in np.atleast_1d(v):
+        dist = np.abs(vals - x)
+        best = np.nonzero(dist == dist.min())[0]
+        cand = table_codes[best]
+        pick = cand[(cand & 1) == 0] if np.any((cand & 1) == 0) else cand
+        out.append(int(pick[0]))
+    return np.array(out)
+
+
+def test_e2m1_e4m3_round_to_nearest_even_bruteforce():
+    rng = np.random.default_rng(50)
+    pos4 = np.arange(8)                                         # non-negative E2M1 codes
+    mids = (orc.e2m1_decode(pos4[:-1]) + orc.e2m1_decode(pos4[1:])) / 2
+    v = np.concatenate([mids, rng.uniform(0, 7.5, 400), [0.0, 6.0, 9.0, 1e9]])
+    np.testing.assert_array_equal(orc.e2m1_encode(v), _nearest_even(v, pos4, orc.e2m1_decode))
+    np.testing.assert_array_equal(orc.e2m1_encode(-v) & 7, orc.e2m1_encode(v))
+    assert (orc.e2m1_encode(-v[v > 0]) & 8 == 8).all()
+    pos8 = np.arange(0x7F)                                      # finite non-negative E4M3 codes
+    vals = orc.e4m3_decode(pos8)
+    mids8 = (vals[:-1] + vals[1:]) / 2
+    v8 = np.concatenate([mids8, rng.uniform(0, 500, 400), np.exp(rng.uniform(-12, 6, 300)), [448.0, 1e6]])
+    np.testing.assert_array_equal(orc.e4m3_encode(v8), _nearest_even(v8, pos8, orc.e4m3_decode))
+
+
+@pytest.mark.parametrize("fmt,block,emax,top", [("e2m1", 32, 2, 6.0), ("e4m3", 64, 8, 448.0)])
+def test_mx_block_scale_rule(fmt, block, emax, top):
+    """The shared scale puts the block's largest magnitude in [2^emax, 2^(emax+1))
+    after scaling; every element is the nearest grid value (saturating)."""
+    rng = np.random.default_rng(51)
+    w = rng.normal(size=(6, 4 * block)) * np.exp(rng.uniform(-8, 8, size=(6, 1)))
+    w[0, :block] = 0.0                                          # an all-zero block
+    codes, sc = orc.mx_quantize(w, block, fmt)
+    dec = orc.e2m1_decode if fmt == "e2m1" else orc.e4m3_decode
+    scale = np.ldexp(1.0, sc - 127)
+    amax = np.abs(w.reshape(6, -1, block)).max(axis=2)
+    ratio = amax[amax > 0] / scale[amax > 0]
+    assert np.all((ratio >= 2.0 ** emax) & (ratio < 2.0 ** (emax + 1)))
+    assert np.all(codes[0, :block] % (8 if fmt == "e2m1" else 128) == 0)
+    table = np.arange(8) if fmt == "e2m1" else np.arange(0x7F)
+    scaled = (w.reshape(6, -1, block) / scale[:, :, None]).reshape(6, -1)
+    want = _nearest_even(np.abs(scaled[1:4].ravel()), table, dec)
+    got = codes[1:4].ravel() & (7 if fmt == "e2m1" else 0x7F)
+    np.testing.assert_array_equal(got, want)
+    deq = orc.mx_dequantize(codes, sc, block, fmt)
+    assert np.all(np.abs(deq) <= top * scale.repeat(block, axis=1) + 0)
+
+
+def test_expert_ffn_mx_composition():
+    """h, a and o of the MX expert FFN against torch on the dequantised values."""
+    rng = np.random.default_rng(52)
+    d, F, E = 64, 64, 3
+    offsets = np.array([0, 5, 5, 12])
+    x = rng.normal(size=(12, d))
+    W13 = rng.normal(size=(E, 2 * F, d)) * 0.2
+    W2 = rng.normal(size=(E, d, F)) * 0.2
+    xq, xs = orc.mx_quantize(x, 64, "e4m3")
+    W13q = np.stack([orc.mx_quantize(W13[e], 32, "e2m1")[0] for e in range(E)])
+    W13s = np.stack([orc.mx_quantize(W13[e], 32, "e2m1")[1] for e in range(E)])
+    W2q = np.stack([orc.mx_quantize(W2[e], 32, "e2m1")[0] for e in range(E)])
+    W2s = np.stack([orc.mx_quantize(W2[e], 32, "e2m1")[1] for e in range(E)])
+    o, a, aq, as_ = orc.expert_ffn_mx(xq, xs, offsets, W13q, W13s, W2q, W2s, "swiglu")
+    xd = torch.from_numpy(orc.mx_dequantize(xq, xs, 64, "e4m3"))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        W13d = torch.from_numpy(orc.mx_dequantize(W13q[e], W13s[e], 32, "e2m1"))
+        W2d = torch.from_numpy(orc.mx_dequantize(W2q[e], W2s[e], 32, "e2m1"))
+        h = xd[r0:r1] @ W13d.T
+        ar = TF.silu(h[:, :F]) * h[:, F:]
+        np.testing.assert_allclose(a[r0:r1], ar.numpy(), rtol=1e-12, atol=1e-12)
+        aqe, ase = orc.mx_quantize(ar.numpy(), 64, "e4m3")
+        ad = torch.from_numpy(orc.mx_dequantize(aqe, ase, 64, "e4m3"))
+        np.testing.assert_allclose(o[r0:r1], (ad @ W2d.T).numpy(), rtol=1e-12, atol=1e-12)
