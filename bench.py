@@ -175,6 +175,22 @@ def main():
         "combine": dict(us=t_comb * 1e6, GBps=perf.combine_bytes(p, R) / t_comb / 1e9,
                         hbm_frac=perf.combine_bytes(p, R) / t_comb / 1e9 / perf.PEAK_HBM_GBS),
     }
+    if p.dtype == "bf16" and p.d % 256 == 0 and p.F % 256 == 0:
+        # the same routed experts with MXFP4 weights and FP8 activations
+        # (weights quantised once, outside the timed region, as a serving
+        # deployment stores them)
+        W13q, W13s = B.mx_quantize_weights(p, w.W13)
+        W2q, W2s = B.mx_quantize_weights(p, w.W2)
+        xs_stride = B.mx_stride(p.T * p.k)
+        xq, xs = B.mx_quantize_act(p, pm["x_perm"], stride=xs_stride)
+        t_q = timed(lambda: B.mx_quantize_act(p, pm["x_perm"], stride=xs_stride), it)
+        t_mx = timed(lambda: B.expert_ffn_mx(p, xq, xs, pm["offsets"], W13q, W13s, W2q, W2s,
+                                             max_rows=p.T * p.k), it)
+        bmx = perf.ffn_mx_bytes(p, R, active)
+        stages["expert_ffn_mx"] = dict(us=t_mx * 1e6, TFLOPs=fl / t_mx / 1e12,
+                                       mfma_frac=fl / t_mx / 1e12 / perf.PEAK_FP8_TFLOPS,
+                                       GBps=bmx / t_mx / 1e9, quant_x_us=t_q * 1e6,
+                                       vs_bf16=t_ffn / t_mx)
     for k_, v in stages.items():
         log(f"[bench] {k_:10s} " + " ".join(f"{a}={b:.4g}" for a, b in v.items()))
 

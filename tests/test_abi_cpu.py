@@ -129,3 +129,24 @@ def test_balance_entry_points_reject_bad_arguments(L):
     assert r(4, 8, ok, None, ok, None, ok, ok, None) == B.MOE_ERR_INVALID_ARG  # out_perm w/o offsets
     assert r(4, 8, None, None, None, None, None, ok, None) == B.MOE_ERR_INVALID_ARG
     assert r(300, 8, ok, None, None, None, None, ok, None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_mx_entry_points_reject_bad_arguments(L):
+    p = presets.get("c4")
+    o = B.opts_of(p)
+    ok, bad = C.c_void_p(256), C.c_void_p(264)
+    qw = B.lib().moe_mx_quantize_weights
+    assert qw(C.byref(o), ok, 2, 256, 96, ok, ok, None) == B.MOE_ERR_INVALID_ARG     # K % 64
+    assert qw(C.byref(o), bad, 2, 256, 512, ok, ok, None) == B.MOE_ERR_INVALID_ARG   # misaligned w
+    assert qw(C.byref(o), ok, 2, 256, 512, bad, ok, None) == B.MOE_ERR_INVALID_ARG   # misaligned codes
+    qa = B.lib().moe_mx_quantize_act
+    assert qa(C.byref(o), ok, 10, 512, 8, ok, ok, None) == B.MOE_ERR_INVALID_ARG     # stride < rows
+    assert qa(C.byref(o), bad, 10, 512, 16, ok, ok, None) == B.MOE_ERR_INVALID_ARG   # misaligned x
+    assert qa(C.byref(o), ok, 0, 512, 0, None, None, None) == B.MOE_OK              # no rows
+    d = B.dims_of(p)
+    f = B.lib().moe_expert_ffn_mx
+    args = lambda xs_stride, a_stride, F: (C.byref(d), C.byref(o), p.E, 1000, F, ok, ok, xs_stride, ok,
+                                           ok, ok, ok, ok, ok, ok, a_stride, ok, None)
+    assert f(*args(1000, 1004, p.F)) == B.MOE_ERR_INVALID_ARG    # x_stride < max_rows + 4
+    assert f(*args(1006, 1008, p.F)) == B.MOE_ERR_INVALID_ARG    # x_stride % 4
+    assert f(*args(1004, 1004, 320)) == B.MOE_ERR_UNSUPPORTED    # F % 256

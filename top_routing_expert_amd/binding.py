@@ -72,7 +72,8 @@ class Stats(C.Structure):
 ABI_FUNCTIONS = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute",
                  "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd",
                  "moe_bias_update", "moe_score_histogram", "moe_bias_from_histogram",
-                 "moe_router_report", "moe_strerror")
+                 "moe_router_report", "moe_mx_quantize_weights", "moe_mx_quantize_act",
+                 "moe_expert_ffn_mx", "moe_strerror")
 
 _lib: Optional[C.CDLL] = None
 
@@ -102,6 +103,10 @@ def lib() -> C.CDLL:
     L.moe_score_histogram.argtypes = [VP, I64, I64, F32, F32, C.c_int32, VP, VP]
     L.moe_bias_from_histogram.argtypes = [VP, I64, C.c_int32, F32, F32, F32, VP, VP]
     L.moe_router_report.argtypes = [I64, I64, VP, VP, VP, VP, VP, VP, VP]
+    L.moe_mx_quantize_weights.argtypes = [O, VP, I64, I64, I64, VP, VP, VP]
+    L.moe_mx_quantize_act.argtypes = [O, VP, I64, I64, I64, VP, VP, VP]
+    L.moe_expert_ffn_mx.argtypes = [D, O, I64, I64, I64, VP, VP, I64, VP, VP, VP, VP, VP, VP, VP,
+                                    I64, VP, VP]
     L.moe_strerror.argtypes = [C.c_int]
     L.moe_strerror.restype = C.c_char_p
     for f in ABI_FUNCTIONS[:-1]:
@@ -447,3 +452,51 @@ def router_report(counts, n_dropped=None, out_perm=None, offsets=None, d: int = 
         E, d if out_perm is None else out_perm.shape[1], _ptr(counts), _ptr(n_dropped),
         _ptr(out_perm), _ptr(offsets), _ptr(norm), _ptr(rep), _stream()))
     return dict(report=rep, expert_norm=norm)
+
+
+# --------------------------------------------------------------------------- MXFP4 experts
+def mx_quantize_weights(p: Preset, w):
+    """moe_mx_quantize_weights: w [G, N, K] -> codes [G, N, K/2] u8, scales [G, K/32, N] u8."""
+    G, N, K = w.shape
+    _need(w, "w", (G, N, K), TORCH_DTYPE[p.dtype], w.device)
+    codes = torch.empty(G, N, K // 2, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(G, K // 32, N, dtype=torch.uint8, device=w.device)
+    _check("moe_mx_quantize_weights", lib().moe_mx_quantize_weights(
+        C.byref(opts_of(p)), _ptr(w), G, N, K, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def mx_stride(rows: int) -> int:
+    """Row stride of an activation scale array usable by moe_expert_ffn_mx."""
+    return (rows + 4 + 3) // 4 * 4
+
+
+def mx_quantize_act(p: Preset, x, stride: Optional[int] = None):
+    """moe_mx_quantize_act: x [rows, K] -> FP8 codes [rows, K] u8, scales [K/64, stride] u8."""
+    rows, K = x.shape
+    stride = rows if stride is None else stride
+    _need(x, "x", (rows, K), TORCH_DTYPE[p.dtype], x.device)
+    codes = torch.empty(max(rows, 1), K, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(K // 64, max(stride, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_mx_quantize_act", lib().moe_mx_quantize_act(
+        C.byref(opts_of(p)), _ptr(x), rows, K, stride, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def expert_ffn_mx(p: Preset, xq, xs, offsets, W13q, W13s, W2q, W2s, *, max_rows: int,
+                  F: Optional[int] = None, act: Optional[str] = None):
+    """moe_expert_ffn_mx: returns dict(out [rows, d] f32, aq [rows, F] u8, aqs [F/64, rows] u8)."""
+    dev = xq.device
+    G = offsets.numel() - 1
+    F = p.F if F is None else F
+    q = p.with_(act=p.act if act is None else act, F=F)
+    rows = max(max_rows, 1)
+    a_stride = mx_stride(rows)
+    out = torch.empty(rows, p.d, dtype=torch.float32, device=dev)
+    aq = torch.empty(rows, F, dtype=torch.uint8, device=dev)
+    aqs = torch.empty(F // 64, a_stride, dtype=torch.uint8, device=dev)
+    _check("moe_expert_ffn_mx", lib().moe_expert_ffn_mx(
+        C.byref(dims_of(q)), C.byref(opts_of(q)), G, max_rows, F, _ptr(xq), _ptr(xs), xs.shape[1],
+        _ptr(offsets), _ptr(W13q), _ptr(W13s), _ptr(W2q), _ptr(W2s), _ptr(aq), _ptr(aqs), a_stride,
+        _ptr(out), _stream()))
+    return dict(out=out, aq=aq, aqs=aqs)

@@ -638,6 +638,49 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   return MOE_OK;
 }
 
+int moe_mx_quantize_weights(const moe_opts* o, const void* w, int64_t G, int64_t N, int64_t K,
+                            uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!o || !w || !codes || !scales || G < 1 || N < 1 || K < 64 || K % 64) return MOE_ERR_INVALID_ARG;
+  if (o->dtype != MOE_DTYPE_F32 && o->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  if (K >= (int64_t(1) << 31) || G * N * K >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_mx_quantize_weights(w, o->dtype == MOE_DTYPE_BF16, G * N, int(K), int(N),
+                                               codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+int moe_mx_quantize_act(const moe_opts* o, const void* x, int64_t rows, int64_t K, int64_t stride,
+                        uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!o || rows < 0 || K < 64 || K % 64 || stride < rows) return MOE_ERR_INVALID_ARG;
+  if (o->dtype != MOE_DTYPE_F32 && o->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_mx_quantize_act(x, o->dtype == MOE_DTYPE_BF16, rows, int(K), stride,
+                                           codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn_mx(const moe_dims* d, const moe_opts* o, int64_t n_groups, int64_t max_rows,
+                      int64_t F, const uint8_t* xq, const uint8_t* xs, int64_t x_stride,
+                      const int32_t* offsets, const uint8_t* W13q, const uint8_t* W13s,
+                      const uint8_t* W2q, const uint8_t* W2s, uint8_t* aq, uint8_t* aqs,
+                      int64_t a_stride, float* out, void* stream) {
+  if (!d || !o || n_groups < 1 || n_groups > 256 || max_rows < 0 || max_rows >= (int64_t(1) << 31) ||
+      F < 256 || x_stride < max_rows + 4 || a_stride < max_rows + 4 || x_stride % 4 ||
+      a_stride % 4)
+    return MOE_ERR_INVALID_ARG;
+  if (o->act != MOE_ACT_SWIGLU && o->act != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
+  if (d->d % 256 || F % 256) return MOE_ERR_UNSUPPORTED;
+  if (max_rows == 0) return MOE_OK;
+  if (!xq || !xs || !offsets || !W13q || !W13s || !W2q || !W2s || !aq || !aqs || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(W13q) || !aligned16(W2q) || !aligned16(aq) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(W13s) & 3) || (reinterpret_cast<uintptr_t>(W2s) & 3) ||
+      (reinterpret_cast<uintptr_t>(xs) & 3) || (reinterpret_cast<uintptr_t>(aqs) & 3))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_mx_ffn(xq, xs, x_stride, offsets, int(n_groups), max_rows, int(d->d),
+                                  int(F), o->act, W13q, W13s, W2q, W2s, aq, aqs, a_stride, out,
+                                  static_cast<hipStream_t>(stream)));
+}
+
 int moe_score_histogram(const float* scores, int64_t T, int64_t E, float lo, float hi,
                         int32_t nbins, int32_t* hist, void* stream) {
   if (!hist || T < 0 || E < 1 || nbins < 1 || !isfinite(lo) || !isfinite(hi) || !(lo < hi))

@@ -130,4 +130,17 @@ hipError_t launch_router_report(int E, int d, const int32_t* counts, const int32
                                 const float* o, const int32_t* offsets, float* norm, float* report,
                                 hipStream_t st);
 
+// ------------------------------------------------------------------ MXFP4 experts
+// weights w [rows = G*N, K] (bf16 or fp32) -> codes [rows, K/2], scales [G][K/32][N]
+hipError_t launch_mx_quantize_weights(const void* w, bool bf16, int64_t rows, int K, int N,
+                                      uint8_t* codes, uint8_t* scales, hipStream_t st);
+// activations x [rows, K] -> FP8 codes [rows, K], scales [K/64][stride]
+hipError_t launch_mx_quantize_act(const void* x, bool bf16, int64_t rows, int K, int64_t stride,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_mx_ffn(const uint8_t* xq, const uint8_t* xs, int64_t x_stride,
+                         const int32_t* offsets, int G, int64_t max_rows, int d, int F, int act,
+                         const uint8_t* W13q, const uint8_t* W13s, const uint8_t* W2q,
+                         const uint8_t* W2s, uint8_t* aq, uint8_t* aqs, int64_t a_stride,
+                         float* out, hipStream_t st);
+
 }  // namespace moe

@@ -5,7 +5,8 @@ that received at least one row, each tensor read or written once.  These are
 the figures the roofline fractions are computed from.
 
 Peaks of one MI355X (AMD's published dense figures): HBM3E 8 TB/s; bf16 MFMA
-2.5 PFLOP/s; fp32 vector 157.3 TFLOP/s (packed), 78.6 TFLOP/s without packed
+2.5 PFLOP/s; fp8 MFMA 5.0 PFLOP/s (also the rate of the scaled FP8 x FP4
+matrix instruction, whose issue rate is set by its wider operand); fp32 vector 157.3 TFLOP/s (packed), 78.6 TFLOP/s without packed
 FP32 instructions.
 """
 
@@ -18,6 +19,7 @@ from .presets import Preset
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP32_TFLOPS = 157.3
 
 
@@ -44,6 +46,16 @@ def ffn_bytes(p: Preset, R: int, active_experts: int, shared: bool = True) -> fl
     b += R * p.d * eb(p) + 2 * R * p.F * eb(p) + R * p.d * 4
     if shared and p.F_shared:
         b += 3 * p.d * p.F_shared * eb(p) + p.T * p.d * eb(p) + 2 * p.T * p.F_shared * eb(p) + p.T * p.d * 4
+    return float(b)
+
+
+def ffn_mx_bytes(p: Preset, R: int, active_experts: int) -> float:
+    """MXFP4 routed expert FFN: FP4 weights (half a byte per element) and their
+    E8M0 scales (one per 32) of active experts, FP8 x_perm and its scales (one
+    per 64), FP8 activation and scales written then read, fp32 output written."""
+    w = active_experts * n_mats(p) * p.d * p.F
+    b = w // 2 + w // 32
+    b += R * p.d + R * p.d // 64 + 2 * (R * p.F + R * p.F // 64) + R * p.d * 4
     return float(b)
 
 
