@@ -15,16 +15,21 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------- bf16 <-> f32
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// Round to nearest even; NaN stays a quiet NaN.
+// Round to nearest even; NaN stays a quiet NaN (a select, not a branch).
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? (u >> 16) | 0x40u : r);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (lo in the low half) with gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32): round to nearest even, NaN quiet.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+  const floatx2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // ---------------------------------------------------------------- wave helpers

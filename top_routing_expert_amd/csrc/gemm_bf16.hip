@@ -13,13 +13,14 @@
 //    activations as stored (K-major), out [g][M_fixed, N] fp32.
 //
 // Design for CDNA4:
-//  * 256 threads = 4 waves in a 2x2 grid; each wave owns a (BM/2) x (BN/2)
-//    sub-tile of every panel as (BM/64) x (BN/64) blocks of
-//    v_mfma_f32_32x32x16_bf16.  With BM = BN = 256 a wave issues 16 MFMAs per
-//    8 operand fragments, half the LDS bytes per MFMA of a 64x64 wave tile.
+//  * 512 threads = 8 waves in a 2x4 grid (two waves per SIMD); each wave owns
+//    a (BM/2) x (BN/4) sub-tile of every panel as (BM/64) x (BN/128) blocks of
+//    v_mfma_f32_32x32x16_bf16.  With BM = BN = 256 a wave issues 8 MFMAs per
+//    6 operand fragments.
 //  * Global -> LDS with global_load_lds_dwordx4 (no staging registers): each
-//    wave instruction fills 1 KB of LDS.  Two K stages of 64 are double
-//    buffered: the loads of stage k+1 are in flight while stage k multiplies.
+//    wave instruction fills 1 KB of LDS.  A ring of K stages of 64 (as many as
+//    fit 144 KB, at most 4): the loads of the next stages are in flight while
+//    a stage multiplies.
 //  * A K-contiguous operand is staged as rows of 64 k (128 B) whose eight
 //    16-byte chunks are XOR-swizzled by (row & 7) ^ ((row >> 3) & 1); an MFMA
 //    fragment is one 16-byte LDS read per lane, conflict-free whether the LDS
@@ -43,6 +44,9 @@
 //  * NP = 2 (SwiGLU forward): the gate rows n0.. and up rows up_off+n0.. of
 //    W13 are two B panels multiplied against one A tile; the epilogue forms
 //    silu(gate) * up directly.
+//  * The epilogue stages the accumulators through LDS (row-contiguous 16-lane
+//    stores), applies GELU / SwiGLU or their backward with hardware 2^x and
+//    reciprocal and the bf16 conversion instruction, and writes bf16 or fp32.
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -418,24 +422,24 @@ void gg_bf16_kernel(GemmArgs g) {
           const float4 hu = unpack_bf4(*reinterpret_cast<const uint2*>(hr + g.up_off + n));
           uint16_t* orow = static_cast<uint16_t*>(g.out) + row * g.n_b;
           *reinterpret_cast<uint2*>(orow + n) =
-              make_uint2(pack_bf2(v0.x * hu.x * dsilu(hg.x), v0.y * hu.y * dsilu(hg.y)),
-                         pack_bf2(v0.z * hu.z * dsilu(hg.z), v0.w * hu.w * dsilu(hg.w)));
+              make_uint2(pack_bf2(v0.x * hu.x * dsilu_fast(hg.x), v0.y * hu.y * dsilu_fast(hg.y)),
+                         pack_bf2(v0.z * hu.z * dsilu_fast(hg.z), v0.w * hu.w * dsilu_fast(hg.w)));
           *reinterpret_cast<uint2*>(orow + g.up_off + n) =
-              make_uint2(pack_bf2(v0.x * silu(hg.x), v0.y * silu(hg.y)),
-                         pack_bf2(v0.z * silu(hg.z), v0.w * silu(hg.w)));
+              make_uint2(pack_bf2(v0.x * silu_fast(hg.x), v0.y * silu_fast(hg.y)),
+                         pack_bf2(v0.z * silu_fast(hg.z), v0.w * silu_fast(hg.w)));
         } else if constexpr (EPI == EPI_GELU_BWD) {
           const float4 h = unpack_bf4(
               *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(g.h_in) + row * g.n_b + n));
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + row * g.n_b + n) =
-              make_uint2(pack_bf2(v0.x * dgelu_erf(h.x), v0.y * dgelu_erf(h.y)),
-                         pack_bf2(v0.z * dgelu_erf(h.z), v0.w * dgelu_erf(h.w)));
+              make_uint2(pack_bf2(v0.x * dgelu_fast(h.x), v0.y * dgelu_fast(h.y)),
+                         pack_bf2(v0.z * dgelu_fast(h.z), v0.w * dgelu_fast(h.w)));
         } else if constexpr (EPI == EPI_GELU) {
           if (g.h_save)
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.h_save) + row * g.n_b + n) =
                 make_uint2(pack_bf2(v0.x, v0.y), pack_bf2(v0.z, v0.w));
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + row * g.N + n) =
-              make_uint2(pack_bf2(gelu_erf(v0.x), gelu_erf(v0.y)),
-                         pack_bf2(gelu_erf(v0.z), gelu_erf(v0.w)));
+              make_uint2(pack_bf2(gelu_fast(v0.x), gelu_fast(v0.y)),
+                         pack_bf2(gelu_fast(v0.z), gelu_fast(v0.w)));
         } else {
           const float4 v1 = *reinterpret_cast<const float4*>(cw + (32 + rl) * CST + c4);
           if (g.h_save) {
@@ -445,8 +449,8 @@ void gg_bf16_kernel(GemmArgs g) {
                 make_uint2(pack_bf2(v1.x, v1.y), pack_bf2(v1.z, v1.w));
           }
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + row * g.N + n) =
-              make_uint2(pack_bf2(silu(v0.x) * v1.x, silu(v0.y) * v1.y),
-                         pack_bf2(silu(v0.z) * v1.z, silu(v0.w) * v1.w));
+              make_uint2(pack_bf2(silu_fast(v0.x) * v1.x, silu_fast(v0.y) * v1.y),
+                         pack_bf2(silu_fast(v0.z) * v1.z, silu_fast(v0.w) * v1.w));
         }
       }
     }

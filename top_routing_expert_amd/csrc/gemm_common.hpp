@@ -45,6 +45,48 @@ __device__ __forceinline__ float dgelu_erf(float v) {
   return 0.5f * (1.0f + erff(v * 0.70710678118654752f)) +
          v * 0.39894228040143268f * expf(-0.5f * v * v);
 }
+// Cheaper forms for epilogues whose results are rounded to bf16 (relative
+// step 2^-9): hardware 2^x and reciprocal (about 1 ulp each) and erf from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+// t = 1 / (1 + p x) for x >= 0, |error| <= 1.5e-7.  GELU's exp(-v^2/2) is the
+// same exponential, so gelu' costs one more multiply-add.
+__device__ __forceinline__ float exp_fast(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+// 1 - erf(|x|) = poly(t) * e with e = exp(-x^2) supplied by the caller
+__device__ __forceinline__ float erfc_poly(float ax) {
+  const float t = rcp_fast(fmaf(0.3275911f, ax, 1.0f));
+  float p = 1.061405429f;
+  p = fmaf(p, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  return p * t;
+}
+// Phi(v) = (1 + erf(v / sqrt 2)) / 2 and the Gaussian factor exp(-v^2/2)
+__device__ __forceinline__ float phi_cdf(float v, float& e) {
+  const float x = v * 0.70710678118654752f;
+  e = exp_fast(-x * x);
+  const float q = 0.5f * erfc_poly(fabsf(x)) * e;   // (1 - erf|x|) / 2
+  return v >= 0.0f ? 1.0f - q : q;
+}
+__device__ __forceinline__ float gelu_fast(float v) {
+  float e;
+  return v * phi_cdf(v, e);
+}
+__device__ __forceinline__ float dgelu_fast(float v) {
+  float e;
+  const float c = phi_cdf(v, e);
+  return fmaf(v * 0.39894228040143268f, e, c);
+}
+__device__ __forceinline__ float silu_fast(float v) { return v * rcp_fast(1.0f + exp_fast(-v)); }
+__device__ __forceinline__ float dsilu_fast(float v) {
+  const float s = rcp_fast(1.0f + exp_fast(-v));
+  return s * fmaf(v, 1.0f - s, 1.0f);
+}
+
 __device__ __forceinline__ float4 unpack_bf4(uint2 u) {
   return make_float4(bf2f(uint16_t(u.x & 0xffffu)), bf2f(uint16_t(u.x >> 16)),
                      bf2f(uint16_t(u.y & 0xffffu)), bf2f(uint16_t(u.y >> 16)));
