@@ -153,6 +153,7 @@ def test_layer_bwd_full_size(name):
         dg[m, j] = np.sum(dy[m] * o[ros[m, j]], axis=1)
     dz = orc.router_bwd(p, r["s"], r["z"], idx, counts, dg)
     e1 = _close(g["dWg"].cpu().numpy(), X64.T @ dz, 2e-2, "dWg")
+    print(f"[{name} bwd] dWg max-abs error / rms {e1:.2e}", flush=True)
 
     # sampled experts: hottest, median, last, and empty ones
     sizes = np.diff(offsets)

@@ -8,6 +8,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 using namespace moe;
 
 namespace {
@@ -82,12 +84,30 @@ int check_router_inputs(const moe_opts* o, const moe_router_inputs* ri) {
 }
 
 // ---- workspace plans -------------------------------------------------------
-struct RouteWs { size_t wsplit, part_p, part_cnt, part_lse2, part_nf, zn; int nblk, EP; };
+// Logits of bf16 tokens for 64 or more (padded) experts run as one grouped-GEMM
+// launch: x . [hi; mid; lo]^T with the three bf16 planes of Wg stacked as the
+// rows of B, into z3 [T, np3] fp32, then a per-token kernel adds the planes and
+// runs the router epilogue.  (With 32 experts the fused logits kernel, which
+// keeps z on chip, is as fast.)
+bool route_gemm(const moe_dims* d, const moe_opts* o, int EP) {
+  return route_mfma(d, o, EP) && EP >= 64 && d->d % 64 == 0 &&
+         o->routing != MOE_ROUTING_NOISY_TOPK;
+}
+
+struct RouteWs {
+  size_t wsplit, part_p, part_cnt, part_lse2, part_nf, zn, z3, off1;
+  int nblk, EP, np3;
+  bool gemm;
+};
 RouteWs plan_route(Carver& c, const moe_dims* d, const moe_opts* o) {
   RouteWs r;
   r.EP = route_pad_experts(int(d->E));
   r.nblk = int(cdiv(d->T, ROUTE_BT));
-  r.wsplit = c.take(size_t(3) * r.EP * d->d * 2);
+  r.gemm = route_gemm(d, o, r.EP);
+  r.np3 = int(cdiv(3 * r.EP, 128) * 128);
+  r.wsplit = c.take(size_t(r.gemm ? r.np3 : 3 * r.EP) * d->d * 2);
+  r.z3 = c.take(r.gemm ? size_t(d->T) * r.np3 * 4 : 0);
+  r.off1 = c.take(r.gemm ? 2 * 4 : 0);
   r.part_p = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_cnt = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_lse2 = c.take(size_t(r.nblk) * 4);
@@ -201,15 +221,30 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
     an.offset = nullptr;
     an.logits = zn;
     an.logits_only = 1;
-    if (mfma) MOE_TRY(launch_wg_split(ri->W_noise, a.d, a.E, a.EP, at<uint16_t>(ws, rw.wsplit), st));
+    if (mfma)
+      MOE_TRY(launch_wg_split(ri->W_noise, a.d, a.E, a.EP, 0, at<uint16_t>(ws, rw.wsplit), nullptr,
+                              a.T, st));
     MOE_TRY(launch_route(an, mfma, st));
     a.noise = ri->noise;
     a.noise_logit = zn;
   }
   if (o->routing == MOE_ROUTING_RANDOM_SECOND) a.uniform = ri->uniform;
   if (o->routing == MOE_ROUTING_HASH) a.token_ids = ri->token_ids;
-  if (mfma) MOE_TRY(launch_wg_split(Wg, a.d, a.E, a.EP, at<uint16_t>(ws, rw.wsplit), st));
-  MOE_TRY(launch_route(a, mfma, st));
+  if (rw.gemm) {
+    int32_t* off1 = at<int32_t>(ws, rw.off1);
+    float* z3 = at<float>(ws, rw.z3);
+    MOE_TRY(launch_wg_split(Wg, a.d, a.E, a.EP, rw.np3 - 3 * a.EP, at<uint16_t>(ws, rw.wsplit),
+                            off1, a.T, st));
+    GemmArgs g{};
+    g.A = x; g.B = a.wsplit; g.offsets = off1; g.G = 1; g.max_rows = a.T; g.N = rw.np3; g.K = a.d;
+    g.epi = EPI_STORE_F32; g.out = z3; g.mode = GM_NT;
+    MOE_TRY(launch_grouped_gemm_bf16(g, st));
+    MOE_TRY(launch_route_from_partials(a, z3, rw.np3, st));
+  } else {
+    if (mfma)
+      MOE_TRY(launch_wg_split(Wg, a.d, a.E, a.EP, 0, at<uint16_t>(ws, rw.wsplit), nullptr, a.T, st));
+    MOE_TRY(launch_route(a, mfma, st));
+  }
   if (counts || losses || n_nonfinite)
     MOE_TRY(launch_route_reduce(a, rw.nblk, o->aux_coef, o->z_coef, counts, losses, n_nonfinite, st));
   return MOE_OK;
@@ -293,9 +328,31 @@ int shared_split(const moe_dims* d, int64_t M, int64_t N) {
   return int(s < by_t ? s : by_t);
 }
 
+// Router gradients of bf16 layers run on the bf16 grouped GEMM (dz and Wg as
+// exact three-way bf16 splits): dx_router = dz Wg^T over K' = 6E plane slots,
+// dWg = x^T dz over token chunks.  fp32 layers and noisy top-k use the fp32
+// FMA kernels.
+bool router_bwd_mfma(const moe_dims* d, const moe_opts* o) {
+  return o->dtype == MOE_DTYPE_BF16 && d->d % 256 == 0 && o->routing != MOE_ROUTING_NOISY_TOPK;
+}
+int64_t router_kp(int64_t E) { return cdiv(6 * E, 128) * 128; }   // plane slots, padded
+int64_t router_n3(int64_t E) { return cdiv(3 * E, 128) * 128; }   // dWg's B columns, padded
+// Token chunks of dWg's reduction: about one 256-row output tile per CU, at
+// least 256 tokens per chunk, at most 32 MB of fp32 partials.
+int router_split(const moe_dims* d) {
+  const int64_t n3 = router_n3(d->E);
+  const int64_t tiles = (d->d / 256) * (n3 / (n3 % 256 == 0 ? 256 : 128));
+  int64_t s = cdiv(256, tiles);
+  const int64_t by_t = d->T / 256 > 0 ? d->T / 256 : 1;
+  const int64_t by_mem = std::max<int64_t>(1, (int64_t(32) << 20) / (d->d * n3 * 4));
+  s = std::min(std::min(s, by_t), by_mem);
+  return int(s < 1 ? 1 : s);
+}
+
 struct BwdWs {
   FfnWs ffn, ffn_s;
   size_t dO, dg, dH, dXp, dz, dwg_part, dxr;
+  size_t rplanes, wplanes, rpart, roff1, roffs;   // router gradients on the matrix cores
   size_t dyx, dHs, dxs, soff, ssplit_off, spart;
   size_t dzn, dwn_part;   // noisy top-k
 };
@@ -311,7 +368,13 @@ BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   b.dH = c.take(size_t(R) * nu * eb);
   b.dXp = c.take(size_t(R) * d->d * 4);
   b.dz = c.take(size_t(d->T) * d->E * 4);
-  b.dwg_part = c.take(size_t(dwg_split(d)) * d->d * d->E * 4);
+  const bool rm = router_bwd_mfma(d, o);
+  b.dwg_part = c.take(rm ? 0 : size_t(dwg_split(d)) * d->d * d->E * 4);
+  b.rplanes = c.take(rm ? size_t(d->T) * router_kp(d->E) * 2 : 0);
+  b.wplanes = c.take(rm ? size_t(d->d) * router_kp(d->E) * 2 : 0);
+  b.rpart = c.take(rm ? size_t(router_split(d)) * d->d * router_n3(d->E) * 4 : 0);
+  b.roff1 = c.take(rm ? 2 * 4 : 0);
+  b.roffs = c.take(rm ? size_t(router_split(d) + 1) * 4 : 0);
   const bool noisy = o->routing == MOE_ROUTING_NOISY_TOPK;
   // noisy top-k: dx_router = dz Wg^T + dzn W_noise^T as two partials summed in order
   b.dxr = c.take(size_t(noisy ? 2 : 1) * d->T * d->d * 4);
@@ -617,10 +680,30 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   MOE_TRY(launch_router_bwd(sv->logits, sv->topk_idx, at<float>(ws, b.dg), sv->counts, T, E, k,
                             o->score, o->renorm != 0, o->gate_scale, o->aux_coef, o->z_coef, dz,
                             st));
-  MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
-                              at<float>(ws, b.dwg_part), grads->dWg, st));
   float* dxr = at<float>(ws, b.dxr);
-  if (noisy) {
+  if (router_bwd_mfma(d, o)) {
+    const int KP = int(router_kp(E)), N3 = int(router_n3(E)), s = router_split(d);
+    uint16_t* zp = at<uint16_t>(ws, b.rplanes);     // [T, KP]: dz slots hi mid lo hi hi mid
+    uint16_t* wp = at<uint16_t>(ws, b.wplanes);     // [D, KP]: Wg slots hi hi hi mid lo mid
+    MOE_TRY(launch_router_planes(dz, T, E, KP, 0x100210u, zp, st));
+    MOE_TRY(launch_router_planes(w->Wg, D, E, KP, 0x121000u, wp, st));
+    int32_t* off1 = at<int32_t>(ws, b.roff1);
+    MOE_TRY(fill_offsets_1(off1, int32_t(T), st));
+    GemmArgs gx{};
+    gx.A = zp; gx.B = wp; gx.offsets = off1; gx.G = 1; gx.max_rows = T; gx.N = D; gx.K = KP;
+    gx.epi = EPI_STORE_F32; gx.out = dxr; gx.mode = GM_NT;
+    MOE_TRY(launch_grouped_gemm_bf16(gx, st));
+    // dWg = x^T [hi | mid | lo] per token chunk; chunks and planes summed in order
+    int32_t* coff = at<int32_t>(ws, b.roffs);
+    float* part = at<float>(ws, b.rpart);
+    MOE_TRY(launch_fill_seq_i32(coff, s + 1, int32_t(cdiv(T, s)), int32_t(T), st));
+    GemmArgs gw = gemm_wgrad(x, zp, coff, s, D, N3, part);
+    gw.ldb = KP;
+    MOE_TRY(launch_grouped_gemm_bf16(gw, st));
+    MOE_TRY(launch_dwg_reduce(part, s, D, N3, E, grads->dWg, st));
+  } else if (noisy) {
+    MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
+                                at<float>(ws, b.dwg_part), grads->dWg, st));
     // H = z + noise * softplus(zn): dzn = dz * noise * sigmoid(zn);
     // dW_noise = x^T dzn; dx_router = dz Wg^T + dzn W_noise^T
     float* dzn = at<float>(ws, b.dzn);
@@ -632,6 +715,8 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
     MOE_TRY(launch_strided_gemm(dzn, false, E, 1, ri->W_noise, 1, E, T, D, E, 1, part, nullptr, st));
     MOE_TRY(launch_sum_partials(dxr, 2, int64_t(T) * D, dxr, st));
   } else {
+    MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
+                                at<float>(ws, b.dwg_part), grads->dWg, st));
     MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, st));
   }
   MOE_TRY(launch_unpermute_sum(at<float>(ws, b.dXp), sv->row_of_slot, dxs, dxr, T, k, D, dx, st));

@@ -357,6 +357,61 @@ hipError_t launch_strided_gemm(const void* A, bool a_bf16, int64_t sam, int64_t 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Router gradients on the bf16 matrix cores.  An fp32 value v splits exactly
+// into three bf16 planes (hi = rne(v), mid = rne(v - hi), lo = rne(v - hi -
+// mid); each residual is exact in fp32, so hi + mid + lo == v for normal v).
+// With dz and Wg both split, dz . Wg^T is the sum of the six plane products
+// p_i q_j with i + j <= 2 (the dropped ones are below 2^-24 relative), laid
+// out as K' = 6E slots: dz slots [hi mid lo hi hi mid], Wg slots [hi hi hi mid
+// lo mid].  The first three dz slots are also the B operand of dWg = x^T dz.
+__global__ void router_planes_kernel(const float* __restrict__ src, int64_t rows, int E, int KP,
+                                     uint32_t pattern, uint16_t* __restrict__ out) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= rows * KP) return;
+  const int64_t r = i / KP;
+  const int c = int(i - r * KP);
+  uint16_t v = 0;
+  if (c < 6 * E) {
+    const int slot = c / E, e = c - slot * E;
+    const float x = src[r * E + e];
+    const uint16_t hi = f2bf(x);
+    const float r1 = x - bf2f(hi);
+    const uint16_t mid = f2bf(r1);
+    const int pl = int(pattern >> (4 * slot)) & 15;
+    v = pl == 0 ? hi : (pl == 1 ? mid : f2bf(r1 - bf2f(mid)));
+  }
+  out[i] = v;
+}
+
+__global__ void dwg_reduce_kernel(const float* __restrict__ P, int nchunks, int D, int N3, int E,
+                                  float* __restrict__ dWg) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(D) * E) return;
+  const int dd = int(i / E), e = int(i % E);
+  float acc = 0.0f;
+  for (int c = 0; c < nchunks; ++c) {
+    const float* p = P + (int64_t(c) * D + dd) * N3;
+    acc += (p[e] + p[E + e]) + p[2 * E + e];
+  }
+  dWg[i] = acc;
+}
+
+hipError_t launch_router_planes(const float* src, int64_t rows, int E, int KP, uint32_t pattern,
+                                uint16_t* out, hipStream_t st) {
+  const int64_t n = rows * KP;
+  if (n == 0) return hipSuccess;
+  router_planes_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(src, rows, E, KP, pattern, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dwg_reduce(const float* P, int nchunks, int D, int N3, int E, float* dWg,
+                             hipStream_t st) {
+  const int64_t n = int64_t(D) * E;
+  dwg_reduce_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(P, nchunks, D, N3, E, dWg);
+  return hipGetLastError();
+}
+
 hipError_t launch_sum_partials(const float* P, int nz, int64_t n, float* out, hipStream_t st) {
   sum_partials_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(P, nz, n, out);
   return hipGetLastError();

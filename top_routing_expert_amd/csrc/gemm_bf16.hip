@@ -181,6 +181,8 @@ void gg_bf16_kernel(GemmArgs g) {
     tile = (bid & 7) * per + (bid >> 3);
     if ((bid >> 3) >= per || tile >= total) return;
   }
+  // Row stride of a K-major B: [rows, ldb] in the K-grouped mode, [K, N] otherwise.
+  const int64_t ldb = (MODE == GM_KGROUP && g.ldb) ? g.ldb : int64_t(g.N);
   TileCoord tc;
   int K;                                     // reduction length of this tile
   const uint16_t* A;
@@ -197,7 +199,7 @@ void gg_bf16_kernel(GemmArgs g) {
     const int32_t r0 = g.offsets[tc.grp];
     K = g.offsets[tc.grp + 1] - r0;
     A = static_cast<const uint16_t*>(g.A) + int64_t(r0) * g.M_fixed;
-    B = static_cast<const uint16_t*>(g.B) + int64_t(r0) * g.N;
+    B = static_cast<const uint16_t*>(g.B) + int64_t(r0) * ldb;
   } else {
     locate_tile(ts, g.offsets, g.G, tile, BM, BN, tc);
     K = g.K;
@@ -236,7 +238,7 @@ void gg_bf16_kernel(GemmArgs g) {
     if constexpr (BKM) {
       int col;
       kmajor_slot<BN>(w + WV * i, l, b_krow[i], col);
-      b_src[i] = B + int64_t(b_krow[i]) * g.N + tc.n0 + col;
+      b_src[i] = B + int64_t(b_krow[i]) * ldb + tc.n0 + col;
     } else {
       b_src[i] = B + int64_t(i * g.up_off + tc.n0 + 8 * w + lrow) * K + 8 * lchunk;
       b_krow[i] = 0;
@@ -258,7 +260,7 @@ void gg_bf16_kernel(GemmArgs g) {
     }
     uint4* bbase = base + BM * 8;
     if constexpr (BKM) {
-      const int64_t koff = int64_t(k0) * g.N;
+      const int64_t koff = int64_t(k0) * ldb;
 #pragma unroll
       for (int i = 0; i < B_INS; ++i) {
         const uint16_t* s = b_src[i] + koff;
@@ -488,7 +490,8 @@ static void launch_rows_np1(const GemmArgs& g, bool bm256, bool bn256, hipStream
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.G == 0) return hipSuccess;
   if (g.mode == GM_KGROUP) {
-    if (g.epi != EPI_STORE_F32 || g.M_fixed % 128 || g.N % 128) return hipErrorInvalidValue;
+    if (g.epi != EPI_STORE_F32 || g.M_fixed % 128 || g.N % 128 || (g.ldb && g.ldb < g.N))
+      return hipErrorInvalidValue;
     const bool m256 = g.M_fixed % 256 == 0, n256 = g.N % 256 == 0;
     if (m256 && n256) launch_cfg<256, 256, 1, EPI_STORE_F32, GM_KGROUP>(g, st);
     else if (m256) launch_cfg<256, 128, 1, EPI_STORE_F32, GM_KGROUP>(g, st);

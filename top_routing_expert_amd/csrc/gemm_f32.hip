@@ -161,6 +161,7 @@ static void launch_rows(const GemmArgs& g, unsigned grid, hipStream_t st) {
 }
 
 hipError_t launch_grouped_gemm_f32(const GemmArgs& g, hipStream_t st) {
+  if (g.ldb && g.ldb != g.N) return hipErrorInvalidValue;   // B row stride: N only
   if (g.G == 0) return hipSuccess;
   const int NT = int(cdiv(g.N, F32_BN));
   if (g.mode == GM_KGROUP) {

@@ -35,7 +35,11 @@ struct RouteArgs {
 constexpr int ROUTE_BT = 32;   // tokens per route block
 
 int route_pad_experts(int E);  // 32, 64, 128 or 256
-hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, uint16_t* out, hipStream_t st);
+hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, int pad_rows, uint16_t* out,
+                           int32_t* off1, int T, hipStream_t st);
+// Route from z3 [T, ldz] fp32 = x . [planes of Wg]^T (columns p*EP + e).
+hipError_t launch_route_from_partials(const RouteArgs& a, const float* z3, int ldz,
+                                      hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, bool mfma, hipStream_t st);
 hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, float z_coef,
                                int32_t* counts, float* losses, int32_t* n_nonfinite,
@@ -87,6 +91,7 @@ struct GemmArgs {
   int32_t* tile_start;      // [G+1] scratch for the fp32 planner
   int mode;                 // GemmMode
   int M_fixed;              // K mode: rows of each group's output
+  int64_t ldb;              // K mode: row stride of B in elements (0: N)
 };
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st);
 hipError_t launch_grouped_gemm_f32(const GemmArgs& g, hipStream_t st);
@@ -118,6 +123,15 @@ hipError_t launch_noise_grad(const float* dz, const float* noise, const float* z
                              float* dzn, hipStream_t st);
 // out[i] = sum over z of P[z * n + i], z = 0..nz-1 in order
 hipError_t launch_sum_partials(const float* P, int nz, int64_t n, float* out, hipStream_t st);
+// Router gradients on the bf16 grouped GEMM: src [rows, E] fp32 written as rows
+// of KP bf16 values whose slot s (columns s*E..s*E+E-1, s < 6) holds plane
+// (pattern >> 4s) & 15 of the exact three-way split (0 hi, 1 mid, 2 lo);
+// columns from 6E on are zero.
+hipError_t launch_router_planes(const float* src, int64_t rows, int E, int KP, uint32_t pattern,
+                                uint16_t* out, hipStream_t st);
+// dWg[d][e] = sum over chunks g (in order) of P[g][d][e] + P[g][d][E+e] + P[g][d][2E+e].
+hipError_t launch_dwg_reduce(const float* P, int nchunks, int D, int N3, int E, float* dWg,
+                             hipStream_t st);
 hipError_t launch_unpermute_sum(const float* dxp, const int32_t* ros, const float* e1,
                                 const float* e2, int T, int k, int d, float* dx, hipStream_t st);
 

@@ -18,15 +18,23 @@ namespace moe {
 int route_pad_experts(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256; }
 
 // ---------------------------------------------------------------------------
-// Wg [d, E] fp32 -> three bf16 planes [3][EP][d], expert-major (K-contiguous).
+// Wg [d, E] fp32 -> three bf16 planes [3][EP][d], expert-major (K-contiguous),
+// followed by pad_rows zero rows (the planes are also the B operand [rows, d] of
+// the logits GEMM, whose row count must be a multiple of 128); off1, when
+// given, receives the row offsets {0, T} of that GEMM's single group.
 // hi = rne(w), mid = rne(w - hi), lo = rne(w - hi - mid); each residual is
 // exact in fp32 and the last has at most 8 significant bits, so
 // hi + mid + lo == w for every normal w.  Experts e >= E are zero.
-__global__ void wg_split_kernel(const float* __restrict__ Wg, int d, int E, int EP,
-                                uint16_t* __restrict__ out) {
+__global__ void wg_split_kernel(const float* __restrict__ Wg, int d, int E, int EP, int pad_rows,
+                                uint16_t* __restrict__ out, int32_t* __restrict__ off1, int T) {
   const int64_t n = int64_t(EP) * d;
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i == 0 && off1) {
+    off1[0] = 0;
+    off1[1] = T;
+  }
   if (i >= n) return;
+  if (i < int64_t(pad_rows) * d) out[3 * n + i] = 0;
   const int e = int(i / d), kk = int(i % d);
   const float w = e < E ? Wg[int64_t(kk) * E + e] : 0.0f;
   const uint16_t hi = f2bf(w);
@@ -417,9 +425,47 @@ __global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nbl
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, uint16_t* out, hipStream_t st) {
+hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, int pad_rows, uint16_t* out,
+                           int32_t* off1, int T, hipStream_t st) {
+  if (pad_rows > EP) return hipErrorInvalidValue;
   const int64_t n = int64_t(EP) * d;
-  wg_split_kernel<<<dim3(unsigned(cdiv(n, 256))), dim3(256), 0, st>>>(Wg, d, E, EP, out);
+  wg_split_kernel<<<dim3(unsigned(cdiv(n, 256))), dim3(256), 0, st>>>(Wg, d, E, EP, pad_rows, out,
+                                                                      off1, T);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Route from the logits GEMM's output: z3 [T, ldz] fp32 holds, per token, the
+// three plane products x . q_p at columns p*EP + e (p = 0, 1, 2), added here
+// in plane order.
+template <int EP>
+__global__ __launch_bounds__(512) void route_from_partials_kernel(RouteArgs a, const float* z3,
+                                                                  int ldz) {
+  constexpr int NW = 8;
+  __shared__ float zs[1][ROUTE_BT][EP + 1];
+  __shared__ float red_p[NW * EP];
+  __shared__ int32_t red_c[NW * EP];
+  __shared__ float red_s[2 * NW];
+  const int t0 = blockIdx.x * ROUTE_BT;
+  for (int o = threadIdx.x; o < ROUTE_BT * EP; o += blockDim.x) {
+    const int tl = o / EP, e = o - tl * EP;
+    const float* zr = z3 + int64_t(min(t0 + tl, a.T - 1)) * ldz + e;
+    zs[0][tl][e] = (zr[0] + zr[EP]) + zr[2 * EP];
+  }
+  __syncthreads();
+  route_epilogue<EP, 1, NW>(a, zs, t0, red_p, red_c, red_s);
+}
+
+hipError_t launch_route_from_partials(const RouteArgs& a, const float* z3, int ldz,
+                                      hipStream_t st) {
+  const unsigned nblk = unsigned(cdiv(a.T, ROUTE_BT));
+  switch (a.EP) {
+    case 32: route_from_partials_kernel<32><<<nblk, 512, 0, st>>>(a, z3, ldz); break;
+    case 64: route_from_partials_kernel<64><<<nblk, 512, 0, st>>>(a, z3, ldz); break;
+    case 128: route_from_partials_kernel<128><<<nblk, 512, 0, st>>>(a, z3, ldz); break;
+    case 256: route_from_partials_kernel<256><<<nblk, 512, 0, st>>>(a, z3, ldz); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
