@@ -44,6 +44,53 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
   return (uint64_t(hi) << 32) | lo;
 }
 
+// Reductions over aligned groups of G <= 16 lanes with DPP inside a row of
+// 16 lanes: quad swaps (lane ^ 1, lane ^ 2), then the half-row mirror (lane i
+// <-> 7 - i) and the row mirror (i <-> 15 - i), which pair each partial with
+// one from the other half once the halves are uniform.  Every lane of a group
+// ends with the same result (each step combines two equal-order partials), no
+// LDS crossbar round trips.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return uint64_t(dpp_u32<CTRL>(uint32_t(v))) | (uint64_t(dpp_u32<CTRL>(uint32_t(v >> 32))) << 32);
+}
+template <int G>
+__device__ __forceinline__ float row_max(float v) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group of 2..16 lanes");
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  if constexpr (G >= 4) v = fmaxf(v, dpp_f32<0x4E>(v));
+  if constexpr (G >= 8) v = fmaxf(v, dpp_f32<0x141>(v));
+  if constexpr (G >= 16) v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group of 2..16 lanes");
+  v += dpp_f32<0xB1>(v);
+  if constexpr (G >= 4) v += dpp_f32<0x4E>(v);
+  if constexpr (G >= 8) v += dpp_f32<0x141>(v);
+  if constexpr (G >= 16) v += dpp_f32<0x140>(v);
+  return v;
+}
+template <int G>
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group of 2..16 lanes");
+  uint64_t o = dpp_u64<0xB1>(v);
+  v = o > v ? o : v;
+  if constexpr (G >= 4) { o = dpp_u64<0x4E>(v); v = o > v ? o : v; }
+  if constexpr (G >= 8) { o = dpp_u64<0x141>(v); v = o > v ? o : v; }
+  if constexpr (G >= 16) { o = dpp_u64<0x140>(v); v = o > v ? o : v; }
+  return v;
+}
+
 // Reductions over aligned groups of G lanes (G a power of two <= 64).
 template <int G>
 __device__ __forceinline__ float group_max(float v) {

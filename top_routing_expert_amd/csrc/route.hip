@@ -49,13 +49,15 @@ __global__ void wg_split_kernel(const float* __restrict__ Wg, int d, int E, int 
 // ---------------------------------------------------------------------------
 // Per-token epilogue shared by both logit kernels (NW waves per block).  zs
 // holds KS partial logit sums for the block's 32 tokens.  Each token is
-// handled by a group of LG lanes, each owning VPL experts e = lane_in_group +
-// LG * v.  LDS scratch: red_p/red_c [NW * EP], red_s [2 * NW].
+// handled by a group of LG = 16 lanes (one DPP row, four tokens per wave at
+// a time), each owning VPL experts e = lane_in_group + LG * v; all per-token
+// reductions stay inside the row.  LDS scratch: red_p/red_c [NW * EP],
+// red_s [2 * NW].
 template <int EP, int KS, int NW>
 __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[ROUTE_BT][EP + 1],
                                                int t0, float* red_p, int32_t* red_c,
                                                float* red_s) {
-  constexpr int LG = EP < 64 ? EP : 64;
+  constexpr int LG = EP < 16 ? EP : 16;
   constexpr int TPI = 64 / LG;
   constexpr int VPL = EP / LG;
   constexpr int KMAX = 16;
@@ -111,12 +113,12 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
           if (lg + LG * v < E) a.logits[int64_t(t) * E + lg + LG * v] = z[v];
       continue;
     }
-    m = group_max<LG>(m);
+    m = row_max<LG>(m);
     float sexp = 0.0f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
       if (lg + LG * v < E) sexp += expf(z[v] - m);
-    sexp = group_sum<LG>(sexp);
+    sexp = row_sum<LG>(sexp);
     float ssum = 0.0f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
@@ -132,7 +134,7 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
       s[v] = e < E ? sv : 0.0f;
       ssum += s[v];
     }
-    ssum = group_sum<LG>(ssum);
+    ssum = row_sum<LG>(ssum);
     const float lse = m + logf(sexp);
 
     uint64_t key[VPL];
@@ -158,7 +160,7 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
           uint64_t best = 0;
 #pragma unroll
           for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-          best = group_max_u64<LG>(best);
+          best = row_max_u64<LG>(best);
           e = int(~uint32_t(best));
         }
         float sv = 0.0f;
@@ -169,7 +171,8 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
             key[v] = 0;
             cacc[v] += valid ? 1 : 0;
           }
-        const float ge = __shfl(sv, gi * LG + (e % LG), 64);
+        // the owner's score (the other lanes add zeros: exact)
+        const float ge = row_sum<LG>(sv);
         isel[j] = e;
         gsel[j] = ge;
         gs += ge;
