@@ -133,7 +133,14 @@ def main():
     def timed(fn, iters):
         fn()
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(2e7))          # keep the GPU busy while the host enqueues
+        # A device-side spin keeps the queue full while the host enqueues the
+        # iterations, so the events see only GPU time; it is sized from the host
+        # cost of one call (binding overhead included), with a 2x margin.
+        h0 = time.perf_counter()
+        fn()
+        host = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(min(2.4e9 * (2.0 * host * iters + 2e-3), 1.2e10)))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(iters):

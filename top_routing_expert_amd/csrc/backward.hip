@@ -10,6 +10,8 @@
 #include "gemm_common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace moe {
 
 constexpr int BWD_KMAX = 16;
@@ -365,23 +367,25 @@ hipError_t launch_strided_gemm(const void* A, bool a_bf16, int64_t sam, int64_t 
 // p_i q_j with i + j <= 2 (the dropped ones are below 2^-24 relative), laid
 // out as K' = 6E slots: dz slots [hi mid lo hi hi mid], Wg slots [hi hi hi mid
 // lo mid].  The first three dz slots are also the B operand of dWg = x^T dz.
-__global__ void router_planes_kernel(const float* __restrict__ src, int64_t rows, int E, int KP,
+// One thread per (row, e) (grid.y = row): the split is computed once and
+// written to the six slots; columns 6E .. KP-1 are zeroed.
+__global__ void router_planes_kernel(const float* __restrict__ src, int E, int KP,
                                      uint32_t pattern, uint16_t* __restrict__ out) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= rows * KP) return;
-  const int64_t r = i / KP;
-  const int c = int(i - r * KP);
-  uint16_t v = 0;
-  if (c < 6 * E) {
-    const int slot = c / E, e = c - slot * E;
-    const float x = src[r * E + e];
-    const uint16_t hi = f2bf(x);
-    const float r1 = x - bf2f(hi);
-    const uint16_t mid = f2bf(r1);
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = blockIdx.y;
+  if (e >= E) return;
+  const float x = src[r * E + e];
+  const uint16_t hi = f2bf(x);
+  const float r1 = x - bf2f(hi);
+  const uint16_t mid = f2bf(r1);
+  const uint16_t lo = f2bf(r1 - bf2f(mid));
+  uint16_t* o = out + r * KP;
+#pragma unroll
+  for (int slot = 0; slot < 6; ++slot) {
     const int pl = int(pattern >> (4 * slot)) & 15;
-    v = pl == 0 ? hi : (pl == 1 ? mid : f2bf(r1 - bf2f(mid)));
+    o[slot * E + e] = pl == 0 ? hi : (pl == 1 ? mid : lo);
   }
-  out[i] = v;
+  for (int c = 6 * E + e; c < KP; c += E) o[c] = 0;
 }
 
 __global__ void dwg_reduce_kernel(const float* __restrict__ P, int nchunks, int D, int N3, int E,
@@ -399,9 +403,13 @@ __global__ void dwg_reduce_kernel(const float* __restrict__ P, int nchunks, int 
 
 hipError_t launch_router_planes(const float* src, int64_t rows, int E, int KP, uint32_t pattern,
                                 uint16_t* out, hipStream_t st) {
-  const int64_t n = rows * KP;
-  if (n == 0) return hipSuccess;
-  router_planes_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(src, rows, E, KP, pattern, out);
+  if (rows == 0) return hipSuccess;
+  // rows beyond the grid's y limit are taken in slices
+  for (int64_t r0 = 0; r0 < rows; r0 += 65535) {
+    const unsigned ny = unsigned(std::min<int64_t>(65535, rows - r0));
+    router_planes_kernel<<<dim3(unsigned(cdiv(E, 256)), ny), 256, 0, st>>>(
+        src + r0 * E, E, KP, pattern, out + r0 * KP);
+  }
   return hipGetLastError();
 }
 

@@ -485,7 +485,7 @@ static void launch_rows_np1(const GemmArgs& g, bool bm256, bool bn256, hipStream
 
 // Tile shape (row modes): 256-row tiles when groups average at least 192 rows
 // (fewer re-reads of each weight panel), else 128; 256-column tiles when that
-// still gives a tile per CU, else 128.  K-grouped mode: 256 x 256 when the
+// still gives three tiles per four CUs, else 128.  K-grouped mode: 256 x 256 when the
 // output dimensions allow it.
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.G == 0) return hipSuccess;
@@ -504,7 +504,7 @@ hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   const int64_t avg = g.max_rows / g.G;
   const bool bm256 = avg >= 192;
   const int64_t mt = cdiv(g.max_rows, bm256 ? 256 : 128);
-  const bool bn256 = (g.N % 256 == 0) && mt * (g.N / 256) >= 256;
+  const bool bn256 = (g.N % 256 == 0) && mt * (g.N / 256) >= 192;
   if (g.mode == GM_NN) {
     switch (g.epi) {
       case EPI_STORE_F32: launch_rows_np1<EPI_STORE_F32, GM_NN>(g, bm256, bn256, st); break;

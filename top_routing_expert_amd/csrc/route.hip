@@ -143,59 +143,62 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
       const int e = lg + LG * v;
       key[v] = e < E ? (uint64_t(order_key(s[v] + bia[v])) << 32) | uint32_t(~uint32_t(e)) : 0ull;
     }
-    int isel[KMAX];
-    float gsel[KMAX];
-    float gs = 0.0f;
+    // k selection rounds, kept rolled (the per-expert work inside is
+    // unrolled): lane j of the token's group keeps round j's expert and gate,
+    // which it writes below; the first two gates are kept for the random
+    // second-expert rule.
+    int my_e = 0, e1 = 0;
+    float my_g = 0.0f, g0 = 0.0f, g1 = 0.0f, gs = 0.0f;
+#pragma unroll 1
+    for (int j = 0; j < k; ++j) {
+      int e;
+      if (a.routing == 1) {
+        e = int((int64_t(t) * k + j) % E);
+      } else if (a.routing == 4) {
+        e = valid ? int((int64_t(fmix32(uint32_t(a.token_ids[t]))) + j) % E) : 0;
+      } else {
+        uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      isel[j] = 0;
-      gsel[j] = 0.0f;
-      if (j < k) {
-        int e;
-        if (a.routing == 1) {
-          e = int((int64_t(t) * k + j) % E);
-        } else if (a.routing == 4) {
-          e = valid ? int((int64_t(fmix32(uint32_t(a.token_ids[t]))) + j) % E) : 0;
-        } else {
-          uint64_t best = 0;
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-          best = row_max_u64<LG>(best);
-          e = int(~uint32_t(best));
-        }
-        float sv = 0.0f;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-          if (lg + LG * v == e) {
-            sv = s[v];
-            key[v] = 0;
-            cacc[v] += valid ? 1 : 0;
-          }
-        // the owner's score (the other lanes add zeros: exact)
-        const float ge = row_sum<LG>(sv);
-        isel[j] = e;
-        gsel[j] = ge;
-        gs += ge;
+        for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+        best = row_max_u64<LG>(best);
+        e = int(~uint32_t(best));
       }
+      float sv = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (lg + LG * v == e) {
+          sv = s[v];
+          key[v] = 0;
+          cacc[v] += valid ? 1 : 0;
+        }
+      // the owner's score (the other lanes add zeros: exact)
+      const float ge = row_sum<LG>(sv);
+      if (lg == j) {
+        my_e = e;
+        my_g = ge;
+      }
+      if (j == 0) g0 = ge;
+      if (j == 1) {
+        g1 = ge;
+        e1 = e;
+      }
+      gs += ge;
     }
     // Random second expert (k = 2): keep it iff u < 2 s2 / (s1 + s2); a skipped
     // slot is reported as E + expert and not counted.
     bool skip2 = false;
     if (a.routing == 3 && valid) {
-      skip2 = !(a.uniform[t] < 2.0f * gsel[1] / (gsel[0] + gsel[1]));
+      skip2 = !(a.uniform[t] < 2.0f * g1 / (g0 + g1));
       if (skip2)
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
-          if (lg + LG * v == isel[1]) cacc[v] -= 1;
+          if (lg + LG * v == e1) cacc[v] -= 1;
     }
     if (valid) {
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < k && lg == j) {
-          const float g = a.renorm ? (gsel[j] / gs) * a.gate_scale : gsel[j] * a.gate_scale;
-          a.idx[int64_t(t) * k + j] = isel[j] + ((j == 1 && skip2) ? E : 0);
-          a.gate[int64_t(t) * k + j] = g;
-        }
+      if (lg < k) {
+        const float g = a.renorm ? (my_g / gs) * a.gate_scale : my_g * a.gate_scale;
+        a.idx[int64_t(t) * k + lg] = my_e + ((lg == 1 && skip2) ? E : 0);
+        a.gate[int64_t(t) * k + lg] = g;
       }
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
@@ -450,10 +453,22 @@ __global__ __launch_bounds__(512) void route_from_partials_kernel(RouteArgs a, c
   __shared__ int32_t red_c[NW * EP];
   __shared__ float red_s[2 * NW];
   const int t0 = blockIdx.x * ROUTE_BT;
-  for (int o = threadIdx.x; o < ROUTE_BT * EP; o += blockDim.x) {
-    const int tl = o / EP, e = o - tl * EP;
+  // every load of the block's slab is issued before the first use
+  constexpr int PER = ROUTE_BT * EP / (64 * NW);
+  float v[PER][3];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int o = threadIdx.x + 64 * NW * i;
+    const int tl = o / EP, e = o % EP;
     const float* zr = z3 + int64_t(min(t0 + tl, a.T - 1)) * ldz + e;
-    zs[0][tl][e] = (zr[0] + zr[EP]) + zr[2 * EP];
+    v[i][0] = zr[0];
+    v[i][1] = zr[EP];
+    v[i][2] = zr[2 * EP];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int o = threadIdx.x + 64 * NW * i;
+    zs[0][o / EP][o % EP] = (v[i][0] + v[i][1]) + v[i][2];
   }
   __syncthreads();
   route_epilogue<EP, 1, NW>(a, zs, t0, red_p, red_c, red_s);
