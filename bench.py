@@ -173,7 +173,9 @@ def main():
                                avg_launch_us=t_ffn * 1e6)
     stages = {
         "route": dict(us=t_route * 1e6, GBps=perf.route_bytes(p) / t_route / 1e9,
-                      hbm_frac=perf.route_bytes(p) / t_route / 1e9 / perf.PEAK_HBM_GBS),
+                      hbm_frac=perf.route_bytes(p) / t_route / 1e9 / perf.PEAK_HBM_GBS,
+                      roofline_us=perf.route_roofline_s(p) * 1e6,
+                      roofline_frac=perf.route_roofline_s(p) / t_route),
         "permute": dict(us=t_perm * 1e6, GBps=perf.permute_bytes(p, R) / t_perm / 1e9,
                         hbm_frac=perf.permute_bytes(p, R) / t_perm / 1e9 / perf.PEAK_HBM_GBS),
         "expert_ffn": dict(us=t_ffn * 1e6, TFLOPs=fl / t_ffn / 1e12,

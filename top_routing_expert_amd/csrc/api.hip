@@ -338,13 +338,13 @@ bool router_bwd_mfma(const moe_dims* d, const moe_opts* o) {
 int64_t router_kp(int64_t E) { return cdiv(6 * E, 128) * 128; }   // plane slots, padded
 int64_t router_n3(int64_t E) { return cdiv(3 * E, 128) * 128; }   // dWg's B columns, padded
 // Token chunks of dWg's reduction: about one 256-row output tile per CU, at
-// least 256 tokens per chunk, at most 32 MB of fp32 partials.
+// least 256 tokens per chunk, at most 64 MB of fp32 partials.
 int router_split(const moe_dims* d) {
   const int64_t n3 = router_n3(d->E);
   const int64_t tiles = (d->d / 256) * (n3 / (n3 % 256 == 0 ? 256 : 128));
   int64_t s = cdiv(256, tiles);
   const int64_t by_t = d->T / 256 > 0 ? d->T / 256 : 1;
-  const int64_t by_mem = std::max<int64_t>(1, (int64_t(32) << 20) / (d->d * n3 * 4));
+  const int64_t by_mem = std::max<int64_t>(1, (int64_t(64) << 20) / (d->d * n3 * 4));
   s = std::min(std::min(s, by_t), by_mem);
   return int(s < 1 ? 1 : s);
 }
@@ -384,7 +384,7 @@ BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   b.dHs = c.take(size_t(d->T) * 2 * Fs * eb);
   b.dxs = c.take(Fs ? size_t(d->T) * d->d * 4 : 0);
   b.soff = c.take(2 * 4);
-  b.ssplit_off = c.take(Fs ? size_t(17) * 4 : 0);
+  b.ssplit_off = c.take(Fs ? size_t(2 * 17) * 4 : 0);   // two chunk tables (dWs2, dWs13)
   b.spart = c.take(Fs ? size_t(std::max(shared_split(d, 2 * Fs, d->d) * 2 * Fs * d->d,
                                          shared_split(d, d->d, Fs) * d->d * Fs)) * 4
                       : 0);
@@ -649,12 +649,29 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dO), sv->a, sv->offsets, E, D, F, grads->dW2), ts, st));
   MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dH), sv->x_perm, sv->offsets, E, nu, D, grads->dW13),
                   ts, st));
+  // row-offset tables of the shared expert and the router gradients, in one launch
+  const bool rmfma = router_bwd_mfma(d, o);
+  const int s2 = Fs ? shared_split(d, D, int(Fs)) : 0, s13 = Fs ? shared_split(d, 2 * Fs, D) : 0;
+  const int rs = rmfma ? router_split(d) : 0;
+  {
+    SeqFills f{};
+    if (Fs > 0) {
+      int32_t* so = at<int32_t>(ws, b.ssplit_off);
+      f.add(at<int32_t>(ws, b.soff), 2, int32_t(T), int32_t(T));
+      f.add(so, s2 + 1, int32_t(cdiv(T, s2)), int32_t(T));
+      f.add(so + 17, s13 + 1, int32_t(cdiv(T, s13)), int32_t(T));
+    }
+    if (rmfma) {
+      f.add(at<int32_t>(ws, b.roff1), 2, int32_t(T), int32_t(T));
+      f.add(at<int32_t>(ws, b.roffs), rs + 1, int32_t(cdiv(T, rs)), int32_t(T));
+    }
+    MOE_TRY(launch_fill_seqs(f, st));
+  }
   // shared expert (gate 1 on every token)
   float* dxs = nullptr;
   if (Fs > 0) {
     const int fs = int(Fs);
     int32_t* soff = at<int32_t>(ws, b.soff);
-    MOE_TRY(fill_offsets_1(soff, int32_t(T), st));
     dxs = at<float>(ws, b.dxs);
     MOE_TRY(gemm_on(o, gemm_dgrad(dyx, w->Ws2, 0, soff, 1, T, fs, D, EPI_SWIGLU_BWD,
                                   at<void>(ws, b.dHs), sv->h_shared, 2 * fs, fs),
@@ -666,12 +683,9 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
     // K-grouped GEMM over the chunks), then the chunk partials summed in order
     int32_t* coff = at<int32_t>(ws, b.ssplit_off);
     float* part = at<float>(ws, b.spart);
-    const int s2 = shared_split(d, D, fs), s13 = shared_split(d, 2 * fs, D);
-    MOE_TRY(launch_fill_seq_i32(coff, s2 + 1, int32_t(cdiv(T, s2)), int32_t(T), st));
     MOE_TRY(gemm_on(o, gemm_wgrad(dyx, sv->a_shared, coff, s2, D, fs, part), ts_s, st));
     MOE_TRY(launch_sum_partials(part, s2, int64_t(D) * fs, grads->dWs2, st));
-    MOE_TRY(launch_fill_seq_i32(coff, s13 + 1, int32_t(cdiv(T, s13)), int32_t(T), st));
-    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dHs), x, coff, s13, 2 * fs, D, part), ts_s, st));
+    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dHs), x, coff + 17, s13, 2 * fs, D, part), ts_s, st));
     MOE_TRY(launch_sum_partials(part, s13, int64_t(2) * fs * D, grads->dWs13, st));
   }
   // router: dz from the kept gates' gradient and the two losses; dWg = x^T dz;
@@ -681,14 +695,13 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
                             o->score, o->renorm != 0, o->gate_scale, o->aux_coef, o->z_coef, dz,
                             st));
   float* dxr = at<float>(ws, b.dxr);
-  if (router_bwd_mfma(d, o)) {
-    const int KP = int(router_kp(E)), N3 = int(router_n3(E)), s = router_split(d);
+  if (rmfma) {
+    const int KP = int(router_kp(E)), N3 = int(router_n3(E)), s = rs;
     uint16_t* zp = at<uint16_t>(ws, b.rplanes);     // [T, KP]: dz slots hi mid lo hi hi mid
     uint16_t* wp = at<uint16_t>(ws, b.wplanes);     // [D, KP]: Wg slots hi hi hi mid lo mid
     MOE_TRY(launch_router_planes(dz, T, E, KP, 0x100210u, zp, st));
     MOE_TRY(launch_router_planes(w->Wg, D, E, KP, 0x121000u, wp, st));
     int32_t* off1 = at<int32_t>(ws, b.roff1);
-    MOE_TRY(fill_offsets_1(off1, int32_t(T), st));
     GemmArgs gx{};
     gx.A = zp; gx.B = wp; gx.offsets = off1; gx.G = 1; gx.max_rows = T; gx.N = D; gx.K = KP;
     gx.epi = EPI_STORE_F32; gx.out = dxr; gx.mode = GM_NT;
@@ -696,7 +709,6 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
     // dWg = x^T [hi | mid | lo] per token chunk; chunks and planes summed in order
     int32_t* coff = at<int32_t>(ws, b.roffs);
     float* part = at<float>(ws, b.rpart);
-    MOE_TRY(launch_fill_seq_i32(coff, s + 1, int32_t(cdiv(T, s)), int32_t(T), st));
     GemmArgs gw = gemm_wgrad(x, zp, coff, s, D, N3, part);
     gw.ldb = KP;
     MOE_TRY(launch_grouped_gemm_bf16(gw, st));

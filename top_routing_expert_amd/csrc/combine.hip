@@ -65,6 +65,21 @@ __global__ void fill_seq_i32_kernel(int32_t* out, int n, int32_t step, int32_t c
   if (i < n) out[i] = int32_t(min(int64_t(i) * step, int64_t(cap)));
 }
 
+// Several fill_seq tables in one launch: block y fills table y.
+__global__ void fill_seqs_kernel(SeqFills f) {
+  const int y = blockIdx.y;
+  if (y >= f.count) return;
+  for (int i = threadIdx.x; i < f.n[y]; i += blockDim.x)
+    f.out[y][i] = int32_t(min(int64_t(i) * f.step[y], int64_t(f.cap[y])));
+}
+
+hipError_t launch_fill_seqs(const SeqFills& f, hipStream_t st) {
+  if (f.count <= 0) return hipSuccess;
+  if (f.count > 8) return hipErrorInvalidValue;
+  fill_seqs_kernel<<<dim3(1, unsigned(f.count)), dim3(256), 0, st>>>(f);
+  return hipGetLastError();
+}
+
 __global__ void zero_i32_kernel(int32_t* out, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) out[i] = 0;

@@ -104,6 +104,17 @@ hipError_t launch_fill_i32(int32_t* out, int n, int32_t v0, int32_t v1, int32_t 
 hipError_t launch_zero_i32(int32_t* out, int64_t n, hipStream_t st);
 // out[i] = min(i * step, cap) for i < n
 hipError_t launch_fill_seq_i32(int32_t* out, int n, int32_t step, int32_t cap, hipStream_t st);
+// Up to 8 such tables in one launch.
+struct SeqFills {
+  int32_t* out[8];
+  int n[8];
+  int32_t step[8], cap[8];
+  int count;
+  void add(int32_t* o, int nn, int32_t s, int32_t c) {
+    out[count] = o; n[count] = nn; step[count] = s; cap[count] = c; ++count;
+  }
+};
+hipError_t launch_fill_seqs(const SeqFills& f, hipStream_t st);
 hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, float target,
                               float gamma, hipStream_t st);
 

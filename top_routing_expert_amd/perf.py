@@ -63,6 +63,17 @@ def route_flops(p: Preset) -> float:
     return 2.0 * p.T * p.d * p.E
 
 
+def route_roofline_s(p: Preset) -> float:
+    """Binding roofline of the router: its HBM bytes at the HBM peak, or, for
+    bf16 tokens, the logits contraction as three exact bf16 planes of Wg on the
+    bf16 matrix cores (fp32 tokens: the fp32 vector peak), whichever is longer."""
+    if p.dtype == "bf16":
+        t_math = 3 * route_flops(p) / (PEAK_BF16_TFLOPS * 1e12)
+    else:
+        t_math = route_flops(p) / (PEAK_FP32_TFLOPS * 1e12)
+    return max(route_bytes(p) / (PEAK_HBM_GBS * 1e9), t_math)
+
+
 def route_bytes(p: Preset) -> float:
     """x read once, Wg read once, indices and gates written."""
     return float(p.T * p.d * eb(p) + p.d * p.E * 4 + p.T * p.k * 8)
