@@ -14,7 +14,8 @@ bar is elementwise:
 plus an RMS-level check  rms(got - ref) <= 1e-2 * rms(ref).
 (A flat max-abs <= 2e-2 * rms bar is wrong for experts with a handful of rows:
 replaying the bf16 roundings in fp64 gives 6.9% for a 7-row expert.)
-dWg (fp32 router, reduction over T in fp32) keeps max-abs <= 2e-2 * rms.
+dWg (fp32 router: exact bf16-plane products, fp32 sums over T) keeps
+max-abs <= 1e-4 * rms.
 """
 
 import math
@@ -122,9 +123,15 @@ def _bwd_terms(X, W13e, W2e, dO, F, act):
     return dX, dW13, dW2, adH, np.abs(a)
 
 
-@pytest.mark.parametrize("name", ["c2", "c5"])
-def test_layer_bwd_full_size(name):
-    p = presets.get(name)
+@pytest.mark.parametrize("name,over", [
+    ("c2", {}), ("c5", {}),
+    # ragged token counts through the bf16 router-gradient GEMMs (chunk tails,
+    # one-tile grids) and the logits GEMM (E >= 64)
+    ("c5", dict(T=300, d=256, F=256, F_shared=256)),
+    ("c4", dict(T=333, d=256, F=256, F_shared=0)),
+    ("c2", dict(T=257, d=256, F=512))])
+def test_layer_bwd_full_size(name, over):
+    p = presets.get(name, **over)
     print(f"[{name} bwd] generating inputs", flush=True)
     inp = synth.make_inputs(p, seed=0, with_dy=True)
     x, w, saved, y, g = _train(p, inp)
@@ -152,7 +159,8 @@ def test_layer_bwd_full_size(name):
         m = ros[:, j] >= 0
         dg[m, j] = np.sum(dy[m] * o[ros[m, j]], axis=1)
     dz = orc.router_bwd(p, r["s"], r["z"], idx, counts, dg)
-    e1 = _close(g["dWg"].cpu().numpy(), X64.T @ dz, 2e-2, "dWg")
+    # FP32 router: dWg is formed from exact bf16-plane products with fp32 sums
+    e1 = _close(g["dWg"].cpu().numpy(), X64.T @ dz, 1e-4, "dWg")
     print(f"[{name} bwd] dWg max-abs error / rms {e1:.2e}", flush=True)
 
     # sampled experts: hottest, median, last, and empty ones

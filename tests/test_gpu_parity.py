@@ -87,6 +87,19 @@ def test_route_parity(name):
     print(f"{name}: near-tie flips {nflip}, flagged {int(np.sum(ref['near_tie'] | ref['near_tie_order']))}")
 
 
+@pytest.mark.parametrize("name,over", [("c4", dict(T=333)), ("c5", dict(T=1)), ("c5", dict(T=97)),
+                                       ("c3", dict(T=33))])
+def test_route_parity_ragged(name, over):
+    """Ragged token counts through the logits GEMM (E >= 64) and the fused
+    kernel (E < 64): row tails of the GEMM tile and of the 32-token blocks."""
+    p, inp, x, w = case(name, **over)
+    out = B.route(p, x, w.Wg, w.offset, w.sel_bias)
+    torch.cuda.synchronize()
+    ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                    inp["sel_bias"])
+    check_route(p, out, ref)
+
+
 def test_route_exact_ties_and_nan():
     p = presets.get("c2", T=96)
     x = torch.zeros(96, p.d, dtype=torch.bfloat16, device=DEV)
