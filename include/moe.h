@@ -286,11 +286,13 @@ int moe_router_report(int64_t E, int64_t d, const int32_t* counts, const int32_t
  * (2^(code-127)); a block's shared exponent is floor(log2(max|v|)) minus the
  * element type's largest exponent (2 for E2M1, 8 for E4M3), elements v*2^-X
  * rounded to nearest even and saturated (6, 448).
- * Weights: one scale per 32 consecutive k; codes [G, N, K/2] bytes (low nibble =
- * even k), scales [G, K/32, N].  Activations: one scale per 64 consecutive k
- * (what the FP8 x FP4 matrix instruction pairs per lane); codes [rows, K] bytes,
- * scales [K/64, stride] with stride >= rows (moe_expert_ffn_mx: stride a multiple
- * of 4 and >= rows + 4, the scale arrays 4-byte aligned).
+ * Layouts are k-block-major (a 64-k step of a tile is one contiguous run).
+ * Weights: one scale per 32 consecutive k; codes [G][K/64][N][32] bytes (two
+ * E2M1 values per byte, low nibble = even k), scales [G][K/32][N].
+ * Activations: one scale per 64 consecutive k (what the FP8 x FP4 matrix
+ * instruction pairs per lane); codes [K/64][stride][64] bytes, scales
+ * [K/64][stride], stride >= rows shared by both (moe_expert_ffn_mx: stride a
+ * multiple of 4 and >= rows + 4, the scale arrays 4-byte aligned).
  *
  * Errors (synchronous): MOE_ERR_INVALID_ARG for null or non-16-byte-aligned
  * inputs and codes, K not a multiple of 64, stride < rows, dtype other than
@@ -306,11 +308,12 @@ int moe_mx_quantize_act(const moe_opts* opts, const void* x, int64_t rows, int64
 
 /* moe_expert_ffn_mx: the routed expert FFN of moe_expert_ffn with FP8 activations
  * and MXFP4 weights: h = x W13^T, a = act(h) (SwiGLU with fused gate/up, or exact
- * GELU), a quantised to FP8 in the same pass (aq [max_rows, F], aqs [F/64,
- * a_stride]), out = a W2^T [max_rows, d] fp32.  xq/xs: the rows' FP8 activations
- * (x_stride >= max_rows); W13q/W13s, W2q/W2s: MXFP4 weights [G, n_up, d] and
- * [G, d, F].  Requires d and F multiples of 256; x_stride, a_stride multiples of
- * 4 and >= max_rows + 4.  Allocates nothing. */
+ * GELU), a quantised to FP8 in the same pass (aq [F/64][a_stride][64], aqs
+ * [F/64][a_stride]: the activation layout above), out = a W2^T [max_rows, d]
+ * fp32.  xq/xs: the rows' FP8 activations (row stride x_stride); W13q/W13s,
+ * W2q/W2s: MXFP4 weights of [G, n_up, d] and [G, d, F].  Requires d and F
+ * multiples of 256; x_stride, a_stride multiples of 4 and >= max_rows + 4.
+ * Allocates nothing. */
 int moe_expert_ffn_mx(const moe_dims* dims, const moe_opts* opts, int64_t n_groups,
                       int64_t max_rows, int64_t F, const uint8_t* xq, const uint8_t* xs,
                       int64_t x_stride, const int32_t* offsets, const uint8_t* W13q,

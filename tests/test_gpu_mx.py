@@ -25,8 +25,9 @@ DEV = torch.device("cuda:0")
 
 
 def _w_oracle(codes_u8, scales_u8):
-    """Device MXFP4 layout -> oracle codes [N, K] and scales [N, K/32] of one expert."""
-    c = codes_u8.astype(np.int64)
+    """Device MXFP4 layout of one expert (codes [K/64, N, 32], scales [K/32, N])
+    -> oracle codes [N, K] and scales [N, K/32]."""
+    c = codes_u8.transpose(1, 0, 2).reshape(codes_u8.shape[1], -1).astype(np.int64)
     lo, hi = c & 15, c >> 4
     codes = np.stack([lo, hi], axis=-1).reshape(c.shape[0], -1)
     return codes, scales_u8.T.astype(np.int64)
@@ -57,8 +58,13 @@ def test_mx_quantizers_bit_exact(dtype):
         np.testing.assert_array_equal(gs, rs)
         np.testing.assert_array_equal(gc, rc)
     rc, rs = orc.mx_quantize(x, 64, "e4m3")
-    np.testing.assert_array_equal(xq.cpu().numpy().astype(np.int64), rc)
+    np.testing.assert_array_equal(_act_rows(xq.cpu().numpy())[:300].astype(np.int64), rc)
     np.testing.assert_array_equal(xs.cpu().numpy()[:, :300].T.astype(np.int64), rs)
+
+
+def _act_rows(codes_u8):
+    """Device FP8 activation codes [K/64, stride, 64] -> rows [stride, K]."""
+    return codes_u8.transpose(1, 0, 2).reshape(codes_u8.shape[1], -1)
 
 
 def _grid_step(v, sc):
@@ -89,8 +95,8 @@ def test_expert_ffn_mx_parity(name):
     sizes = np.diff(offsets)
     order = np.argsort(sizes)
     sample = sorted({int(order[-1]), int(order[len(order) // 2]), p.E - 1} - {e for e in range(p.E) if sizes[e] == 0})
-    xq_h, xs_h = xq.cpu().numpy(), xs.cpu().numpy()
-    aq_h, aqs_h = res["aq"].cpu().numpy(), res["aqs"].cpu().numpy()
+    xq_h, xs_h = _act_rows(xq.cpu().numpy()), xs.cpu().numpy()
+    aq_h, aqs_h = _act_rows(res["aq"].cpu().numpy()), res["aqs"].cpu().numpy()
     out_h = res["out"].cpu().numpy()
     W13q_h, W13s_h = W13q.cpu().numpy(), W13s.cpu().numpy()
     W2q_h, W2s_h = W2q.cpu().numpy(), W2s.cpu().numpy()

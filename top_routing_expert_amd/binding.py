@@ -456,10 +456,10 @@ def router_report(counts, n_dropped=None, out_perm=None, offsets=None, d: int = 
 
 # --------------------------------------------------------------------------- MXFP4 experts
 def mx_quantize_weights(p: Preset, w):
-    """moe_mx_quantize_weights: w [G, N, K] -> codes [G, N, K/2] u8, scales [G, K/32, N] u8."""
+    """moe_mx_quantize_weights: w [G, N, K] -> codes [G, K/64, N, 32] u8, scales [G, K/32, N] u8."""
     G, N, K = w.shape
     _need(w, "w", (G, N, K), TORCH_DTYPE[p.dtype], w.device)
-    codes = torch.empty(G, N, K // 2, dtype=torch.uint8, device=w.device)
+    codes = torch.empty(G, K // 64, N, 32, dtype=torch.uint8, device=w.device)
     scales = torch.empty(G, K // 32, N, dtype=torch.uint8, device=w.device)
     _check("moe_mx_quantize_weights", lib().moe_mx_quantize_weights(
         C.byref(opts_of(p)), _ptr(w), G, N, K, _ptr(codes), _ptr(scales), _stream()))
@@ -472,11 +472,11 @@ def mx_stride(rows: int) -> int:
 
 
 def mx_quantize_act(p: Preset, x, stride: Optional[int] = None):
-    """moe_mx_quantize_act: x [rows, K] -> FP8 codes [rows, K] u8, scales [K/64, stride] u8."""
+    """moe_mx_quantize_act: x [rows, K] -> FP8 codes [K/64, stride, 64] u8, scales [K/64, stride] u8."""
     rows, K = x.shape
     stride = rows if stride is None else stride
     _need(x, "x", (rows, K), TORCH_DTYPE[p.dtype], x.device)
-    codes = torch.empty(max(rows, 1), K, dtype=torch.uint8, device=x.device)
+    codes = torch.empty(K // 64, max(stride, 1), 64, dtype=torch.uint8, device=x.device)
     scales = torch.empty(K // 64, max(stride, 1), dtype=torch.uint8, device=x.device)
     _check("moe_mx_quantize_act", lib().moe_mx_quantize_act(
         C.byref(opts_of(p)), _ptr(x), rows, K, stride, _ptr(codes), _ptr(scales), _stream()))
@@ -485,7 +485,8 @@ def mx_quantize_act(p: Preset, x, stride: Optional[int] = None):
 
 def expert_ffn_mx(p: Preset, xq, xs, offsets, W13q, W13s, W2q, W2s, *, max_rows: int,
                   F: Optional[int] = None, act: Optional[str] = None):
-    """moe_expert_ffn_mx: returns dict(out [rows, d] f32, aq [rows, F] u8, aqs [F/64, rows] u8)."""
+    """moe_expert_ffn_mx: returns dict(out [rows, d] f32, aq [F/64, a_stride, 64] u8,
+    aqs [F/64, a_stride] u8)."""
     dev = xq.device
     G = offsets.numel() - 1
     F = p.F if F is None else F
@@ -493,7 +494,7 @@ def expert_ffn_mx(p: Preset, xq, xs, offsets, W13q, W13s, W2q, W2s, *, max_rows:
     rows = max(max_rows, 1)
     a_stride = mx_stride(rows)
     out = torch.empty(rows, p.d, dtype=torch.float32, device=dev)
-    aq = torch.empty(rows, F, dtype=torch.uint8, device=dev)
+    aq = torch.empty(F // 64, a_stride, 64, dtype=torch.uint8, device=dev)
     aqs = torch.empty(F // 64, a_stride, dtype=torch.uint8, device=dev)
     _check("moe_expert_ffn_mx", lib().moe_expert_ffn_mx(
         C.byref(dims_of(q)), C.byref(opts_of(q)), G, max_rows, F, _ptr(xq), _ptr(xs), xs.shape[1],

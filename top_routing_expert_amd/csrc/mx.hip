@@ -16,11 +16,13 @@
 // lane (m, h) holds the activation bytes [16h, 16h+16) and [32+16h, 32+16h+16)
 // of the step, under one scale for all 64 k.
 //
-// Layouts: activations codes [rows, K] bytes, scales [K/64, row_stride];
-// weights codes [G, N, K/2] bytes, scales [G, K/32, N].  The scale layouts put
-// a tile's scales for one k step in one contiguous run, so they travel through
-// the same global->LDS ring as the codes (one uniform load instruction per
-// wave per stage).
+// Layouts, k-block-major so that one 64-k step of a tile is one contiguous
+// run (1 KB per wave load instruction, whole cache lines; row-major codes
+// would give 64-byte activation and 32-byte weight pieces per row):
+// activations codes [K/64][row_stride][64] bytes, scales [K/64][row_stride];
+// weights codes [G][K/64][N][32] bytes (two E2M1 per byte, low nibble = even
+// k), scales [G][K/32][N].  The scales travel through the same global->LDS
+// ring as the codes (one uniform load instruction per wave per stage).
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -91,8 +93,8 @@ __device__ __forceinline__ float block_amax(const float* v, bool live) {
   return m;
 }
 
-// w [rows, K] (rows = G*N, row r = (g, n)) -> codes [rows, K/2] (low nibble
-// first), scales [G][K/32][N].
+// w [rows, K] (rows = G*N, row r = (g, n)) -> codes [G][K/64][N][32] (low
+// nibble first), scales [G][K/32][N].
 __global__ __launch_bounds__(256) void mx4_quantize_kernel(const void* __restrict__ w, bool bf16,
                                                            int64_t rows, int K, int N,
                                                            uint8_t* __restrict__ codes,
@@ -109,14 +111,12 @@ __global__ __launch_bounds__(256) void mx4_quantize_kernel(const void* __restric
   uint32_t packed = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) packed |= e2m1_code(ldexpf(v[i], 127 - sc)) << (4 * i);
-  *reinterpret_cast<uint32_t*>(codes + (r * K + int64_t(c8) * 8) / 2) = packed;
-  if ((c8 & 3) == 0) {
-    const int64_t g = r / N, n = r - g * N;
-    scales[(g * (K / 32) + c8 / 4) * N + n] = uint8_t(sc);
-  }
+  const int64_t g = r / N, n = r - g * N;
+  *reinterpret_cast<uint32_t*>(codes + ((g * (K / 64) + c8 / 8) * N + n) * 32 + (c8 % 8) * 4) = packed;
+  if ((c8 & 3) == 0) scales[(g * (K / 32) + c8 / 4) * N + n] = uint8_t(sc);
 }
 
-// x [rows, K] -> codes [rows, K], scales[kb * stride + r].
+// x [rows, K] -> codes [K/64][stride][64], scales[kb * stride + r].
 __global__ __launch_bounds__(256) void mx8_quantize_kernel(const void* __restrict__ x, bool bf16,
                                                            int64_t rows, int K, int64_t stride,
                                                            uint8_t* __restrict__ codes,
@@ -133,7 +133,8 @@ __global__ __launch_bounds__(256) void mx8_quantize_kernel(const void* __restric
   uint32_t p[2] = {0, 0};
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i / 4] |= e4m3_code(ldexpf(v[i], 127 - sc)) << (8 * (i % 4));
-  *reinterpret_cast<uint2*>(codes + r * K + int64_t(c8) * 8) = make_uint2(p[0], p[1]);
+  *reinterpret_cast<uint2*>(codes + (int64_t(c8 / 8) * stride + r) * 64 + (c8 % 8) * 8) =
+      make_uint2(p[0], p[1]);
   if ((c8 & 7) == 0) scales[int64_t(c8 / 8) * stride + r] = uint8_t(sc);
 }
 
@@ -162,10 +163,10 @@ __device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 2))
 __device__ __forceinline__ int swz_b(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
 
 struct MxArgs {
-  const uint8_t* A;        // [rows, K] FP8 codes
+  const uint8_t* A;        // [K/64][a_stride][64] FP8 codes
   const uint8_t* As;       // [K/64, a_stride] scales
   int64_t a_stride;
-  const uint8_t* B;        // [G, nb_rows, K/2] FP4 codes
+  const uint8_t* B;        // [G][K/64][nb_rows][32] FP4 codes
   const uint8_t* Bs;       // [G, K/32, nb_rows] scales
   int nb_rows;             // rows of each group's B (n_up for the up projection, d for down)
   const int32_t* offsets;
@@ -173,7 +174,7 @@ struct MxArgs {
   int64_t max_rows;
   int N, K, up_off, epi;
   float* out;              // STORE: [rows, N] fp32
-  uint8_t* aq;             // act epilogues: [rows, N] FP8 codes
+  uint8_t* aq;             // act epilogues: [N/64][aq_stride][64] FP8 codes
   uint8_t* aqs;            // [N/64, aq_stride] scales
   int64_t aq_stride;
 };
@@ -233,7 +234,7 @@ void gg_mx_kernel(MxArgs g) {
     const int row = 16 * (w + WV * i) + (l >> 2);
     const int c = (l & 3) ^ swz_a(row);
     const int mr = min(tc.m0 + row, tc.M - 1);
-    a_src[i] = g.A + (int64_t(tc.row0) + mr) * K + 16 * c;
+    a_src[i] = g.A + (int64_t(tc.row0) + mr) * 64 + 16 * c;
   }
   const uint8_t* b_src[B_INS];
   const uint8_t* Bg = g.B + int64_t(tc.grp) * g.nb_rows * (K / 2);
@@ -242,7 +243,7 @@ void gg_mx_kernel(MxArgs g) {
     const int row = 32 * (w + WV * i) + (l >> 1);          // 0 .. NP*BN-1
     const int p = row / BN, col = row % BN;
     const int c = (l & 1) ^ swz_b(row);
-    b_src[i] = Bg + int64_t(p * g.up_off + tc.n0 + col) * (K / 2) + 16 * c;
+    b_src[i] = Bg + int64_t(p * g.up_off + tc.n0 + col) * 32 + 16 * c;
   }
   // scale loads (4 bytes per lane): waves 0 and 1 bring the A scales of the
   // tile's rows from the aligned start a4 (a_off = misalignment); the next
@@ -254,14 +255,15 @@ void gg_mx_kernel(MxArgs g) {
   const int a_off = int(a_first - a4);
   const int64_t a_last = (g.a_stride & ~int64_t(3)) - 4;   // last whole dword of a scale row
   const uint8_t* Bsg = g.Bs + int64_t(tc.grp) * (K / 32) * g.nb_rows;
+  const int64_t a_kstep = g.a_stride * 64, b_kstep = int64_t(g.nb_rows) * 32;   // bytes per 64-k block
   auto issue = [&](int stage, int ks) {
     char* base = lds + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i)
-      lds_load(a_src[i] + 64 * ks, base + (w + WV * i) * 1024, 16);
+      lds_load(a_src[i] + a_kstep * ks, base + (w + WV * i) * 1024, 16);
 #pragma unroll
     for (int i = 0; i < B_INS; ++i)
-      lds_load(b_src[i] + 32 * ks, base + A_BYTES + (w + WV * i) * 1024, 16);
+      lds_load(b_src[i] + b_kstep * ks, base + A_BYTES + (w + WV * i) * 1024, 16);
     char* sb = base + A_BYTES + B_BYTES;
     if (w < nA) {
       const int64_t o = min(a4 + 256 * w + 4 * l, a_last);
@@ -377,7 +379,7 @@ void gg_mx_kernel(MxArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk |= e4m3_code(ldexpf(a[i], 127 - sc)) << (8 * i);
         if (ok) {
-          *reinterpret_cast<uint32_t*>(g.aq + row * g.N + n) = pk;
+          *reinterpret_cast<uint32_t*>(g.aq + (int64_t(n / 64) * g.aq_stride + row) * 64 + (n % 64)) = pk;
           if ((l & 15) == 0) g.aqs[int64_t(n / 64) * g.aq_stride + row] = uint8_t(sc);
         }
       }
