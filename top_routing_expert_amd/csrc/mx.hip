@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void mx8_quantize_kernel(const void* __restric
 
 // ---------------------------------------------------------------- grouped GEMM
 constexpr int MX_BN = 256;       // tile columns: 4 waves along n, 64 columns each
-constexpr int MX_NS = 4;         // stages of 64 k
+constexpr int MX_NS = 6;         // ring slots, one 64-k stage each
 
 __device__ uint4 g_zero_mx[16];  // a harmless source for the padding scale loads
 
@@ -290,18 +290,12 @@ void gg_mx_kernel(MxArgs g) {
   const int fr = l & 31, fh = l >> 5;
   const int krot = KS > 0 ? tile % KS : 0;
   auto kidx = [&](int j) { const int kn = j + krot; return kn < KS ? kn : kn - KS; };
-#pragma unroll
-  for (int j = 0; j < MX_NS - 1; ++j)
-    if (j < KS) issue(j, kidx(j));
-  int cur = 0, nxt = MX_NS - 1;
-  for (int kt = 0; kt < KS; ++kt) {
-    const int after = min(MX_NS - 2, KS - 1 - kt);
-    if (after >= 2) mx_wait_vmcnt<2 * INS>();
-    else if (after == 1) mx_wait_vmcnt<INS>();
-    else mx_wait_vmcnt<0>();
-    mx_barrier();
-    if (kt + MX_NS - 1 < KS) issue(nxt, kidx(kt + MX_NS - 1));
-    const char* base = lds + cur * STAGE;
+  // Ring of MX_NS = 6 slots (stage s in slot s % 6) walked in steps of two
+  // 64-k stages: one wait and one barrier per 128 k, the next two stages
+  // issued into the slots the previous step released, four stages in flight.
+  // K is a multiple of 256, so KS is even.
+  auto compute = [&](int slot) {
+    const char* base = lds + slot * STAGE;
     const char* Ab = base;
     const char* Bb = base + A_BYTES;
     const uint8_t* Sa = reinterpret_cast<const uint8_t*>(base + A_BYTES + B_BYTES);
@@ -331,9 +325,21 @@ void gg_mx_kernel(MxArgs g) {
           acc[p][mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               af[mi], bf, acc[p][mi][ni], 0, 4, 0, sa[mi], 0, sb);
       }
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j < KS) issue(j, kidx(j));
+  for (int kt = 0; kt < KS; kt += 2) {
+    // stages kt, kt+1 have landed once at most the loads of the stages issued
+    // after them are outstanding (loads complete in order)
+    if (min(KS, kt + 4) - (kt + 2) >= 2) mx_wait_vmcnt<2 * INS>();
+    else mx_wait_vmcnt<0>();
+    mx_barrier();
+    if (kt + 4 < KS) issue((kt + 4) % MX_NS, kidx(kt + 4));
+    if (kt + 5 < KS) issue((kt + 5) % MX_NS, kidx(kt + 5));
+    compute(kt % MX_NS);
+    compute((kt + 1) % MX_NS);
     __builtin_amdgcn_sched_barrier(0);
-    cur = cur + 1 == MX_NS ? 0 : cur + 1;
-    nxt = nxt + 1 == MX_NS ? 0 : nxt + 1;
   }
   __syncthreads();
 
