@@ -119,6 +119,23 @@ def main():
     tok_s = p.T / dt
     log(f"[bench] {dt * 1e3:.3f} ms/step, {tok_s / 1e6:.2f} M tokens/s")
 
+    # cold caches: a 512 MB write before each step evicts L2 and the 256 MB
+    # Infinity Cache; HIP events bracket the step alone; median over the steps
+    flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        torch.cuda._sleep(int(2.4e9 * 3e-3))   # ~3 ms: the host enqueues the step meanwhile
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    cold_ms = float(np.median(cold))
+    log(f"[bench] cold caches: {cold_ms:.3f} ms/step (median of {len(cold)})")
+
     # ---- per-step rates, HIP events on the current stream (the library's stream)
     ws = B.Workspace(dev)
     y, st = B.layer_fwd(p, w, x, stats=True, ri=ri, ws=ws)
@@ -248,6 +265,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": dt * 1e3,
+        "cold_cache_ms_per_step": cold_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
