@@ -228,7 +228,13 @@ int moe_combine(const moe_dims* dims, const float* out_perm, const int32_t* row_
 
 /* Whole forward: route, dispatch, routed expert FFNs, shared expert, combine.
  * y [T,d] fp32 (the caller adds the residual x).  ri, saved and stats nullable
- * (ri as for moe_route). */
+ * (ri as for moe_route).
+ * Streams (moe_layer_fwd and moe_layer_bwd): branches that do not depend on
+ * each other (the shared expert; in the backward also the router gradients) run
+ * on an internal stream of the current device, forked from `stream` and joined
+ * back to it with events before the call returns, so every result is ordered
+ * on `stream` as for a single-stream call.  That stream and its two events are
+ * created on the first call on a device and kept until the process ends. */
 int moe_layer_fwd(const moe_dims* dims, const moe_opts* opts, const moe_weights* w,
                   const moe_router_inputs* ri, const void* x, float* y, moe_saved* saved,
                   moe_stats* stats, void* ws, size_t ws_bytes, void* stream);

@@ -9,6 +9,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 using namespace moe;
 
@@ -306,6 +307,41 @@ hipError_t fill_offsets_1(int32_t* off, int32_t rows, hipStream_t st) {
   return launch_fill_i32(off, 2, 0, rows, 0, 0, st);
 }
 
+// A second stream per device for the layer's independent branches (the shared
+// expert, the router gradients), forked from and joined back to the caller's
+// stream with events; created on first use and kept until the process ends.
+// Record-and-wait pairs run under one lock, so calls from several host
+// threads cannot interleave them.
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+std::mutex g_side_mu;
+SideStream g_side[64] = {};
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream& sd = g_side[dev];
+  if (!sd.s) {
+    if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
+  }
+  *out = &sd;
+  return hipSuccess;
+}
+
+// Work enqueued on `to` from now on waits for everything enqueued on `from` so far.
+hipError_t stream_wait(hipStream_t to, hipStream_t from, hipEvent_t ev) {
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  hipError_t e = hipEventRecord(ev, from);
+  return e == hipSuccess ? hipStreamWaitEvent(to, ev, 0) : e;
+}
+
 // ---- backward workspace ------------------------------------------------------
 // k-chunks of the T-reduction of dWg: enough 64x64 tiles x chunks to fill the
 // chip (about 2048 workgroups), at most 64 chunks and at least 128 tokens each.
@@ -567,26 +603,38 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
                      : (stats && stats->losses) ? stats->losses
                      : want_losses ? at<float>(ws, f.losses) : nullptr;
 
-  s = do_route(d, o, x, w->Wg, w->logit_offset, w->sel_bias, ri, idx, gate, nullptr,
-               sv ? sv->logits : nullptr, nullptr, losses, stats ? stats->n_nonfinite : nullptr,
-               sv ? sv->noise_logits : nullptr, ws, f.route, st);
-  if (s) return s;
-  s = do_permute(d, o, x, idx, counts, offsets, ros, tor, xperm, stats ? stats->n_dropped : nullptr,
-                 ws, f.perm, st);
-  if (s) return s;
-  s = do_ffn(o, d->d, d->E, d->T * d->k, d->F, o->act, xperm, offsets, w->W13, w->W2,
-             sv ? sv->h : nullptr, abuf, obuf, ws, f.ffn, st);
-  if (s) return s;
+  // the shared expert depends only on x: it runs on the side stream while the
+  // router, dispatch and routed experts run on the caller's
+  SideStream* side = nullptr;
   float* shared = nullptr;
+  // an error after the fork still joins the side stream before returning
+  auto joined = [&](int code) {
+    if (side) stream_wait(st, side->s, side->join);
+    return code;
+  };
   if (d->F_shared > 0) {
+    MOE_TRY(side_stream(&side));
+    MOE_TRY(stream_wait(side->s, st, side->fork));
     int32_t* soff = at<int32_t>(ws, f.shared_off);
-    MOE_TRY(fill_offsets_1(soff, int32_t(d->T), st));
+    if (hipError_t e = fill_offsets_1(soff, int32_t(d->T), side->s); e != hipSuccess)
+      return joined(hip_status(e));
     shared = at<float>(ws, f.os);
     s = do_ffn(o, d->d, 1, d->T, d->F_shared, MOE_ACT_SWIGLU, x, soff, w->Ws13, w->Ws2,
                sv ? sv->h_shared : nullptr, sv ? sv->a_shared : at<void>(ws, f.as), shared, ws,
-               f.ffn_shared, st);
-    if (s) return s;
+               f.ffn_shared, side->s);
+    if (s) return joined(s);
   }
+  s = do_route(d, o, x, w->Wg, w->logit_offset, w->sel_bias, ri, idx, gate, nullptr,
+               sv ? sv->logits : nullptr, nullptr, losses, stats ? stats->n_nonfinite : nullptr,
+               sv ? sv->noise_logits : nullptr, ws, f.route, st);
+  if (s) return joined(s);
+  s = do_permute(d, o, x, idx, counts, offsets, ros, tor, xperm, stats ? stats->n_dropped : nullptr,
+                 ws, f.perm, st);
+  if (s) return joined(s);
+  s = do_ffn(o, d->d, d->E, d->T * d->k, d->F, o->act, xperm, offsets, w->W13, w->W2,
+             sv ? sv->h : nullptr, abuf, obuf, ws, f.ffn, st);
+  if (s) return joined(s);
+  if (side) MOE_TRY(stream_wait(st, side->s, side->join));
   MOE_TRY(launch_combine(obuf, ros, gate, shared, int(d->T), int(d->k), int(d->d), y, st));
   if (stats) {
     if (stats->counts) MOE_TRY(hipMemcpyAsync(stats->counts, counts, size_t(d->E) * 4,
@@ -636,19 +684,6 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   void* dyx = Fs ? at<void>(ws, b.dyx) : nullptr;
   MOE_TRY(launch_combine_bwd(dy, sv->o, sv->row_of_slot, sv->topk_gate, T, k, D, bf16,
                              at<void>(ws, b.dO), at<float>(ws, b.dg), dyx, st));
-  // routed experts, data gradients: dA = dO W2 (+ activation backward) -> dH; dXp = dH W13
-  MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dO), w->W2, int64_t(D) * F, sv->offsets, E, R, F, D,
-                                swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, at<void>(ws, b.dH), sv->h,
-                                nu, swiglu ? F : 0),
-                  ts, st));
-  MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dH), w->W13, int64_t(nu) * D, sv->offsets, E, R, D,
-                                nu, EPI_STORE_F32, at<void>(ws, b.dXp), nullptr, 0, 0),
-                  ts, st));
-  // routed experts, weight gradients over each expert's rows:
-  // dW2[e] = dO_e^T a_e, dW13[e] = dH_e^T x_e
-  MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dO), sv->a, sv->offsets, E, D, F, grads->dW2), ts, st));
-  MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dH), sv->x_perm, sv->offsets, E, nu, D, grads->dW13),
-                  ts, st));
   // row-offset tables of the shared expert and the router gradients, in one launch
   const bool rmfma = router_bwd_mfma(d, o);
   const int s2 = Fs ? shared_split(d, D, int(Fs)) : 0, s13 = Fs ? shared_split(d, 2 * Fs, D) : 0;
@@ -667,70 +702,100 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
     }
     MOE_TRY(launch_fill_seqs(f, st));
   }
-  // shared expert (gate 1 on every token)
+  // The shared expert's and the router's gradients depend only on combine
+  // backward's outputs: they run on the side stream while the routed experts'
+  // GEMMs run on the caller's; the join precedes the unpermute-sum.
   float* dxs = nullptr;
-  if (Fs > 0) {
-    const int fs = int(Fs);
-    int32_t* soff = at<int32_t>(ws, b.soff);
-    dxs = at<float>(ws, b.dxs);
-    MOE_TRY(gemm_on(o, gemm_dgrad(dyx, w->Ws2, 0, soff, 1, T, fs, D, EPI_SWIGLU_BWD,
-                                  at<void>(ws, b.dHs), sv->h_shared, 2 * fs, fs),
-                    ts_s, st));
-    MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dHs), w->Ws13, 0, soff, 1, T, D, 2 * fs,
-                                  EPI_STORE_F32, dxs, nullptr, 0, 0),
-                    ts_s, st));
-    // weight gradients: the T-reduction split into equal token chunks (one
-    // K-grouped GEMM over the chunks), then the chunk partials summed in order
-    int32_t* coff = at<int32_t>(ws, b.ssplit_off);
-    float* part = at<float>(ws, b.spart);
-    MOE_TRY(gemm_on(o, gemm_wgrad(dyx, sv->a_shared, coff, s2, D, fs, part), ts_s, st));
-    MOE_TRY(launch_sum_partials(part, s2, int64_t(D) * fs, grads->dWs2, st));
-    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dHs), x, coff + 17, s13, 2 * fs, D, part), ts_s, st));
-    MOE_TRY(launch_sum_partials(part, s13, int64_t(2) * fs * D, grads->dWs13, st));
-  }
-  // router: dz from the kept gates' gradient and the two losses; dWg = x^T dz;
-  // dx_router = dz Wg^T
-  float* dz = at<float>(ws, b.dz);
-  MOE_TRY(launch_router_bwd(sv->logits, sv->topk_idx, at<float>(ws, b.dg), sv->counts, T, E, k,
-                            o->score, o->renorm != 0, o->gate_scale, o->aux_coef, o->z_coef, dz,
-                            st));
   float* dxr = at<float>(ws, b.dxr);
-  if (rmfma) {
-    const int KP = int(router_kp(E)), N3 = int(router_n3(E)), s = rs;
-    uint16_t* zp = at<uint16_t>(ws, b.rplanes);     // [T, KP]: dz slots hi mid lo hi hi mid
-    uint16_t* wp = at<uint16_t>(ws, b.wplanes);     // [D, KP]: Wg slots hi hi hi mid lo mid
-    MOE_TRY(launch_router_planes(dz, T, E, KP, 0x100210u, zp, st));
-    MOE_TRY(launch_router_planes(w->Wg, D, E, KP, 0x121000u, wp, st));
-    int32_t* off1 = at<int32_t>(ws, b.roff1);
-    GemmArgs gx{};
-    gx.A = zp; gx.B = wp; gx.offsets = off1; gx.G = 1; gx.max_rows = T; gx.N = D; gx.K = KP;
-    gx.epi = EPI_STORE_F32; gx.out = dxr; gx.mode = GM_NT;
-    MOE_TRY(launch_grouped_gemm_bf16(gx, st));
-    // dWg = x^T [hi | mid | lo] per token chunk; chunks and planes summed in order
-    int32_t* coff = at<int32_t>(ws, b.roffs);
-    float* part = at<float>(ws, b.rpart);
-    GemmArgs gw = gemm_wgrad(x, zp, coff, s, D, N3, part);
-    gw.ldb = KP;
-    MOE_TRY(launch_grouped_gemm_bf16(gw, st));
-    MOE_TRY(launch_dwg_reduce(part, s, D, N3, E, grads->dWg, st));
-  } else if (noisy) {
-    MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
-                                at<float>(ws, b.dwg_part), grads->dWg, st));
-    // H = z + noise * softplus(zn): dzn = dz * noise * sigmoid(zn);
-    // dW_noise = x^T dzn; dx_router = dz Wg^T + dzn W_noise^T
-    float* dzn = at<float>(ws, b.dzn);
-    float* part = dxr + int64_t(T) * D;
-    MOE_TRY(launch_noise_grad(dz, ri->noise, sv->noise_logits, int64_t(T) * E, dzn, st));
-    MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dzn, E, 1, D, E, T, dwg_split(d),
-                                at<float>(ws, b.dwn_part), grads->dW_noise, st));
-    MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, st));
-    MOE_TRY(launch_strided_gemm(dzn, false, E, 1, ri->W_noise, 1, E, T, D, E, 1, part, nullptr, st));
-    MOE_TRY(launch_sum_partials(dxr, 2, int64_t(T) * D, dxr, st));
-  } else {
-    MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
-                                at<float>(ws, b.dwg_part), grads->dWg, st));
-    MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, st));
-  }
+  auto side_branch = [&](hipStream_t bs) -> int {
+    // shared expert (gate 1 on every token)
+    if (Fs > 0) {
+      const int fs = int(Fs);
+      int32_t* soff = at<int32_t>(ws, b.soff);
+      dxs = at<float>(ws, b.dxs);
+      MOE_TRY(gemm_on(o, gemm_dgrad(dyx, w->Ws2, 0, soff, 1, T, fs, D, EPI_SWIGLU_BWD,
+                                    at<void>(ws, b.dHs), sv->h_shared, 2 * fs, fs),
+                      ts_s, bs));
+      MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dHs), w->Ws13, 0, soff, 1, T, D, 2 * fs,
+                                    EPI_STORE_F32, dxs, nullptr, 0, 0),
+                      ts_s, bs));
+      // weight gradients: the T-reduction split into equal token chunks (one
+      // K-grouped GEMM over the chunks), then the chunk partials summed in order
+      int32_t* coff = at<int32_t>(ws, b.ssplit_off);
+      float* part = at<float>(ws, b.spart);
+      MOE_TRY(gemm_on(o, gemm_wgrad(dyx, sv->a_shared, coff, s2, D, fs, part), ts_s, bs));
+      MOE_TRY(launch_sum_partials(part, s2, int64_t(D) * fs, grads->dWs2, bs));
+      MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dHs), x, coff + 17, s13, 2 * fs, D, part), ts_s, bs));
+      MOE_TRY(launch_sum_partials(part, s13, int64_t(2) * fs * D, grads->dWs13, bs));
+    }
+    // router: dz from the kept gates' gradient and the two losses; dWg = x^T dz;
+    // dx_router = dz Wg^T
+    float* dz = at<float>(ws, b.dz);
+    MOE_TRY(launch_router_bwd(sv->logits, sv->topk_idx, at<float>(ws, b.dg), sv->counts, T, E, k,
+                              o->score, o->renorm != 0, o->gate_scale, o->aux_coef, o->z_coef, dz,
+                              bs));
+    if (rmfma) {
+      const int KP = int(router_kp(E)), N3 = int(router_n3(E)), s = rs;
+      uint16_t* zp = at<uint16_t>(ws, b.rplanes);     // [T, KP]: dz slots hi mid lo hi hi mid
+      uint16_t* wp = at<uint16_t>(ws, b.wplanes);     // [D, KP]: Wg slots hi hi hi mid lo mid
+      MOE_TRY(launch_router_planes(dz, T, E, KP, 0x100210u, zp, bs));
+      MOE_TRY(launch_router_planes(w->Wg, D, E, KP, 0x121000u, wp, bs));
+      int32_t* off1 = at<int32_t>(ws, b.roff1);
+      GemmArgs gx{};
+      gx.A = zp; gx.B = wp; gx.offsets = off1; gx.G = 1; gx.max_rows = T; gx.N = D; gx.K = KP;
+      gx.epi = EPI_STORE_F32; gx.out = dxr; gx.mode = GM_NT;
+      MOE_TRY(launch_grouped_gemm_bf16(gx, bs));
+      // dWg = x^T [hi | mid | lo] per token chunk; chunks and planes summed in order
+      int32_t* coff = at<int32_t>(ws, b.roffs);
+      float* part = at<float>(ws, b.rpart);
+      GemmArgs gw = gemm_wgrad(x, zp, coff, s, D, N3, part);
+      gw.ldb = KP;
+      MOE_TRY(launch_grouped_gemm_bf16(gw, bs));
+      MOE_TRY(launch_dwg_reduce(part, s, D, N3, E, grads->dWg, bs));
+    } else if (noisy) {
+      MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
+                                  at<float>(ws, b.dwg_part), grads->dWg, bs));
+      // H = z + noise * softplus(zn): dzn = dz * noise * sigmoid(zn);
+      // dW_noise = x^T dzn; dx_router = dz Wg^T + dzn W_noise^T
+      float* dzn = at<float>(ws, b.dzn);
+      float* part = dxr + int64_t(T) * D;
+      MOE_TRY(launch_noise_grad(dz, ri->noise, sv->noise_logits, int64_t(T) * E, dzn, bs));
+      MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dzn, E, 1, D, E, T, dwg_split(d),
+                                  at<float>(ws, b.dwn_part), grads->dW_noise, bs));
+      MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, bs));
+      MOE_TRY(launch_strided_gemm(dzn, false, E, 1, ri->W_noise, 1, E, T, D, E, 1, part, nullptr, bs));
+      MOE_TRY(launch_sum_partials(dxr, 2, int64_t(T) * D, dxr, bs));
+    } else {
+      MOE_TRY(launch_strided_gemm(x, bf16, 1, D, dz, E, 1, D, E, T, dwg_split(d),
+                                  at<float>(ws, b.dwg_part), grads->dWg, bs));
+      MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, bs));
+    }
+    return MOE_OK;
+  };
+  auto routed_branch = [&]() -> int {
+    // routed experts, data gradients: dA = dO W2 (+ activation backward) -> dH; dXp = dH W13
+    MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dO), w->W2, int64_t(D) * F, sv->offsets, E, R, F, D,
+                                  swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, at<void>(ws, b.dH), sv->h,
+                                  nu, swiglu ? F : 0),
+                    ts, st));
+    MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dH), w->W13, int64_t(nu) * D, sv->offsets, E, R, D,
+                                  nu, EPI_STORE_F32, at<void>(ws, b.dXp), nullptr, 0, 0),
+                    ts, st));
+    // routed experts, weight gradients over each expert's rows:
+    // dW2[e] = dO_e^T a_e, dW13[e] = dH_e^T x_e
+    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dO), sv->a, sv->offsets, E, D, F, grads->dW2), ts, st));
+    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dH), sv->x_perm, sv->offsets, E, nu, D, grads->dW13),
+                    ts, st));
+    return MOE_OK;
+  };
+  SideStream* side = nullptr;
+  MOE_TRY(side_stream(&side));
+  MOE_TRY(stream_wait(side->s, st, side->fork));
+  const int e_side = side_branch(side->s);
+  const int e_main = routed_branch();
+  MOE_TRY(stream_wait(st, side->s, side->join));
+  if (e_side) return e_side;
+  if (e_main) return e_main;
   MOE_TRY(launch_unpermute_sum(at<float>(ws, b.dXp), sv->row_of_slot, dxs, dxr, T, k, D, dx, st));
   return MOE_OK;
 }
