@@ -49,27 +49,46 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     dot[j] = 0.0f;
   }
   const float4* dyr = reinterpret_cast<const float4*>(dy + int64_t(t) * d);
-  for (int c = l; c < (d >> 2); c += 64) {
-    const float4 v = dyr[c];
+  const int n4 = d >> 2;
+  // four 16-byte chunks per lane per pass, all loads of a pass issued before use
+  for (int c0 = l; c0 < n4; c0 += 256) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = c0 + 64 * u < n4 ? dyr[c0 + 64 * u] : make_float4(0.f, 0.f, 0.f, 0.f);
     if (dy_x) {
-      if constexpr (BF16)
-        reinterpret_cast<uint2*>(static_cast<uint16_t*>(dy_x) + int64_t(t) * d)[c] =
-            make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
-      else
-        reinterpret_cast<float4*>(static_cast<float*>(dy_x) + int64_t(t) * d)[c] = v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 64 * u;
+        if (c >= n4) continue;
+        if constexpr (BF16)
+          reinterpret_cast<uint2*>(static_cast<uint16_t*>(dy_x) + int64_t(t) * d)[c] =
+              make_uint2(pack_bf2(v[u].x, v[u].y), pack_bf2(v[u].z, v[u].w));
+        else
+          reinterpret_cast<float4*>(static_cast<float*>(dy_x) + int64_t(t) * d)[c] = v[u];
+      }
     }
 #pragma unroll
     for (int j = 0; j < BWD_KMAX; ++j) {
       if (rows[j] < 0) continue;
-      const float4 ov = reinterpret_cast<const float4*>(o + int64_t(rows[j]) * d)[c];
-      dot[j] += v.x * ov.x + v.y * ov.y + v.z * ov.z + v.w * ov.w;
+      const float4* orow = reinterpret_cast<const float4*>(o + int64_t(rows[j]) * d);
+      float4 ov[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        ov[u] = c0 + 64 * u < n4 ? orow[c0 + 64 * u] : make_float4(0.f, 0.f, 0.f, 0.f);
       const float g = gs[j];
-      if constexpr (BF16)
-        reinterpret_cast<uint2*>(static_cast<uint16_t*>(dO) + int64_t(rows[j]) * d)[c] =
-            make_uint2(pack_bf2(g * v.x, g * v.y), pack_bf2(g * v.z, g * v.w));
-      else
-        reinterpret_cast<float4*>(static_cast<float*>(dO) + int64_t(rows[j]) * d)[c] =
-            make_float4(g * v.x, g * v.y, g * v.z, g * v.w);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 64 * u;
+        if (c >= n4) continue;
+        dot[j] += v[u].x * ov[u].x + v[u].y * ov[u].y + v[u].z * ov[u].z + v[u].w * ov[u].w;
+        if constexpr (BF16)
+          reinterpret_cast<uint2*>(static_cast<uint16_t*>(dO) + int64_t(rows[j]) * d)[c] =
+              make_uint2(pack_bf2(g * v[u].x, g * v[u].y), pack_bf2(g * v[u].z, g * v[u].w));
+        else
+          reinterpret_cast<float4*>(static_cast<float*>(dO) + int64_t(rows[j]) * d)[c] =
+              make_float4(g * v[u].x, g * v[u].y, g * v[u].z, g * v[u].w);
+      }
     }
   }
 #pragma unroll
