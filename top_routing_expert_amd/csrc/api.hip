@@ -609,7 +609,8 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   float* shared = nullptr;
   // an error after the fork still joins the side stream before returning
   auto joined = [&](int code) {
-    if (side) stream_wait(st, side->s, side->join);
+    // the join's own status cannot replace the error being reported
+    if (side) (void)stream_wait(st, side->s, side->join);
     return code;
   };
   if (d->F_shared > 0) {

@@ -93,9 +93,10 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   }
 #pragma unroll
   for (int j = 0; j < BWD_KMAX; ++j) {
-    if (j >= k) break;
-    const float s = wave_sum(dot[j]);
-    if (l == 0) dg[int64_t(t) * k + j] = rows[j] >= 0 ? s : 0.0f;
+    if (j < k) {  // k is uniform over the wave
+      const float s = wave_sum(dot[j]);
+      if (l == 0) dg[int64_t(t) * k + j] = rows[j] >= 0 ? s : 0.0f;
+    }
   }
 }
 
