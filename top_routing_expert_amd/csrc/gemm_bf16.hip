@@ -519,11 +519,10 @@ static void launch_rows_np1(const GemmArgs& g, bool bm256, bool bn256, hipStream
 // (fewer re-reads of each weight panel), else 128; 256-column tiles when that
 // still gives three tiles per four CUs.  Where 256 x 256 would not (and there
 // are several groups), the tile keeps its 256 columns and drops to 128 rows:
-// the two row halves of an
-// expert share each weight panel through L2, and each CU streams twice the
-// weight bytes per stage (32 experts x 245 rows, K = 4096, N = 1024: 85 vs
-// 90 us against 256 x 128, the data gradient 116 vs 119 us).  K-grouped mode: 256 x 256 when the
-// output dimensions allow it.
+// the two row halves of an expert share each weight panel through L2, and
+// each CU streams twice the weight bytes per stage (32 experts x 245 rows,
+// K = 4096, N = 1024: 85 vs 90 us against 256 x 128; the data gradient 116 vs
+// 119 us).  K-grouped mode: 256 x 256 when the output dimensions allow it.
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.G == 0) return hipSuccess;
   if (g.mode == GM_KGROUP) {
