@@ -792,8 +792,18 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   SideStream* side = nullptr;
   MOE_TRY(side_stream(&side));
   MOE_TRY(stream_wait(side->s, st, side->fork));
-  const int e_side = side_branch(side->s);
-  const int e_main = routed_branch();
+  // Launch order: with a shared expert the side branch holds GEMMs of its own
+  // and is launched first; without one it is only the router's gradients, and
+  // the routed branch goes first so the caller's stream, which the device has
+  // usually drained by then, gets its next kernel without waiting for them.
+  int e_main = 0, e_side = 0;
+  if (Fs > 0) {
+    e_side = side_branch(side->s);
+    e_main = routed_branch();
+  } else {
+    e_main = routed_branch();
+    e_side = side_branch(side->s);
+  }
   MOE_TRY(stream_wait(st, side->s, side->join));
   if (e_side) return e_side;
   if (e_main) return e_main;
