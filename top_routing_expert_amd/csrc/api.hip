@@ -703,9 +703,12 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
     }
     MOE_TRY(launch_fill_seqs(f, st));
   }
-  // The shared expert's and the router's gradients depend only on combine
-  // backward's outputs: they run on the side stream while the routed experts'
-  // GEMMs run on the caller's; the join precedes the unpermute-sum.
+  // The shared expert's and the router's gradients and the routed dW2 depend
+  // only on combine backward's outputs: they run on the side stream while the
+  // routed experts' data gradients and dW13 run on the caller's; the join
+  // precedes the unpermute-sum.  dW2 is store-bound and the data gradients
+  // read weights and multiply, so the two streams overlap well (4096 tokens,
+  // d = 4096, 8 experts of width 14336, top-2: 11.8 -> 10.9 ms per step).
   float* dxs = nullptr;
   float* dxr = at<float>(ws, b.dxr);
   auto side_branch = [&](hipStream_t bs) -> int {
@@ -771,6 +774,10 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
                                   at<float>(ws, b.dwg_part), grads->dWg, bs));
       MOE_TRY(launch_strided_gemm(dz, false, E, 1, w->Wg, 1, E, T, D, E, 1, dxr, nullptr, bs));
     }
+    // routed experts' dW2[e] = dO_e^T a_e needs only combine backward's dO: its
+    // fp32 stores run here, beside the data gradients' weight reads and
+    // products (the K-grouped mode reads no tile table)
+    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dO), sv->a, sv->offsets, E, D, F, grads->dW2), ts_s, bs));
     return MOE_OK;
   };
   auto routed_branch = [&]() -> int {
@@ -782,9 +789,7 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
     MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dH), w->W13, int64_t(nu) * D, sv->offsets, E, R, D,
                                   nu, EPI_STORE_F32, at<void>(ws, b.dXp), nullptr, 0, 0),
                     ts, st));
-    // routed experts, weight gradients over each expert's rows:
-    // dW2[e] = dO_e^T a_e, dW13[e] = dH_e^T x_e
-    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dO), sv->a, sv->offsets, E, D, F, grads->dW2), ts, st));
+    // routed experts, weight gradient over each expert's rows: dW13[e] = dH_e^T x_e
     MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dH), sv->x_perm, sv->offsets, E, nu, D, grads->dW13),
                     ts, st));
     return MOE_OK;
@@ -792,10 +797,10 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   SideStream* side = nullptr;
   MOE_TRY(side_stream(&side));
   MOE_TRY(stream_wait(side->s, st, side->fork));
-  // Launch order: with a shared expert the side branch holds GEMMs of its own
-  // and is launched first; without one it is only the router's gradients, and
-  // the routed branch goes first so the caller's stream, which the device has
-  // usually drained by then, gets its next kernel without waiting for them.
+  // Launch order: with a shared expert the side branch holds its GEMMs and is
+  // launched first; without one it holds only the router's gradients and dW2,
+  // and the routed branch goes first so the caller's stream, which the device
+  // has usually drained by then, gets its next kernel without waiting for them.
   int e_main = 0, e_side = 0;
   if (Fs > 0) {
     e_side = side_branch(side->s);
