@@ -230,7 +230,8 @@ int moe_combine(const moe_dims* dims, const float* out_perm, const int32_t* row_
  * y [T,d] fp32 (the caller adds the residual x).  ri, saved and stats nullable
  * (ri as for moe_route).
  * Streams (moe_layer_fwd and moe_layer_bwd): branches that do not depend on
- * each other (the shared expert; in the backward also the router gradients) run
+ * each other (the shared expert; in the backward also the router gradients and
+ * the routed experts' dW2) run
  * on an internal stream of the current device, forked from `stream` and joined
  * back to it with events before the call returns, so every result is ordered
  * on `stream` as for a single-stream call.  That stream and its two events are
