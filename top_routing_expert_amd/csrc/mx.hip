@@ -30,15 +30,24 @@ namespace moe {
 typedef int v8i32_t __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- element codes
+// 2^k as a float, -126 <= k <= 127 (multiplying by it rounds like ldexpf).
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float(uint32_t(127 + k) << 23); }
+// v * 2^k for -127 <= k <= 127 (the one exponent below the normal range by ldexpf)
+__device__ __forceinline__ float scale_pow2(float v, int k) {
+  return k >= -126 ? v * pow2f(k) : ldexpf(v, k);
+}
+
 // Nearest value of a sign-magnitude grid (mbits mantissa bits, smallest normal
 // exponent emin, subnormals below), ties to even, saturating at maxmag.
 __device__ __forceinline__ uint32_t grid_code(float v, int mbits, int emin, float maxmag, int bias,
                                               int sign_bit) {
   const uint32_t sgn = (__float_as_uint(v) >> 31) << sign_bit;
   const float a = fminf(fabsf(v), maxmag);
-  int e = a > 0.0f ? ilogbf(a) : emin;
+  // binade of a from its exponent field (zero and fp32 subnormals fall below
+  // emin and are clamped to it, as every value under 2^emin is)
+  int e = int((__float_as_uint(a) >> 23) & 0xffu) - 127;
   e = e < emin ? emin : e;
-  const float q = rintf(ldexpf(a, mbits - e));   // exact scaling by a power of two
+  const float q = rintf(a * pow2f(mbits - e));   // exact scaling by a power of two
   const float half = float(1 << mbits), lim = float(2 << mbits);
   uint32_t code;
   if (a >= ldexpf(1.0f, emin)) {
@@ -110,7 +119,7 @@ __global__ __launch_bounds__(256) void mx4_quantize_kernel(const void* __restric
   if (!live) return;
   uint32_t packed = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= e2m1_code(ldexpf(v[i], 127 - sc)) << (4 * i);
+  for (int i = 0; i < 8; ++i) packed |= e2m1_code(scale_pow2(v[i], 127 - sc)) << (4 * i);
   const int64_t g = r / N, n = r - g * N;
   *reinterpret_cast<uint32_t*>(codes + ((g * (K / 64) + c8 / 8) * N + n) * 32 + (c8 % 8) * 4) = packed;
   if ((c8 & 3) == 0) scales[(g * (K / 32) + c8 / 4) * N + n] = uint8_t(sc);
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(256) void mx8_quantize_kernel(const void* __restric
   if (!live) return;
   uint32_t p[2] = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i / 4] |= e4m3_code(ldexpf(v[i], 127 - sc)) << (8 * (i % 4));
+  for (int i = 0; i < 8; ++i) p[i / 4] |= e4m3_code(scale_pow2(v[i], 127 - sc)) << (8 * (i % 4));
   *reinterpret_cast<uint2*>(codes + (int64_t(c8 / 8) * stride + r) * 64 + (c8 % 8) * 8) =
       make_uint2(p[0], p[1]);
   if ((c8 & 7) == 0) scales[int64_t(c8 / 8) * stride + r] = uint8_t(sc);
@@ -372,10 +381,10 @@ void gg_mx_kernel(MxArgs g) {
         float a[4];
         if constexpr (EPI == EPI_SWIGLU) {
           const float4 v1 = *reinterpret_cast<const float4*>(cw + (32 + rl) * CST + c4);
-          a[0] = silu(v0.x) * v1.x; a[1] = silu(v0.y) * v1.y;
-          a[2] = silu(v0.z) * v1.z; a[3] = silu(v0.w) * v1.w;
+          a[0] = silu_fast(v0.x) * v1.x; a[1] = silu_fast(v0.y) * v1.y;
+          a[2] = silu_fast(v0.z) * v1.z; a[3] = silu_fast(v0.w) * v1.w;
         } else {
-          a[0] = gelu_erf(v0.x); a[1] = gelu_erf(v0.y); a[2] = gelu_erf(v0.z); a[3] = gelu_erf(v0.w);
+          a[0] = gelu_fast(v0.x); a[1] = gelu_fast(v0.y); a[2] = gelu_fast(v0.z); a[3] = gelu_fast(v0.w);
         }
         // FP8 quantisation of the 64-column block held by these 16 lanes
         float amax = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3])));
@@ -383,7 +392,7 @@ void gg_mx_kernel(MxArgs g) {
         const int sc = scale_code(amax, 8);
         uint32_t pk = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pk |= e4m3_code(ldexpf(a[i], 127 - sc)) << (8 * i);
+        for (int i = 0; i < 4; ++i) pk |= e4m3_code(scale_pow2(a[i], 127 - sc)) << (8 * i);
         if (ok) {
           *reinterpret_cast<uint32_t*>(g.aq + (int64_t(n / 64) * g.aq_stride + row) * 64 + (n % 64)) = pk;
           if ((l & 15) == 0) g.aqs[int64_t(n / 64) * g.aq_stride + row] = uint8_t(sc);
