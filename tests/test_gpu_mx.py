@@ -138,3 +138,39 @@ def test_expert_ffn_mx_parity(name):
         assert np.all(err <= 2e-4 * cond + 1e-6 * np.sqrt(np.mean(ref ** 2))), f"expert {e}: output"
     print(f"{name}: experts {sample}, output err/sum|terms| {worst_out:.2e}, boundary blocks {near_boundary}, "
           f"codes one step off {codes_off}")
+
+
+def test_fp8_activation_codes_at_every_rounding_midpoint():
+    """E4M3 activation codes bit-exact against the oracle on crafted values:
+    every positive grid point (subnormals included), every midpoint between
+    neighbouring grid points (exact ties, which go to the even code), both fp32
+    neighbours of each midpoint, values that saturate to 448, both signs and
+    both zeros.  Each 64-element block leads with 480, so its scale is 2^0
+    (largest magnitude in [256, 512)) and the element values are coded as
+    they stand."""
+    p = presets.get("c4", dtype="f32")
+    grid = [m * 2.0 ** -9 for m in range(1, 8)]
+    grid += [(8 + m) * 2.0 ** (e - 3) for e in range(-6, 9) for m in range(8) if (8 + m) * 2.0 ** (e - 3) <= 448]
+    grid = np.array(sorted(set([0.0] + grid)), dtype=np.float64)
+    mids = (grid[:-1] + grid[1:]) / 2
+    m32 = mids.astype(np.float32)
+    assert np.all(m32.astype(np.float64) == mids)      # the ties are exact in fp32
+    vals = np.concatenate([grid.astype(np.float32), m32,
+                           np.nextafter(m32, np.float32(np.inf)), np.nextafter(m32, np.float32(0)),
+                           np.array([448.5, 449, 460, 464, 470, 479.9, 480], np.float32)])
+    vals = np.concatenate([vals, -vals, np.array([0.0, -0.0], np.float32)])
+    n_per = 63
+    rows = -(-len(vals) // n_per)
+    x = np.zeros((rows, 64), np.float32)
+    x[:, 0] = 480.0
+    flat = np.zeros(rows * n_per, np.float32)
+    flat[:len(vals)] = vals
+    x[:, 1:] = flat.reshape(rows, n_per)
+    K = 512                                             # eight 64-blocks per row
+    x = np.tile(x, (1, K // 64))
+    xq, xs = B.mx_quantize_act(p, torch.from_numpy(x).to(DEV), stride=B.mx_stride(rows))
+    torch.cuda.synchronize()
+    rc, rs = orc.mx_quantize(x, 64, "e4m3")
+    assert np.all(rs == 127)
+    np.testing.assert_array_equal(xs.cpu().numpy()[:, :rows].T.astype(np.int64), rs)
+    np.testing.assert_array_equal(_act_rows(xq.cpu().numpy())[:rows].astype(np.int64), rc)

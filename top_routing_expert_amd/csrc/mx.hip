@@ -59,7 +59,21 @@ __device__ __forceinline__ uint32_t grid_code(float v, int mbits, int emin, floa
   return code | sgn;
 }
 __device__ __forceinline__ uint32_t e2m1_code(float v) { return grid_code(v, 1, 0, 6.0f, 1, 3); }
-__device__ __forceinline__ uint32_t e4m3_code(float v) { return grid_code(v, 3, -6, 448.0f, 7, 7); }
+// Four E4M3 codes (byte i from v_i) of values already scaled into their block's
+// range: the sign bit of v_i over the code of min(|v_i|, 448), which the
+// hardware conversion produces (round to nearest even, subnormals below 2^-6);
+// it equals the grid rule above, grid_code(v, 3, -6, 448, 7, 7), on every
+// non-negative fp32 up to 448 (checked exhaustively on the device).  A NaN
+// saturates to 448 with its sign, as in the grid rule.
+__device__ __forceinline__ uint32_t e4m3_pack4(float v0, float v1, float v2, float v3) {
+  uint32_t w = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(fminf(fabsf(v0), 448.0f),
+                                                        fminf(fabsf(v1), 448.0f), 0, false));
+  w = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(fminf(fabsf(v2), 448.0f), fminf(fabsf(v3), 448.0f),
+                                               int(w), true));
+  const uint32_t sg = ((__float_as_uint(v0) >> 31) << 7) | ((__float_as_uint(v1) >> 31) << 15) |
+                      ((__float_as_uint(v2) >> 31) << 23) | (__float_as_uint(v3) & 0x80000000u);
+  return w | sg;
+}
 
 // E8M0 scale code of a block with largest magnitude amax (emax of the element type).
 __device__ __forceinline__ int scale_code(float amax, int emax) {
@@ -139,9 +153,9 @@ __global__ __launch_bounds__(256) void mx8_quantize_kernel(const void* __restric
   if (live) load8(x, r * K + int64_t(c8) * 8, bf16, v);
   const int sc = scale_code(block_amax<8>(v, live), 8);
   if (!live) return;
-  uint32_t p[2] = {0, 0};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i / 4] |= e4m3_code(scale_pow2(v[i], 127 - sc)) << (8 * (i % 4));
+  const int k = 127 - sc;
+  const uint32_t p[2] = {e4m3_pack4(scale_pow2(v[0], k), scale_pow2(v[1], k), scale_pow2(v[2], k), scale_pow2(v[3], k)),
+                         e4m3_pack4(scale_pow2(v[4], k), scale_pow2(v[5], k), scale_pow2(v[6], k), scale_pow2(v[7], k))};
   *reinterpret_cast<uint2*>(codes + (int64_t(c8 / 8) * stride + r) * 64 + (c8 % 8) * 8) =
       make_uint2(p[0], p[1]);
   if ((c8 & 7) == 0) scales[int64_t(c8 / 8) * stride + r] = uint8_t(sc);
@@ -390,9 +404,9 @@ void gg_mx_kernel(MxArgs g) {
         float amax = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3])));
         amax = group_max<16>(amax);
         const int sc = scale_code(amax, 8);
-        uint32_t pk = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk |= e4m3_code(scale_pow2(a[i], 127 - sc)) << (8 * i);
+        const int k = 127 - sc;
+        const uint32_t pk = e4m3_pack4(scale_pow2(a[0], k), scale_pow2(a[1], k), scale_pow2(a[2], k),
+                                       scale_pow2(a[3], k));
         if (ok) {
           *reinterpret_cast<uint32_t*>(g.aq + (int64_t(n / 64) * g.aq_stride + row) * 64 + (n % 64)) = pk;
           if ((l & 15) == 0) g.aqs[int64_t(n / 64) * g.aq_stride + row] = uint8_t(sc);
