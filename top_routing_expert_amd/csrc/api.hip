@@ -308,7 +308,7 @@ hipError_t fill_offsets_1(int32_t* off, int32_t rows, hipStream_t st) {
 }
 
 // A second stream per device for the layer's independent branches (the shared
-// expert, the router gradients), forked from and joined back to the caller's
+// expert, the router gradients, the routed dW2), forked from and joined back to the caller's
 // stream with events; created on first use and kept until the process ends.
 // Record-and-wait pairs run under one lock, so calls from several host
 // threads cannot interleave them.
