@@ -330,6 +330,11 @@ void gg_bf16_kernel(GemmArgs g) {
   const int b_lane = (8 * (gq >> 1) + (jq >> 2)) * (2 * BN) + 8 * (jq & 3);
 
   const int KT = int(cdiv(K, GB_BK));
+  // A wave whose half of the tile lies wholly past its group's last row (the
+  // last row tile of a group with few rows) skips its fragment reads and
+  // MFMAs; it still issues its share of every stage's loads and meets every
+  // barrier, and its zero accumulators are never stored.
+  const bool live = tc.m0 + wm * (BM / 2) < tc.M;
   // Each tile walks the K stages starting at its own offset (tile mod KT):
   // concurrent tiles read different K columns, which spreads their requests
   // over the L2 channels instead of having every CU hit the same channel with
@@ -363,6 +368,7 @@ void gg_bf16_kernel(GemmArgs g) {
     const uint4* As = lds + cur * STAGE;
     const char* Ab = reinterpret_cast<const char*>(As);
     const char* Bb = Ab + BM * 128;
+    if (live)
 #pragma unroll
     for (int s = 0; s <= 4; ++s) {
       if (s < 4) {
