@@ -175,6 +175,7 @@ void gg_bf16_kernel(GemmArgs g) {
   static_assert(NI >= 1 && A_INS >= 1 && B_INS >= 1, "tile too small for the wave count");
   constexpr int NS = gb_stages(BM, BN, NP);
   constexpr int INS = A_INS + NP * B_INS;   // load instructions per wave per stage
+  constexpr bool IL = MODE == GM_NT;        // loads interleaved with the sub-steps
   // NS stages of (BM + NP*BN) x 128 bytes (at most 144 KB), dynamic LDS.
   extern __shared__ uint4 lds[];
   __shared__ int32_t ts[257];
@@ -275,8 +276,11 @@ void gg_bf16_kernel(GemmArgs g) {
   const int64_t b_step = int64_t(8 * WV) * K;   // K-contiguous B: rows between a wave's instructions
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(&g_zero16);
 
-  auto issue = [&](int stage, int k0) {
+  // Issue a stage's loads: all of them (part < 0), or the quarter whose
+  // instruction index is part mod 4.
+  auto issue = [&](int stage, int k0, int part = -1) {
     uint4* base = lds + stage * STAGE;
+    auto mine = [&](int idx) { return part < 0 || (idx & 3) == part; };
     if constexpr (AK) {
       const int64_t koff = int64_t(k0) * g.M_fixed;
 #pragma unroll
@@ -284,7 +288,8 @@ void gg_bf16_kernel(GemmArgs g) {
         lds_load16(k0 + a_krow[i] < K ? a_src[i] + koff : zero, base + (w + WV * i) * 64);
     } else {
 #pragma unroll
-      for (int i = 0; i < A_INS; ++i) lds_load16(a_src[i] + k0, base + (w + WV * i) * 64);
+      for (int i = 0; i < A_INS; ++i)
+        if (mine(i)) lds_load16(a_src[i] + k0, base + (w + WV * i) * 64);
     }
     uint4* bbase = base + BM * 8;
     if constexpr (BKM) {
@@ -300,7 +305,8 @@ void gg_bf16_kernel(GemmArgs g) {
       for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
-          lds_load16(b_src[p] + i * b_step + k0, bbase + p * BN * 8 + (w + WV * i) * 64);
+          if (mine(A_INS + p * B_INS + i))
+            lds_load16(b_src[p] + i * b_step + k0, bbase + p * BN * 8 + (w + WV * i) * 64);
     }
   };
 
@@ -364,13 +370,20 @@ void gg_bf16_kernel(GemmArgs g) {
     // Every wave's loads of step kt have landed and every wave has finished
     // reading step kt-1 (its MFMAs were issued before this point).
     lds_barrier();
-    if (kt + NS - 1 < KT) issue(nxt, kcol(kt + NS - 1));
+    const bool more = kt + NS - 1 < KT;
+    const int knext = more ? kcol(kt + NS - 1) : 0;
+    // Forward layout: a live wave spreads the next stage's loads over the
+    // first four fragment sub-steps (a quarter each, after that sub-step's
+    // LDS reads), so they do not arrive as one burst that competes with the
+    // reads (2-4% on large products; the K-major layouts lose with it).
+    if (more && (!IL || !live)) issue(nxt, knext);
     const uint4* As = lds + cur * STAGE;
     const char* Ab = reinterpret_cast<const char*>(As);
     const char* Bb = Ab + BM * 128;
     if (live)
 #pragma unroll
     for (int s = 0; s <= 4; ++s) {
+      if (IL && s < 4 && more) issue(nxt, knext, s);
       if (s < 4) {
         const int pc = (2 * s + fg) ^ (fr & 7) ^ ((fr >> 3) & 1);
 #pragma unroll
@@ -410,6 +423,15 @@ void gg_bf16_kernel(GemmArgs g) {
       // MFMAs of step s-1 (otherwise the scheduler sinks every read next to
       // its use and each MFMA group waits on LDS latency).
       if (s < 4) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_STEP, 0);
+      if constexpr (IL) {
+        // this sub-step's quarter of the loads: (INS + 3 - s) / 4 instructions
+        if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 3) / 4, 0);
+        if (s == 1) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 2) / 4, 0);
+        if constexpr ((INS + 1) / 4 > 0)
+          if (s == 2) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 1) / 4, 0);
+        if constexpr (INS / 4 > 0)
+          if (s == 3) __builtin_amdgcn_sched_group_barrier(0x020, INS / 4, 0);
+      }
       if (s > 0) __builtin_amdgcn_sched_group_barrier(0x008, NP * MI * NI, 0);
     }
     // Every MFMA of this stage is issued before the next wait and barrier.
