@@ -8,7 +8,10 @@ Bars (written per test):
     checked to be a valid top-k; scores, gates and losses within 1e-5 relative;
   * dispatch: counts, offsets, row_of_slot, token_of_row and x_perm bit-exact;
   * expert FFN and layer output: max-abs error <= 2e-2 * RMS(reference) for
-    bf16 experts, <= 1e-4 absolute and <= 1e-4 * RMS for the fp32 layer.
+    bf16 experts, <= 1e-4 absolute and <= 1e-4 * RMS for the fp32 layer; the
+    short-K expert cases also bound every output by 2^-7 times its sum of
+    absolute terms |a| |W2|^T (the bf16 activation is one rounding of 2^-9;
+    replaying that rounding in float64 gives at most 1.8e-3).
 Full-size presets are checked on sampled rows/tokens the oracle computes one
 by one; the tiny fp32 preset is checked everywhere.
 """
@@ -216,6 +219,44 @@ def test_expert_ffn_parity(name):
     else:
         r = _assert_bf16_close(o, o_ref, f"{name} expert out")
         print(f"{name}: expert FFN max-abs/rms {r:.2e} on {len(rows)} rows")
+
+
+@pytest.mark.parametrize("name,over", [
+    # K = 128 in both products: two 64-deep stages, the second one the only
+    # stage a tile loads inside its K loop; a handful of rows per expert
+    ("c2", dict(T=300, d=128, F=128)),
+    # SwiGLU (two weight panels per tile), up K = 128, down K = 256
+    ("c4", dict(T=200, d=128, F=256)),
+    # 256 experts, many of them empty; down K = 128
+    ("c5", dict(T=500, d=256, F=128)),
+    # K = 384 (six stages), row tiles that end mid-tile
+    ("c3", dict(T=700, d=384, F=384))])
+def test_expert_ffn_short_k(name, over):
+    p, inp, x, w = case(name, **over)
+    ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                    inp["sel_bias"])
+    idx = torch.from_numpy(ref["idx"].astype(np.int32)).to(DEV)
+    print(f"[short-K ffn] {name} {over}", flush=True)
+    pm = B.permute(p, x, idx)
+    res = B.expert_ffn(p, pm["x_perm"], pm["offsets"], w.W13, w.W2, max_rows=p.T * p.k,
+                       save_hidden=True)
+    torch.cuda.synchronize()
+    offsets = pm["offsets"].cpu().numpy()
+    R = int(offsets[-1])
+    xp = pm["x_perm"][:R].float().cpu().numpy()
+    o_ref, _, a_ref = orc.expert_ffn(xp, offsets, inp["W13"], inp["W2"], p.act, keep_hidden=True)
+    o = res["out"][:R].cpu().numpy()
+    r = _assert_bf16_close(o, o_ref, f"{name} {over} expert out")
+    # Elementwise: the kernel stores the activation a in bf16 (one RNE
+    # rounding, relative error <= 2^-9) and accumulates in fp32, so each
+    # output is within a few 2^-9 of its sum of absolute terms |a| |W2|^T.
+    for e in range(p.E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            cond = np.abs(a_ref[e]) @ np.abs(inp["W2"][e].astype(np.float64)).T
+            bad = np.abs(o[r0:r1] - o_ref[r0:r1]) > 2.0 ** -7 * cond + 1e-30
+            assert not bad.any(), f"{name} {over} expert {e}: {int(bad.sum())} outputs off"
+    print(f"{name} {over}: expert FFN max-abs/rms {r:.2e} on all {R} rows", flush=True)
 
 
 # --------------------------------------------------------------------------- combine
