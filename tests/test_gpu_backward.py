@@ -129,7 +129,11 @@ def _bwd_terms(X, W13e, W2e, dO, F, act):
     # one-tile grids) and the logits GEMM (E >= 64)
     ("c5", dict(T=300, d=256, F=256, F_shared=256)),
     ("c4", dict(T=333, d=256, F=256, F_shared=0)),
-    ("c2", dict(T=257, d=256, F=512))])
+    ("c2", dict(T=257, d=256, F=512)),
+    # 1024 routed rows per expert (the c3 and c4 training shapes' row counts)
+    # at small widths, one with the shared expert beside them
+    ("c3", dict(T=4096, d=256, F=256)),
+    ("c4", dict(T=8192, d=256, F=128, F_shared=128))])
 def test_layer_bwd_full_size(name, over):
     p = presets.get(name, **over)
     print(f"[{name} bwd] generating inputs", flush=True)
