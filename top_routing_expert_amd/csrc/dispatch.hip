@@ -9,19 +9,15 @@
 // (scanned in wave order) and a ballot/popcount rank inside the wave.  No
 // global atomics decide any order.
 //
-// Slot priority (every token's first choice before any second choice, GShard's
-// overflow order): the same kernels run over the T*k slots in slot-major order,
-// as virtual tokens v = j*T + t with one slot each.  With k >= 4 token priority
-// runs one slot per lane as well, in flat order v = t*k + j: a token's k
-// experts are distinct, so within an expert this is token order and the ranks
-// are the same, with k times more waves and at most 64 distinct experts per
-// wave to peel.
+// Every kernel walks the T*k slots one per lane.  Token priority takes them in
+// flat order v = t*k + j, which inside an expert is ascending token order (and
+// slot order within a token, so a token that lists one expert twice keeps both
+// slots, in slot order).  Slot priority (every token's first choice before any
+// second choice, GShard's overflow order) takes them slot-major, v = j*T + t.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
-
-constexpr int DISP_KMAX = 16;
 
 // Per-block histogram of the slots' experts.  LDS atomics only count, so the
 // result is order independent.  Entries outside [0, E) are skipped.
@@ -31,22 +27,10 @@ __global__ __launch_bounds__(1024) void dispatch_hist_kernel(const int32_t* __re
   __shared__ int32_t hist[256];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;    // blockDim.x = the order's block size
-  if (order == DISP_FLAT) {
-    if (int64_t(t) < int64_t(T) * k) {
-      const int e = idx[t];
-      if (unsigned(e) < unsigned(E)) atomicAdd(&hist[e], 1);
-    }
-  } else if (order == DISP_SLOT) {
-    if (int64_t(t) < int64_t(T) * k) {
-      const int e = idx[int64_t(t % T) * k + t / T];
-      if (unsigned(e) < unsigned(E)) atomicAdd(&hist[e], 1);
-    }
-  } else if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[int64_t(t) * k + j];
-      if (unsigned(e) < unsigned(E)) atomicAdd(&hist[e], 1);
-    }
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (int64_t(v) < int64_t(T) * k) {
+    const int e = order == DISP_SLOT ? idx[int64_t(v % T) * k + v / T] : idx[v];
+    if (unsigned(e) < unsigned(E)) atomicAdd(&hist[e], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) blockcnt[int64_t(blockIdx.x) * E + e] = hist[e];
@@ -125,18 +109,15 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   }
 }
 
-// Stable ranks and the row copy.  Block b covers the NT tokens (or slots)
-// from b*NT, wave w the 64 from b*NT + 64w, one per lane.
-//   1. peel: repeatedly take the expert of the first lane with a pending slot,
+// Stable ranks.  Block b covers the NT slots from b*NT in the order's sequence,
+// wave w the 64 from b*NT + 64w, one per lane.
+//   1. peel: repeatedly take the expert of the first lane still pending,
 //      ballot the lanes holding that expert, rank = popcount of lower lanes;
 //      the leader records the wave's count for the expert;
 //   2. rank in expert = blockbase[b][e] + counts of lower waves + rank in wave;
-//      kept iff rank < C; row = offsets[e] + rank;
+//      kept iff rank < C; row = offsets[e] + rank.
 // The row copy is a separate, token-parallel kernel (permute_copy_kernel).
-// ORDER DISP_SLOT: the block's "tokens" are the slot-major virtual tokens
-// v = j*T + t (KM = 1), slot (v % T, v / T); DISP_FLAT: flat slots v = t*k + j
-// (KM = 1), token v / k.
-template <int KM, int ORDER, int NT = 256>
+template <int ORDER, int NT>
 __global__ __launch_bounds__(NT) void dispatch_rank_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int64_t C,
     const int32_t* __restrict__ blockbase, const int32_t* __restrict__ offsets,
@@ -145,73 +126,42 @@ __global__ __launch_bounds__(NT) void dispatch_rank_kernel(
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   for (int i = tid; i < (NT / 64) * 256; i += NT) (&wavecnt[0][0])[i] = 0;
   const int v = blockIdx.x * NT + tid;
-  constexpr bool ONE = ORDER != DISP_TOKEN;                     // one slot per lane
-  const bool valid = ONE ? int64_t(v) < int64_t(T) * k : v < T;
-  const int t = ORDER == DISP_SLOT ? (valid ? v % T : 0)       // token of this lane's slots
-              : ORDER == DISP_FLAT ? (valid ? v / k : 0) : v;
-  const int64_t slot0 = ORDER == DISP_SLOT ? int64_t(t) * k + (valid ? v / T : 0)
-                      : ORDER == DISP_FLAT ? (valid ? int64_t(v) : 0) : int64_t(t) * k;
-  const int kk = ONE ? 1 : k;                                   // slots per lane
-  int ex[KM];
-  int rk[KM];
-  uint32_t pending = 0;
-#pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    ex[j] = -1;
-    rk[j] = 0;
-    if (valid && j < kk) {
-      const int e = idx[slot0 + j];
-      if (unsigned(e) < unsigned(E)) {
-        ex[j] = e;
-        pending |= 1u << j;
-      }
-    }
+  const bool valid = int64_t(v) < int64_t(T) * k;
+  const int t = !valid ? 0 : (ORDER == DISP_SLOT ? v % T : v / k);      // token of this slot
+  const int64_t slot = !valid ? 0 : (ORDER == DISP_SLOT ? int64_t(t) * k + v / T : int64_t(v));
+  int ex = -1;
+  if (valid) {
+    const int e = idx[slot];
+    if (unsigned(e) < unsigned(E)) ex = e;
   }
   __syncthreads();
   const uint64_t lt_mask = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  bool pending = ex >= 0;
+  int rk = 0;
   while (true) {
-    const uint64_t act = __ballot(pending != 0);
+    const uint64_t act = __ballot(pending);
     if (act == 0) break;
     const int leader = __ffsll(static_cast<unsigned long long>(act)) - 1;
-    int mine = -1;
-    if (pending) {
-      const int j0 = __ffs(pending) - 1;
-#pragma unroll
-      for (int j = 0; j < KM; ++j)
-        if (j == j0) mine = ex[j];
-    }
-    const int e = __shfl(mine, leader, 64);
-    int jm = -1;
-#pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if ((pending >> j & 1u) && ex[j] == e) jm = j;
-    const uint64_t m = __ballot(jm >= 0);
-    if (jm >= 0) {
-      const int r = __popcll(m & lt_mask);
-#pragma unroll
-      for (int j = 0; j < KM; ++j)
-        if (j == jm) rk[j] = r;
-      pending &= ~(1u << jm);
+    const int e = __shfl(ex, leader, 64);
+    const bool mine = pending && ex == e;
+    const uint64_t m = __ballot(mine);
+    if (mine) {
+      rk = __popcll(m & lt_mask);
+      pending = false;
     }
     if (l == leader) wavecnt[w][e] = __popcll(m);
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < KM; ++j) {
-    if (j < kk) {
-      int row = -1;
-      const int e = ex[j];
-      if (e >= 0) {
-        int32_t rank = blockbase[int64_t(blockIdx.x) * E + e] + rk[j];
-        for (int ww = 0; ww < w; ++ww) rank += wavecnt[ww][e];
-        if (C < 0 || rank < C) {
-          row = offsets[e] + rank;
-          token_of_row[row] = t;
-        }
-      }
-      if (valid) row_of_slot[slot0 + j] = row;
+  int row = -1;
+  if (ex >= 0) {
+    int32_t rank = blockbase[int64_t(blockIdx.x) * E + ex] + rk;
+    for (int ww = 0; ww < w; ++ww) rank += wavecnt[ww][ex];
+    if (C < 0 || rank < C) {
+      row = offsets[ex] + rank;
+      token_of_row[row] = t;
     }
   }
+  if (valid) row_of_slot[slot] = row;
 }
 
 // Row copy, token-major, one wave per token: the token's x row is read once
@@ -243,25 +193,19 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const int32_t* __rest
   }
 }
 
-int dispatch_order(int k, bool slot_major) {
-  return slot_major ? DISP_SLOT : (k >= 4 ? DISP_FLAT : DISP_TOKEN);
-}
+int dispatch_order(bool slot_major) { return slot_major ? DISP_SLOT : DISP_FLAT; }
 
-// Slots (or tokens) per dispatch block: 1024 in flat order (16 waves; fewer
-// blocks keep the single-workgroup scan over the blocks short), else 256.
-int dispatch_block_size(int order) { return order == DISP_FLAT ? 1024 : DISP_TB; }
+// Slots per dispatch block (16 waves; fewer blocks keep the single-workgroup
+// scan over the blocks short).
+constexpr int DISP_NT = 1024;
 
-int dispatch_blocks(int T, int k, bool slot_major) {
-  const int order = dispatch_order(k, slot_major);
-  return int(cdiv(order != DISP_TOKEN ? int64_t(T) * k : int64_t(T), dispatch_block_size(order)));
-}
+int dispatch_blocks(int T, int k, bool) { return int(cdiv(int64_t(T) * k, DISP_NT)); }
 
 hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, bool slot_major,
                                 int32_t* blockcnt, hipStream_t st) {
   const unsigned nblk = unsigned(dispatch_blocks(T, k, slot_major));
-  const int order = dispatch_order(k, slot_major);
-  dispatch_hist_kernel<<<dim3(nblk), dim3(dispatch_block_size(order)), 0, st>>>(idx, T, k, E, order,
-                                                                               blockcnt);
+  dispatch_hist_kernel<<<dim3(nblk), dim3(DISP_NT), 0, st>>>(idx, T, k, E, dispatch_order(slot_major),
+                                                             blockcnt);
   return hipGetLastError();
 }
 
@@ -283,28 +227,17 @@ hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int6
   const int row_bytes = d * elem_bytes;
   const auto* xs = static_cast<const uint8_t*>(x);
   auto* xp = static_cast<uint8_t*>(x_perm);
-#define MOE_PERMUTE(KM)                                                                        \
-  dispatch_rank_kernel<KM, DISP_TOKEN><<<dim3(nblk), dim3(256), 0, st>>>(                      \
-      idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);                         \
-  permute_copy_kernel<KM><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp)
-  const int order = dispatch_order(k, slot_major);
-  if (order != DISP_TOKEN) {
-    if (order == DISP_SLOT)
-      dispatch_rank_kernel<1, DISP_SLOT><<<dim3(nblk), dim3(256), 0, st>>>(
-          idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);
-    else
-      dispatch_rank_kernel<1, DISP_FLAT, 1024><<<dim3(nblk), dim3(1024), 0, st>>>(
-          idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);
-    if (k <= 2) permute_copy_kernel<2><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
-    else if (k <= 4) permute_copy_kernel<4><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
-    else if (k <= 8) permute_copy_kernel<8><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
-    else permute_copy_kernel<16><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
-  } else if (k <= 1) { MOE_PERMUTE(1); }
-  else if (k <= 2) { MOE_PERMUTE(2); }
-  else if (k <= 4) { MOE_PERMUTE(4); }
-  else if (k <= 8) { MOE_PERMUTE(8); }
-  else { MOE_PERMUTE(16); }
-#undef MOE_PERMUTE
+  if (slot_major)
+    dispatch_rank_kernel<DISP_SLOT, DISP_NT><<<dim3(nblk), dim3(DISP_NT), 0, st>>>(
+        idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);
+  else
+    dispatch_rank_kernel<DISP_FLAT, DISP_NT><<<dim3(nblk), dim3(DISP_NT), 0, st>>>(
+        idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);
+  if (k <= 1) permute_copy_kernel<1><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
+  else if (k <= 2) permute_copy_kernel<2><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
+  else if (k <= 4) permute_copy_kernel<4><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
+  else if (k <= 8) permute_copy_kernel<8><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
+  else permute_copy_kernel<16><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
   return hipGetLastError();
 }
 

@@ -46,13 +46,12 @@ hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, flo
                                hipStream_t st);
 
 // ------------------------------------------------------------------ dispatch
-constexpr int DISP_TB = 256;   // tokens per dispatch block
+// Orders in which the dispatch kernels walk the T*k slots, one per lane: flat
+// (v = t*k + j, token priority) or slot-major (v = j*T + t, slot priority).
 // Blocks of the histogram / rank kernels (and rows of their per-block count
-// arrays): over tokens, or over the T*k slots in slot-major order.
-// Orders in which the dispatch kernels walk the slots: one token per lane
-// (its k slots), slot-major virtual tokens (slot priority), flat slots.
-enum DispOrder { DISP_TOKEN = 0, DISP_SLOT = 1, DISP_FLAT = 2 };
-int dispatch_order(int k, bool slot_major);
+// arrays) are runs of consecutive slots in that order.
+enum DispOrder { DISP_SLOT = 1, DISP_FLAT = 2 };
+int dispatch_order(bool slot_major);
 int dispatch_blocks(int T, int k, bool slot_major);
 hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, bool slot_major,
                                 int32_t* blockcnt, hipStream_t st);
