@@ -255,6 +255,28 @@ def test_dispatch_bruteforce_ranks():
             assert ros[t, j] == (base + rank if rank < C else -1)
 
 
+def test_dispatch_bruteforce_with_repeated_experts():
+    """A token listing one expert in several slots occupies one row per slot:
+    the rank of slot (t, j) in expert e counts every earlier (token, slot) pair
+    with e, in (token, slot) order."""
+    rng = np.random.default_rng(13)
+    T, E, k, C = 50, 4, 3, 20
+    idx = rng.integers(0, E, size=(T, k))
+    idx[::4, 1] = idx[::4, 0]
+    idx[::9] = 2
+    counts, offsets, ros, tor = orc.dispatch(idx, E, C)
+    np.testing.assert_array_equal(counts, [int(np.sum(idx == e)) for e in range(E)])
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            rank = sum(1 for u in range(T) for i in range(k)
+                       if idx[u, i] == e and (u, i) < (t, j))
+            base = sum(min(int(np.sum(idx == f)), C) for f in range(e))
+            assert ros[t, j] == (base + rank if rank < C else -1)
+            if ros[t, j] >= 0:
+                assert tor[ros[t, j]] == t
+
+
 def test_dispatch_invariants_on_presets():
     for name in ("c1", "c2"):
         p = presets.get(name)
@@ -761,6 +783,59 @@ def test_mx_block_scale_rule(fmt, block, emax, top):
     np.testing.assert_array_equal(got, want)
     deq = orc.mx_dequantize(codes, sc, block, fmt)
     assert np.all(np.abs(deq) <= top * scale.repeat(block, axis=1) + 0)
+
+
+@pytest.mark.parametrize("fmt,block", [("e2m1", 32), ("e4m3", 64)])
+def test_mx_dequantize_block_scale_mapping(fmt, block):
+    """Element k of a row is scaled by the E8M0 scale of its own block k // block:
+    a row whose blocks carry distinct scale codes and one repeated element code
+    decodes to that element's value times 2^(scale code - 127), block by block
+    (the element value from the format's table: E2M1 code 3 = 1.5, E4M3 code
+    0x3A = 1.25)."""
+    nb = 5
+    code, val = (3, 1.5) if fmt == "e2m1" else (0x3A, 1.25)
+    codes = np.full((2, nb * block), code)
+    codes[1] |= 8 if fmt == "e2m1" else 0x80                    # second row negative
+    sc = np.array([[127, 120, 131, 1, 250], [254, 0, 127, 64, 200]])
+    deq = orc.mx_dequantize(codes, sc, block, fmt)
+    for r, sign in ((0, 1.0), (1, -1.0)):
+        for b in range(nb):
+            want = sign * val * 2.0 ** (int(sc[r, b]) - 127)
+            assert np.all(deq[r, b * block:(b + 1) * block] == want), (r, b)
+
+
+@pytest.mark.parametrize("fmt,block,mbits", [("e2m1", 32, 1), ("e4m3", 64, 3)])
+def test_mx_round_trip_within_half_a_grid_step(fmt, block, mbits):
+    """deq(quant(w)) differs from w by at most half the grid step of the
+    element's binade times its block's scale (nearest rounding), on rows whose
+    blocks differ in magnitude by up to 2^40; elements beyond the largest grid
+    value after scaling (the scale rule lets a block's maximum land up to
+    2^(emax+1)) decode to that value with their sign."""
+    rng = np.random.default_rng(53)
+    rows, nb = 4, 6
+    mag = np.ldexp(1.0, rng.integers(-20, 21, size=(rows, nb)))
+    w = rng.uniform(-1, 1, size=(rows, nb, block)) * mag[:, :, None]
+    w = w.reshape(rows, nb * block)
+    codes, sc = orc.mx_quantize(w, block, fmt)
+    deq = orc.mx_dequantize(codes, sc, block, fmt)
+    scale = np.ldexp(1.0, sc - 127).repeat(block, axis=1)
+    emin = 0 if fmt == "e2m1" else -6
+    v = np.abs(w) / scale
+    with np.errstate(divide="ignore"):
+        e = np.maximum(np.floor(np.log2(np.where(v > 0, v, 1.0))), emin)
+    step = np.ldexp(1.0, (e - mbits).astype(np.int64))          # grid spacing at v's binade
+    top = 6.0 if fmt == "e2m1" else 448.0
+    ok = v <= top                                               # not saturated
+    assert 0.5 < ok.mean() < 1.0
+    err = np.abs(deq - w)
+    assert np.all(err[ok] <= 0.5 * step[ok] * scale[ok] * (1 + 1e-12))
+    np.testing.assert_array_equal(deq[~ok], np.sign(w[~ok]) * top * scale[~ok])
+    # blocks keep their own scale: the error of every block is tiny against the
+    # largest block of the row
+    for r in range(rows):
+        for b in range(nb):
+            blk = slice(b * block, (b + 1) * block)
+            assert np.max(err[r, blk]) <= 0.5 * np.max(np.abs(w[r, blk]))
 
 
 def test_expert_ffn_mx_composition():
