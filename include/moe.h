@@ -34,8 +34,9 @@
  *     gradients are fp32.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
  *     only enqueues work on it: there is no device-to-host synchronisation and
- *     the library allocates nothing.  Shape-dependent work (per-expert row
- *     counts) is read on the device.
+ *     the library allocates no memory (the layer calls create one internal
+ *     stream and two events per caller stream, once; see moe_layer_fwd).
+ *     Shape-dependent work (per-expert row counts) is read on the device.
  *   - `ws`/`ws_bytes` is caller-owned device scratch of at least
  *     moe_workspace_size() bytes, 256-byte aligned; contents need no
  *     initialisation and are clobbered.
@@ -54,12 +55,14 @@
 extern "C" {
 #endif
 
+/* Status of every int-returning entry point: 0 on success, a negative code on
+ * failure (moe_strerror names it). */
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARG = 1,  /* null required pointer, bad size or option, misalignment */
-  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement (see limits) */
-  MOE_ERR_WORKSPACE = 3,    /* ws_bytes below moe_workspace_size() */
-  MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+  MOE_ERR_INVALID_ARG = -1,  /* null required pointer, bad size or option, misalignment */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels implement (see limits) */
+  MOE_ERR_WORKSPACE = -3,    /* ws_bytes below moe_workspace_size() */
+  MOE_ERR_HIP = -4           /* a HIP launch or runtime call failed */
 } moe_status;
 
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1, MOE_SCORE_SQRT_SOFTPLUS = 2 } moe_score;
@@ -163,6 +166,12 @@ typedef struct {
   float* dWs13;  /* [2*F_shared, d] (when F_shared > 0) */
   float* dWs2;   /* [d, F_shared]   (when F_shared > 0) */
   float* dW_noise; /* [d, E] (noisy top-k) */
+  /* Nullable: when set, the gradient with respect to the saved pre-activations
+   * is written here (in their element type) instead of into the workspace:
+   * dH [T*k, n_up] for the routed experts' h (rows past offsets[E] are not
+   * written), dH_shared [T, 2*F_shared] for the shared expert's. */
+  void* dH;
+  void* dH_shared;
 } moe_grads;
 
 /* Router monitoring outputs, every field nullable. */
@@ -232,10 +241,13 @@ int moe_combine(const moe_dims* dims, const float* out_perm, const int32_t* row_
  * Streams (moe_layer_fwd and moe_layer_bwd): branches that do not depend on
  * each other (the shared expert; in the backward also the router gradients and
  * the routed experts' dW2) run
- * on an internal stream of the current device, forked from `stream` and joined
- * back to it with events before the call returns, so every result is ordered
- * on `stream` as for a single-stream call.  That stream and its two events are
- * created on the first call on a device and kept until the process ends. */
+ * on an internal stream, forked from `stream` and joined back to it with
+ * events before the call returns, so every result is ordered on `stream` as
+ * for a single-stream call.  There is one internal stream (with its two events)
+ * per (device, caller stream): it is created on the first layer call made on
+ * that caller stream and kept until the process ends, so calls on different
+ * caller streams do not wait on each other.  This is the library's only state;
+ * it holds no data. */
 int moe_layer_fwd(const moe_dims* dims, const moe_opts* opts, const moe_weights* w,
                   const moe_router_inputs* ri, const void* x, float* y, moe_saved* saved,
                   moe_stats* stats, void* ws, size_t ws_bytes, void* stream);

@@ -48,10 +48,19 @@ def test_capacity_matches_golden(L):
         assert B.capacity(p) == want, c
 
 
-def test_strerror(L):
-    for s in range(5):
-        assert L.moe_strerror(s)
+def test_status_codes_are_negative(L):
+    """The header's moe_status values: 0 for success, negative codes for
+    failures, each with its own text."""
+    text = open(HEADER).read()
+    vals = dict((n, int(v)) for n, v in re.findall(r"^\s*(MOE_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", text, re.M))
+    assert vals == {"MOE_OK": 0, "MOE_ERR_INVALID_ARG": -1, "MOE_ERR_UNSUPPORTED": -2,
+                    "MOE_ERR_WORKSPACE": -3, "MOE_ERR_HIP": -4}
+    assert (B.MOE_OK, B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE,
+            B.MOE_ERR_HIP) == (0, -1, -2, -3, -4)
+    texts = [L.moe_strerror(s) for s in (0, -1, -2, -3, -4)]
+    assert len(set(texts)) == 5 and b"unknown status" not in texts
     assert L.moe_strerror(99) == b"unknown status"
+    assert L.moe_strerror(1) == b"unknown status"
 
 
 def test_workspace_size_grows_with_tokens(L):

@@ -20,7 +20,8 @@ from .presets import Preset
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+# moe_status: 0 on success, negative on failure
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
 ACT = {"swiglu": 0, "gelu": 1}
 DTYPE = {"f32": 0, "bf16": 1}
@@ -62,7 +63,8 @@ class Saved(C.Structure):
 
 
 class Grads(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("dWg", "dW13", "dW2", "dWs13", "dWs2", "dW_noise")]
+    _fields_ = [(n, C.c_void_p) for n in ("dWg", "dW13", "dW2", "dWs13", "dWs2", "dW_noise", "dH",
+                                          "dH_shared")]
 
 
 class Stats(C.Structure):
@@ -351,16 +353,22 @@ def layer_fwd(p: Preset, w: LayerWeights, x, *, saved: Optional[dict] = None, st
 
 
 def layer_bwd(p: Preset, w: LayerWeights, x, saved: dict, dy, *,
-              ri: Optional[LayerRouterInputs] = None, ws: Optional[Workspace] = None):
-    """moe_layer_bwd; returns dict(dx, dWg, dW13, dW2, dWs13, dWs2, dW_noise)."""
+              ri: Optional[LayerRouterInputs] = None, ws: Optional[Workspace] = None,
+              want_dH: bool = False):
+    """moe_layer_bwd; returns dict(dx, dWg, dW13, dW2, dWs13, dWs2, dW_noise, dH, dH_shared)
+    (dH and dH_shared, the gradients of the saved pre-activations, only when asked)."""
     dev = x.device
     T = x.shape[0]
     e = lambda *s: torch.empty(*s, dtype=torch.float32, device=dev)
     nu = 2 * p.F if p.act == "swiglu" else p.F
+    xd = TORCH_DTYPE[p.dtype]
     g = dict(dx=e(T, p.d), dWg=e(p.d, p.E), dW13=e(p.E, nu, p.d), dW2=e(p.E, p.d, p.F),
              dWs13=e(2 * p.F_shared, p.d) if p.F_shared else None,
              dWs2=e(p.d, p.F_shared) if p.F_shared else None,
-             dW_noise=e(p.d, p.E) if p.routing == "noisy_topk" else None)
+             dW_noise=e(p.d, p.E) if p.routing == "noisy_topk" else None,
+             dH=torch.empty(max(T * p.k, 1), nu, dtype=xd, device=dev) if want_dH else None,
+             dH_shared=(torch.empty(T, 2 * p.F_shared, dtype=xd, device=dev)
+                        if want_dH and p.F_shared else None))
     gc = Grads(*(None if g[n] is None else g[n].data_ptr() for n, _ in Grads._fields_))
     ws = ws or Workspace(dev)
     nb = workspace_size(p, with_bwd=True, T=T)
@@ -412,7 +420,7 @@ class Layer:
                               dWs2=e(p.d, p.F_shared) if p.F_shared else None,
                               dW_noise=e(p.d, p.E) if p.routing == "noisy_topk" else None)
             self.dx = e(self.T, p.d)
-            self._grads_c = Grads(*(None if self.grads[n] is None else self.grads[n].data_ptr()
+            self._grads_c = Grads(*(None if self.grads.get(n) is None else self.grads[n].data_ptr()
                                     for n, _ in Grads._fields_))
         _check("moe_layer_bwd", lib().moe_layer_bwd(
             C.byref(self._dims), C.byref(self._opts), C.byref(self._w),

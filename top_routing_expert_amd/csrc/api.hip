@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 using namespace moe;
 
@@ -307,31 +308,45 @@ hipError_t fill_offsets_1(int32_t* off, int32_t rows, hipStream_t st) {
   return launch_fill_i32(off, 2, 0, rows, 0, 0, st);
 }
 
-// A second stream per device for the layer's independent branches (the shared
-// expert, the router gradients, the routed dW2), forked from and joined back to the caller's
-// stream with events; created on first use and kept until the process ends.
-// Record-and-wait pairs run under one lock, so calls from several host
-// threads cannot interleave them.
+// A second stream for the layer's independent branches (the shared expert,
+// the router gradients, the routed dW2), forked from and joined back to the
+// caller's stream with events.  One is kept per (device, caller stream), created
+// on the first layer call from that stream and kept until the process ends, so
+// calls made on different caller streams (from one host thread or several)
+// never wait on each other through it.  The table and every record-and-wait
+// pair are guarded by one lock.
 struct SideStream {
+  int dev;
+  hipStream_t caller;
   hipStream_t s;
   hipEvent_t fork, join;
 };
 std::mutex g_side_mu;
-SideStream g_side[64] = {};
+std::vector<SideStream*> g_side;
 
-hipError_t side_stream(SideStream** out) {
+hipError_t side_stream(hipStream_t caller, SideStream** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream& sd = g_side[dev];
-  if (!sd.s) {
-    if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) return e;
+  for (SideStream* sd : g_side)
+    if (sd->dev == dev && sd->caller == caller) {
+      *out = sd;
+      return hipSuccess;
+    }
+  SideStream sd{dev, caller, nullptr, nullptr, nullptr};
+  if ((e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess) return e;
+  if ((e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess) {
+    (void)hipEventDestroy(sd.fork);
+    return e;
   }
-  *out = &sd;
+  if ((e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking)) != hipSuccess) {
+    (void)hipEventDestroy(sd.fork);
+    (void)hipEventDestroy(sd.join);
+    return e;
+  }
+  g_side.push_back(new SideStream(sd));
+  *out = g_side.back();
   return hipSuccess;
 }
 
@@ -614,7 +629,7 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
     return code;
   };
   if (d->F_shared > 0) {
-    MOE_TRY(side_stream(&side));
+    MOE_TRY(side_stream(st, &side));
     MOE_TRY(stream_wait(side->s, st, side->fork));
     int32_t* soff = at<int32_t>(ws, f.shared_off);
     if (hipError_t e = fill_offsets_1(soff, int32_t(d->T), side->s); e != hipSuccess)
@@ -659,6 +674,8 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   if (noisy && (!sv || !sv->noise_logits || !grads || !grads->dW_noise)) return MOE_ERR_INVALID_ARG;
   if (!w || !x || !sv || !dy || !dx || !grads || !w->Wg || !w->W13 || !w->W2) return MOE_ERR_INVALID_ARG;
   if (!grads->dWg || !grads->dW13 || !grads->dW2) return MOE_ERR_INVALID_ARG;
+  if ((grads->dH && !aligned16(grads->dH)) || (grads->dH_shared && !aligned16(grads->dH_shared)))
+    return MOE_ERR_INVALID_ARG;
   if (Fs > 0 && (!w->Ws13 || !w->Ws2 || !grads->dWs13 || !grads->dWs2 || !sv->h_shared ||
                  !sv->a_shared))
     return MOE_ERR_INVALID_ARG;
@@ -680,6 +697,9 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   const bool swiglu = o->act == MOE_ACT_SWIGLU;
   int32_t* ts = at<int32_t>(ws, b.ffn.tile_up);
   int32_t* ts_s = at<int32_t>(ws, b.ffn_s.tile_up);
+  // gradients of the pre-activations: the caller's buffers when given
+  void* dH = grads->dH ? grads->dH : at<void>(ws, b.dH);
+  void* dHs = grads->dH_shared ? grads->dH_shared : at<void>(ws, b.dHs);
 
   // combine backward: dO, dg, and dy in the x type for the shared expert
   void* dyx = Fs ? at<void>(ws, b.dyx) : nullptr;
@@ -718,9 +738,9 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
       int32_t* soff = at<int32_t>(ws, b.soff);
       dxs = at<float>(ws, b.dxs);
       MOE_TRY(gemm_on(o, gemm_dgrad(dyx, w->Ws2, 0, soff, 1, T, fs, D, EPI_SWIGLU_BWD,
-                                    at<void>(ws, b.dHs), sv->h_shared, 2 * fs, fs),
+                                    dHs, sv->h_shared, 2 * fs, fs),
                       ts_s, bs));
-      MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dHs), w->Ws13, 0, soff, 1, T, D, 2 * fs,
+      MOE_TRY(gemm_on(o, gemm_dgrad(dHs, w->Ws13, 0, soff, 1, T, D, 2 * fs,
                                     EPI_STORE_F32, dxs, nullptr, 0, 0),
                       ts_s, bs));
       // weight gradients: the T-reduction split into equal token chunks (one
@@ -729,7 +749,7 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
       float* part = at<float>(ws, b.spart);
       MOE_TRY(gemm_on(o, gemm_wgrad(dyx, sv->a_shared, coff, s2, D, fs, part), ts_s, bs));
       MOE_TRY(launch_sum_partials(part, s2, int64_t(D) * fs, grads->dWs2, bs));
-      MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dHs), x, coff + 17, s13, 2 * fs, D, part), ts_s, bs));
+      MOE_TRY(gemm_on(o, gemm_wgrad(dHs, x, coff + 17, s13, 2 * fs, D, part), ts_s, bs));
       MOE_TRY(launch_sum_partials(part, s13, int64_t(2) * fs * D, grads->dWs13, bs));
     }
     // router: dz from the kept gates' gradient and the two losses; dWg = x^T dz;
@@ -783,19 +803,19 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
   auto routed_branch = [&]() -> int {
     // routed experts, data gradients: dA = dO W2 (+ activation backward) -> dH; dXp = dH W13
     MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dO), w->W2, int64_t(D) * F, sv->offsets, E, R, F, D,
-                                  swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, at<void>(ws, b.dH), sv->h,
+                                  swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, dH, sv->h,
                                   nu, swiglu ? F : 0),
                     ts, st));
-    MOE_TRY(gemm_on(o, gemm_dgrad(at<void>(ws, b.dH), w->W13, int64_t(nu) * D, sv->offsets, E, R, D,
+    MOE_TRY(gemm_on(o, gemm_dgrad(dH, w->W13, int64_t(nu) * D, sv->offsets, E, R, D,
                                   nu, EPI_STORE_F32, at<void>(ws, b.dXp), nullptr, 0, 0),
                     ts, st));
     // routed experts, weight gradient over each expert's rows: dW13[e] = dH_e^T x_e
-    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dH), sv->x_perm, sv->offsets, E, nu, D, grads->dW13),
+    MOE_TRY(gemm_on(o, gemm_wgrad(dH, sv->x_perm, sv->offsets, E, nu, D, grads->dW13),
                     ts, st));
     return MOE_OK;
   };
   SideStream* side = nullptr;
-  MOE_TRY(side_stream(&side));
+  MOE_TRY(side_stream(st, &side));
   MOE_TRY(stream_wait(side->s, st, side->fork));
   // Launch order: with a shared expert the side branch holds its GEMMs and is
   // launched first; without one it holds only the router's gradients and dW2,
