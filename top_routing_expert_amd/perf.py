@@ -40,13 +40,29 @@ def ffn_flops(p: Preset, R: int, shared: bool = True) -> float:
 
 
 def ffn_bytes(p: Preset, R: int, active_experts: int, shared: bool = True) -> float:
-    """Routed expert FFN: weights of active experts, x_perm read, activation
-    written then read (x dtype), fp32 output written."""
+    """Algorithmic HBM bytes of the routed expert FFN: the weights of the active
+    experts read once, the x_perm rows read once and the fp32 output rows
+    written once.  The activation between the two projections is an
+    intermediate (a fused FFN keeps it on chip), so it is not counted."""
     b = active_experts * n_mats(p) * p.d * p.F * eb(p)
-    b += R * p.d * eb(p) + 2 * R * p.F * eb(p) + R * p.d * 4
+    b += R * p.d * eb(p) + R * p.d * 4
     if shared and p.F_shared:
-        b += 3 * p.d * p.F_shared * eb(p) + p.T * p.d * eb(p) + 2 * p.T * p.F_shared * eb(p) + p.T * p.d * 4
+        b += 3 * p.d * p.F_shared * eb(p) + p.T * p.d * eb(p) + p.T * p.d * 4
     return float(b)
+
+
+def ffn_bytes_unfused(p: Preset, R: int, active_experts: int) -> float:
+    """What the two-launch FFN moves at best: ffn_bytes plus the activation
+    written by the up projection and read back by the down projection."""
+    return ffn_bytes(p, R, active_experts, shared=False) + 2.0 * R * p.F * eb(p)
+
+
+def ffn_roofline_s(p: Preset, R: int, active_experts: int) -> tuple:
+    """(seconds, bound) of the routed expert FFN at the bf16 MFMA peak or the
+    HBM peak, whichever is longer."""
+    t_mfma = ffn_flops(p, R, shared=False) / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = ffn_bytes(p, R, active_experts, shared=False) / (PEAK_HBM_GBS * 1e9)
+    return (t_mfma, "mfma") if t_mfma >= t_hbm else (t_hbm, "hbm")
 
 
 def ffn_mx_bytes(p: Preset, R: int, active_experts: int) -> float:
