@@ -442,8 +442,11 @@ def layer_fwd(p, inp, keep_hidden: bool = False):
     return out
 
 
-def expert_bwd(X, h, a, W13e, W2e, dO, act):
-    """Backward of o = act(X W13^T) W2^T for one expert; returns dX, dW13, dW2."""
+def expert_bwd(X, h, a, W13e, W2e, dO, act, dH_in=None, keep_dH=False):
+    """Backward of o = act(X W13^T) W2^T for one expert; returns dX, dW13, dW2
+    (and the pre-activation gradient dH when keep_dH).  With dH_in given, dX
+    and dW13 are formed from it instead of from the dH computed here (each
+    product checked on another implementation's own dH)."""
     dA = dO @ np.asarray(W2e, F64)
     dW2 = dO.T @ a
     if act == "swiglu":
@@ -456,9 +459,10 @@ def expert_bwd(X, h, a, W13e, W2e, dO, act):
         phi = np.exp(-0.5 * h * h) / math.sqrt(2.0 * math.pi)
         Phi = 0.5 * (1.0 + erf(h / math.sqrt(2.0)))
         dH = dA * (Phi + h * phi)
-    dX = dH @ np.asarray(W13e, F64)
-    dW13 = dH.T @ np.asarray(X, F64)
-    return dX, dW13, dW2
+    dHu = dH if dH_in is None else np.asarray(dH_in, F64)
+    dX = dHu @ np.asarray(W13e, F64)
+    dW13 = dHu.T @ np.asarray(X, F64)
+    return (dX, dW13, dW2, dH) if keep_dH else (dX, dW13, dW2)
 
 
 def router_bwd(p, s, z, idx, counts, dg):

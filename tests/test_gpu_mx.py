@@ -93,17 +93,17 @@ def test_expert_ffn_mx_parity(name):
     torch.cuda.synchronize()
     offsets = pm["offsets"].cpu().numpy().astype(np.int64)
     sizes = np.diff(offsets)
-    order = np.argsort(sizes)
-    sample = sorted({int(order[-1]), int(order[len(order) // 2]), p.E - 1} - {e for e in range(p.E) if sizes[e] == 0})
+    experts = [e for e in range(p.E) if sizes[e] > 0]
     xq_h, xs_h = _act_rows(xq.cpu().numpy()), xs.cpu().numpy()
     aq_h, aqs_h = _act_rows(res["aq"].cpu().numpy()), res["aqs"].cpu().numpy()
     out_h = res["out"].cpu().numpy()
     W13q_h, W13s_h = W13q.cpu().numpy(), W13s.cpu().numpy()
     W2q_h, W2s_h = W2q.cpu().numpy(), W2s.cpu().numpy()
     worst_out, near_boundary, codes_off = 0.0, 0, 0
-    for e in sample:
+    print(f"[mx] {name}: oracle on all {int(offsets[-1])} rows of {len(experts)} experts", flush=True)
+    for e in experts:
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        rows = np.arange(r0, min(r1, r0 + 64))
+        rows = np.arange(r0, r1)
         xd = orc.mx_dequantize(xq_h[rows].astype(np.int64), xs_h[:, rows].T.astype(np.int64), 64, "e4m3")
         c13, s13 = _w_oracle(W13q_h[e], W13s_h[e])
         W13d = orc.mx_dequantize(c13, s13, 32, "e2m1")
@@ -136,8 +136,8 @@ def test_expert_ffn_mx_parity(name):
         err = np.abs(out_h[rows] - ref)
         worst_out = max(worst_out, float(np.max(err / (cond + 1e-30))))
         assert np.all(err <= 2e-4 * cond + 1e-6 * np.sqrt(np.mean(ref ** 2))), f"expert {e}: output"
-    print(f"{name}: experts {sample}, output err/sum|terms| {worst_out:.2e}, boundary blocks {near_boundary}, "
-          f"codes one step off {codes_off}")
+    print(f"{name}: every row of {len(experts)} experts, output err/sum|terms| {worst_out:.2e}, "
+          f"boundary blocks {near_boundary}, codes one step off {codes_off}")
 
 
 def test_fp8_activation_codes_at_every_rounding_midpoint():

@@ -9,11 +9,12 @@ Bars (written per test):
   * dispatch: counts, offsets, row_of_slot, token_of_row and x_perm bit-exact;
   * expert FFN and layer output: max-abs error <= 2e-2 * RMS(reference) for
     bf16 experts, <= 1e-4 absolute and <= 1e-4 * RMS for the fp32 layer; the
-    short-K expert cases also bound every output by 2^-7 times its sum of
-    absolute terms |a| |W2|^T (the bf16 activation is one rounding of 2^-9;
-    replaying that rounding in float64 gives at most 1.8e-3).
-Full-size presets are checked on sampled rows/tokens the oracle computes one
-by one; the tiny fp32 preset is checked everywhere.
+    expert FFN also bounds every output by 2^-7 times its sum of absolute
+    terms |a| |W2|^T (the bf16 activation is one rounding, relative 2^-8 at
+    most; replaying that rounding in float64 gives at most 1.8e-3).
+The expert FFN and the layer output are checked on every routed row and every
+token at the full workload sizes; the routing studies and variant routers'
+layer outputs on sampled tokens.
 """
 
 import math
@@ -154,6 +155,31 @@ def test_permute_ragged_and_drops(T, k, cf):
     _check_dispatch(p, x, idx, orc.capacity(T, p.E, k, cf))
 
 
+@pytest.mark.parametrize("k,priority", [(2, "token"), (3, "token"), (8, "token"), (3, "slot")])
+def test_permute_duplicate_ids(k, priority):
+    """A token may list one expert in several slots (the dispatch step does not
+    require distinct ids): every slot is routed and ranked in (token, slot)
+    order, or (slot, token) order under slot priority, as the oracle does."""
+    p = presets.get("c1", T=700, k=k, capacity_factor=0.9, priority=priority)
+    rng = np.random.default_rng(11 + k)
+    idx = rng.integers(0, p.E, size=(p.T, k))
+    idx[::5, 1] = idx[::5, 0]                     # a duplicate in every fifth token
+    idx[::13, :] = 3                              # tokens that list expert 3 k times
+    assert any(len(set(r)) < k for r in idx.tolist())
+    x = torch.randn(p.T, p.d, device=DEV)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    out = B.permute(p, x, idx_t)
+    torch.cuda.synchronize()
+    C = orc.capacity(p.T, p.E, k, p.capacity_factor)
+    counts, offsets, ros, tor = orc.dispatch(idx, p.E, C, priority=priority)
+    R = int(offsets[-1])
+    np.testing.assert_array_equal(out["counts"].cpu().numpy(), counts)
+    np.testing.assert_array_equal(out["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(out["row_of_slot"].cpu().numpy(), ros)
+    np.testing.assert_array_equal(out["token_of_row"].cpu().numpy()[:R], tor[:R])
+    assert torch.equal(out["x_perm"][:R], x[torch.from_numpy(tor[:R]).to(DEV)])
+
+
 def test_permute_ignores_out_of_range_experts():
     p = presets.get("c1", T=300)
     rng = np.random.default_rng(5)
@@ -166,24 +192,27 @@ def test_permute_ignores_out_of_range_experts():
 
 
 # --------------------------------------------------------------------------- expert FFN
-def _sample_rows(offsets, rng, per_group=3):
-    rows = []
-    for e in range(len(offsets) - 1):
-        r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        if r1 > r0:
-            rows += [r0, r1 - 1] + list(rng.integers(r0, r1, size=per_group))
-    return np.unique(np.array(rows, np.int64))
+# Oracle expert outputs of (token, expert) pairs, per workload: the expert-FFN
+# test stores every routed row's output, and the layer test of the same
+# workload reads them back instead of recomputing the whole FFN in float64.
+_O_CACHE = {}
 
 
-def _ffn_rows(p, inp, xp, offsets, rows, W13=None, W2=None, act=None):
-    W13 = inp["W13"] if W13 is None else W13
-    W2 = inp["W2"] if W2 is None else W2
-    grp = np.searchsorted(offsets, rows, side="right") - 1
-    out = np.zeros((len(rows), W2.shape[1]))
-    for e in np.unique(grp):
-        sel = grp == e
-        out[sel] = orc.expert_ffn(xp[sel], np.array([0, int(sel.sum())]), W13[e:e + 1], W2[e:e + 1],
-                                  act or p.act)
+def _oracle_pairs(name, p, inp, toks, exps):
+    """Oracle FFN output [n, d] of expert exps[i] on token toks[i] (cached)."""
+    keys = toks.astype(np.int64) * p.E + exps.astype(np.int64)
+    ck, co = _O_CACHE.get(name, (np.zeros(0, np.int64), np.zeros((0, p.d))))
+    out = np.empty((len(keys), p.d))
+    hit = np.zeros(len(keys), bool)
+    if len(ck):
+        pos = np.minimum(np.searchsorted(ck, keys), len(ck) - 1)
+        hit = ck[pos] == keys
+        out[hit] = co[pos[hit]]
+    for e in np.unique(exps[~hit]):
+        sel = ~hit & (exps == e)
+        n = int(sel.sum())
+        out[sel] = orc.expert_ffn(inp["x"][toks[sel]], np.array([0, n]), inp["W13"][e:e + 1],
+                                  inp["W2"][e:e + 1], p.act)
     return out
 
 
@@ -194,8 +223,34 @@ def _assert_bf16_close(got, ref, what):
     return err / rms
 
 
+def _check_ffn_all_rows(name, p, inp, xp, offsets, o, what, store=False):
+    """Every routed row: max-abs <= 2e-2 * RMS (the benchmark spec) and, elementwise,
+    within 2^-7 of the output's sum of absolute terms |a| |W2|^T.  The kernel's
+    deviation is the one bf16 rounding of the stored activation (relative
+    2^-8 at most) plus fp32 accumulation, so 2^-7 keeps a 2x margin."""
+    R = int(offsets[-1])
+    o_ref = np.zeros((R, p.d))
+    worst = 0.0
+    for e in range(len(offsets) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        oe, _, ae = orc.expert_ffn(xp[r0:r1], np.array([0, r1 - r0]), inp["W13"][e:e + 1],
+                                   inp["W2"][e:e + 1], p.act, keep_hidden=True)
+        cond = np.abs(ae[0]) @ np.abs(inp["W2"][e].astype(np.float64)).T
+        ratio = np.abs(o[r0:r1] - oe) / (2.0 ** -7 * cond + 1e-30)
+        worst = max(worst, float(ratio.max()))
+        assert ratio.max() <= 1.0, f"{what} expert {e}: {int((ratio > 1).sum())} outputs off"
+        o_ref[r0:r1] = oe
+    r = _assert_bf16_close(o, o_ref, what)
+    return r, worst, o_ref
+
+
 @pytest.mark.parametrize("name", ALL)
 def test_expert_ffn_parity(name):
+    """The routed expert FFN on every kept row at the full workload sizes (the
+    tile shapes the layer runs with), on the GPU's own x_perm (checked
+    bit-exact against the token rows by the dispatch tests)."""
     p, inp, x, w = case(name)
     ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
                     inp["sel_bias"])
@@ -206,19 +261,22 @@ def test_expert_ffn_parity(name):
     torch.cuda.synchronize()
     offsets = pm["offsets"].cpu().numpy()
     R = int(offsets[-1])
+    tor = pm["token_of_row"][:R].cpu().numpy().astype(np.int64)
+    o = res["out"][:R].cpu().numpy().astype(np.float64)
+    print(f"[ffn] {name}: oracle on all {R} rows", flush=True)
+    xp = inp["x"][tor]
     if p.dtype == "f32":
-        rows = np.arange(R)
-    else:
-        rows = _sample_rows(offsets, np.random.default_rng(1))
-    xp = pm["x_perm"][torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
-    o_ref = _ffn_rows(p, inp, xp, offsets, rows)
-    o = res["out"][torch.from_numpy(rows).to(DEV)].cpu().numpy()
-    if p.dtype == "f32":
+        o_ref = orc.expert_ffn(xp, offsets, inp["W13"], inp["W2"], p.act)
         err = np.max(np.abs(o - o_ref))
         assert err <= 1e-4 and err <= 1e-4 * np.sqrt(np.mean(o_ref ** 2)), err
-    else:
-        r = _assert_bf16_close(o, o_ref, f"{name} expert out")
-        print(f"{name}: expert FFN max-abs/rms {r:.2e} on {len(rows)} rows")
+        return
+    r, worst, o_ref = _check_ffn_all_rows(name, p, inp, xp, offsets, o, f"{name} expert out")
+    exps = np.repeat(np.arange(p.E), np.diff(offsets))
+    keys = tor * p.E + exps
+    order = np.argsort(keys)
+    _O_CACHE[name] = (keys[order], o_ref[order])
+    print(f"{name}: expert FFN max-abs/rms {r:.2e}, worst elementwise {worst:.2f} of the "
+          f"2^-7 bound, on all {R} rows")
 
 
 @pytest.mark.parametrize("name,over", [
@@ -230,7 +288,13 @@ def test_expert_ffn_parity(name):
     # 256 experts, many of them empty; down K = 128
     ("c5", dict(T=500, d=256, F=128)),
     # K = 384 (six stages), row tiles that end mid-tile
-    ("c3", dict(T=700, d=384, F=384))])
+    ("c3", dict(T=700, d=384, F=384)),
+    # the large-tile shapes (every row, as above): about 256 rows per expert
+    # -> 256x128 SwiGLU up tiles with two weight panels and 128x256 down tiles;
+    # ragged experts end in row tiles whose second 128-row half is empty
+    ("c4", dict(T=1024, k=2, E=8, d=256, F=256, F_shared=0)),
+    # 512 rows per expert -> 256x128 GELU up tiles and 256x256 down tiles
+    ("c2", dict(T=4096, E=8, d=4096, F=128))])
 def test_expert_ffn_short_k(name, over):
     p, inp, x, w = case(name, **over)
     ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
@@ -244,19 +308,10 @@ def test_expert_ffn_short_k(name, over):
     offsets = pm["offsets"].cpu().numpy()
     R = int(offsets[-1])
     xp = pm["x_perm"][:R].float().cpu().numpy()
-    o_ref, _, a_ref = orc.expert_ffn(xp, offsets, inp["W13"], inp["W2"], p.act, keep_hidden=True)
     o = res["out"][:R].cpu().numpy()
-    r = _assert_bf16_close(o, o_ref, f"{name} {over} expert out")
-    # Elementwise: the kernel stores the activation a in bf16 (one RNE
-    # rounding, relative error <= 2^-9) and accumulates in fp32, so each
-    # output is within a few 2^-9 of its sum of absolute terms |a| |W2|^T.
-    for e in range(p.E):
-        r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        if r1 > r0:
-            cond = np.abs(a_ref[e]) @ np.abs(inp["W2"][e].astype(np.float64)).T
-            bad = np.abs(o[r0:r1] - o_ref[r0:r1]) > 2.0 ** -7 * cond + 1e-30
-            assert not bad.any(), f"{name} {over} expert {e}: {int(bad.sum())} outputs off"
-    print(f"{name} {over}: expert FFN max-abs/rms {r:.2e} on all {R} rows", flush=True)
+    r, worst, _ = _check_ffn_all_rows(name, p, inp, xp, offsets, o, f"{name} {over} expert out")
+    print(f"{name} {over}: expert FFN max-abs/rms {r:.2e}, worst {worst:.2f} of the 2^-7 "
+          f"bound, on all {R} rows", flush=True)
 
 
 # --------------------------------------------------------------------------- combine
@@ -319,11 +374,22 @@ def test_layer_fwd_parity(name):
         rms = np.sqrt(np.mean(ref["y"] ** 2))
         assert err <= 1e-4 and err <= 1e-4 * rms, (err, rms)
         return
-    rng = np.random.default_rng(2)
-    tokens = np.unique(np.concatenate([[0, p.T - 1], rng.integers(0, p.T, size=48)]))
-    y_ref = _layer_ref_sampled(p, inp, saved, tokens)
-    r = _assert_bf16_close(y[tokens], y_ref, f"{name} y")
-    print(f"{name}: layer y max-abs/rms {r:.2e} on {len(tokens)} tokens; drops {drops}")
+    # every token: y_t = sum over kept slots of g_tj E_idx(x_t) (+ the shared
+    # expert), on the GPU's routing, gates from the oracle's scores
+    R = int(offsets[-1])
+    tor_g = saved["token_of_row"][:R].cpu().numpy().astype(np.int64)
+    exps = np.repeat(np.arange(p.E), np.diff(offsets))
+    print(f"[layer] {name}: oracle on all {p.T} tokens ({R} routed rows)", flush=True)
+    o_ref = _oracle_pairs(name, p, inp, tor_g, exps)
+    _O_CACHE.pop(name, None)
+    r = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],
+                  inp["sel_bias"])
+    g = orc.gates(r["s"], idx_g, p.renorm, p.gate_scale)
+    y_ref = orc.combine(o_ref, ros, g)
+    if p.F_shared:
+        y_ref += orc.shared_expert(inp["x"], inp["Ws13"], inp["Ws2"])
+    r_ = _assert_bf16_close(y, y_ref, f"{name} y")
+    print(f"{name}: layer y max-abs/rms {r_:.2e} on all {p.T} tokens; drops {drops}")
 
 
 # --------------------------------------------------------------------------- routing studies
