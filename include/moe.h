@@ -112,11 +112,21 @@ typedef enum { MOE_PRIORITY_TOKEN = 0, MOE_PRIORITY_SLOT = 1 } moe_priority;
  * renorm != 0: kept gates are divided by their sum, then multiplied by gate_scale;
  * capacity_factor <= 0: no capacity limit, else C = ceil(cf * T * k / E) slots per expert;
  * aux_coef, z_coef: load-balance and z-loss coefficients (0 = not computed);
- * routing: moe_routing (0 = top-k); priority: moe_priority (0 = token order). */
+ * routing: moe_routing (0 = top-k); priority: moe_priority (0 = token order);
+ * act_pair (bf16 only; 0 or 1): the routed experts' activation reaches the down
+ *   projection as a pair of bf16 values, hi = bf16(a) and lo = bf16(a - hi)
+ *   (about 16 significant bits instead of 8), at twice the down projection's
+ *   work and activation bytes; the saved activation `a` is then [rows, 2F]
+ *   (hi | lo per row) and the weight gradient of W2 uses hi.  Selective
+ *   precision in the sense of "Switch Transformers": for layers whose gates
+ *   are raw router probabilities (top-1 without renormalisation) the single
+ *   bf16 rounding of a, scaled by the few largest gates, dominates the
+ *   output error. */
 typedef struct {
   int32_t score, act, dtype, renorm;
   float gate_scale, capacity_factor, aux_coef, z_coef;
   int32_t routing, priority;
+  int32_t act_pair;
 } moe_opts;
 
 /* Per-call inputs of the variant routers (device pointers, fp32 unless noted).
@@ -151,7 +161,7 @@ typedef struct {
   int32_t* token_of_row; /* [T*k] token of each row (entries >= R unspecified) */
   void* x_perm;          /* [T*k, d] expert-contiguous copy of x */
   void* h;               /* [T*k, n_up] expert pre-activations */
-  void* a;               /* [T*k, F] expert activations */
+  void* a;               /* [T*k, F] expert activations ([T*k, 2F] with opts.act_pair) */
   float* o;              /* [T*k, d] expert outputs */
   void* h_shared;        /* [T, 2*F_shared] (when F_shared > 0) */
   void* a_shared;        /* [T, F_shared]   (when F_shared > 0) */
@@ -222,8 +232,9 @@ int moe_permute(const moe_dims* dims, const moe_opts* opts, const void* x,
  * through act(x W13[g]^T) W2[g]^T with width F (act: SwiGLU with the gate/up
  * projections fused, or exact GELU).  out [max_rows, d] fp32.  max_rows is an
  * upper bound of offsets[n_groups] used to size the launch.  h_save
- * [max_rows, n_up] and a_save [max_rows, F] (nullable) receive the
- * pre-activation and the activation in the x element type. */
+ * [max_rows, n_up] and a_save [max_rows, F] ([max_rows, 2F] with
+ * opts.act_pair) (nullable) receive the pre-activation and the activation in
+ * the x element type. */
 int moe_expert_ffn(const moe_dims* dims, const moe_opts* opts, int64_t n_groups,
                    int64_t max_rows, int64_t F, const void* x_perm, const int32_t* offsets,
                    const void* W13, const void* W2, void* h_save, void* a_save, float* out,

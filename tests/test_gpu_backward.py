@@ -214,7 +214,9 @@ def test_layer_bwd_full_size(name, over):
     X64 = inp["x"].astype(np.float64)
     dy32 = inp["dy"].astype(np.float32)
     dy = dy32.astype(np.float64)
-    h_all, a_all, dH_all = _np(saved["h"], R), _np(saved["a"], R), _np(g["dH"], R)
+    # the saved activation (its hi half when the layer carries (hi, lo) pairs:
+    # the weight gradient of W2 uses hi)
+    h_all, a_all, dH_all = _np(saved["h"], R), _np(saved["a"], R)[:, :F], _np(g["dH"], R)
 
     # router gradient on the GPU's routing and expert outputs
     r = orc.route(inp["x"], inp["Wg"], k, p.score, p.renorm, p.gate_scale, inp["offset"],

@@ -294,7 +294,10 @@ def test_expert_ffn_parity(name):
     # ragged experts end in row tiles whose second 128-row half is empty
     ("c4", dict(T=1024, k=2, E=8, d=256, F=256, F_shared=0)),
     # 512 rows per expert -> 256x128 GELU up tiles and 256x256 down tiles
-    ("c2", dict(T=4096, E=8, d=4096, F=128))])
+    ("c2", dict(T=4096, E=8, d=4096, F=128)),
+    # the activation as one bf16 rounding (GELU), and as (hi, lo) pairs (SwiGLU)
+    ("c2", dict(T=300, d=128, F=128, act_pair=False)),
+    ("c4", dict(T=200, d=128, F=256, act_pair=True))])
 def test_expert_ffn_short_k(name, over):
     p, inp, x, w = case(name, **over)
     ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],

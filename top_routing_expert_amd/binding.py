@@ -44,7 +44,7 @@ class Opts(C.Structure):
     _fields_ = [("score", C.c_int32), ("act", C.c_int32), ("dtype", C.c_int32),
                 ("renorm", C.c_int32), ("gate_scale", C.c_float),
                 ("capacity_factor", C.c_float), ("aux_coef", C.c_float), ("z_coef", C.c_float),
-                ("routing", C.c_int32), ("priority", C.c_int32)]
+                ("routing", C.c_int32), ("priority", C.c_int32), ("act_pair", C.c_int32)]
 
 
 class RouterInputs(C.Structure):
@@ -136,7 +136,14 @@ def dims_of(p: Preset, T: Optional[int] = None) -> Dims:
 
 def opts_of(p: Preset) -> Opts:
     return Opts(SCORE[p.score], ACT[p.act], DTYPE[p.dtype], int(p.renorm), p.gate_scale,
-                p.capacity_factor, p.aux_coef, p.z_coef, ROUTING[p.routing], PRIORITY[p.priority])
+                p.capacity_factor, p.aux_coef, p.z_coef, ROUTING[p.routing], PRIORITY[p.priority],
+                int(p.act_pair))
+
+
+def act_cols(p: Preset, F: Optional[int] = None) -> int:
+    """Columns of the saved routed activation: F, or 2F for bf16 (hi, lo) pairs."""
+    F = p.F if F is None else F
+    return 2 * F if (p.act_pair and p.dtype == "bf16") else F
 
 
 def capacity(p: Preset, T: Optional[int] = None) -> int:
@@ -230,9 +237,9 @@ def expert_ffn(p: Preset, x_perm, offsets, W13, W2, *, max_rows=None, F=None, ac
     _need(W2, "W2", (G, p.d, F), TORCH_DTYPE[p.dtype], dev)
     out = torch.empty(max(rows, 1), p.d, dtype=torch.float32, device=dev)
     h = torch.empty(max(rows, 1), nu, dtype=x_perm.dtype, device=dev) if save_hidden else None
-    a = torch.empty(max(rows, 1), F, dtype=x_perm.dtype, device=dev) if save_hidden else None
+    a = torch.empty(max(rows, 1), act_cols(q, F), dtype=x_perm.dtype, device=dev) if save_hidden else None
     ws = ws or Workspace(dev)
-    nb = workspace_size(q) + rows * F * (2 if p.dtype == "bf16" else 4) + 4096
+    nb = workspace_size(q) + rows * act_cols(q, F) * (2 if p.dtype == "bf16" else 4) + 4096
     buf = ws.get(nb)
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         C.byref(dims_of(q)), C.byref(opts_of(q)), G, rows, F, _ptr(x_perm), _ptr(offsets),
@@ -313,7 +320,7 @@ def alloc_saved(p: Preset, device, T: Optional[int] = None) -> dict:
     s = dict(topk_idx=e(T, p.k, dt=torch.int32), topk_gate=e(T, p.k), logits=e(T, p.E),
              counts=e(p.E, dt=torch.int32), offsets=e(p.E + 1, dt=torch.int32),
              row_of_slot=e(T, p.k, dt=torch.int32), token_of_row=e(Tk, dt=torch.int32),
-             x_perm=e(Tk, p.d, dt=xd), h=e(Tk, nu, dt=xd), a=e(Tk, p.F, dt=xd), o=e(Tk, p.d),
+             x_perm=e(Tk, p.d, dt=xd), h=e(Tk, nu, dt=xd), a=e(Tk, act_cols(p), dt=xd), o=e(Tk, p.d),
              h_shared=e(T, 2 * p.F_shared, dt=xd) if p.F_shared else None,
              a_shared=e(T, p.F_shared, dt=xd) if p.F_shared else None, losses=e(2),
              noise_logits=e(T, p.E) if p.routing == "noisy_topk" else None)

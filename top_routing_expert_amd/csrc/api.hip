@@ -30,6 +30,9 @@ struct Carver {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int elem_bytes(const moe_opts* o) { return o->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+// The routed experts' activation as a bf16 (hi, lo) pair: 2F columns per row.
+bool act_pair(const moe_opts* o) { return o->act_pair && o->dtype == MOE_DTYPE_BF16; }
+int64_t act_cols(const moe_opts* o, int64_t F) { return act_pair(o) ? 2 * F : F; }
 int64_t n_up(const moe_opts* o, int64_t F) { return o->act == MOE_ACT_SWIGLU ? 2 * F : F; }
 
 int check_width(const moe_opts* o, int64_t v) {
@@ -46,6 +49,7 @@ int check_dims(const moe_dims* d, const moe_opts* o) {
   if (o->priority != MOE_PRIORITY_TOKEN && o->priority != MOE_PRIORITY_SLOT) return MOE_ERR_INVALID_ARG;
   if (o->routing == MOE_ROUTING_RANDOM_SECOND && d && d->k != 2) return MOE_ERR_INVALID_ARG;
   if (o->act != MOE_ACT_SWIGLU && o->act != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
+  if (o->act_pair != 0 && o->act_pair != 1) return MOE_ERR_INVALID_ARG;
   if (d->T < 0 || d->E < 1 || d->k < 1 || d->k > d->E || d->F_shared < 0) return MOE_ERR_INVALID_ARG;
   if (!isfinite(o->gate_scale) || !isfinite(o->capacity_factor) || !isfinite(o->aux_coef) ||
       !isfinite(o->z_coef))
@@ -128,11 +132,12 @@ PermWs plan_perm(Carver& c, const moe_dims* d, const moe_opts* o) {
 }
 
 struct FfnWs { size_t tile_up, tile_down, act; };
-FfnWs plan_ffn(Carver& c, int64_t G, int64_t max_rows, int64_t F, int eb, bool need_act) {
+// a_cols: columns of the activation buffer (F, or 2F for bf16 pairs)
+FfnWs plan_ffn(Carver& c, int64_t G, int64_t max_rows, int64_t a_cols, int eb, bool need_act) {
   FfnWs f;
   f.tile_up = c.take(size_t(G + 1) * 4);
   f.tile_down = c.take(size_t(G + 1) * 4);
-  f.act = need_act ? c.take(size_t(max_rows) * F * eb) : 0;
+  f.act = need_act ? c.take(size_t(max_rows) * a_cols * eb) : 0;
   return f;
 }
 
@@ -157,7 +162,7 @@ FwdWs plan_fwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   f.ros = c.take(size_t(Tk) * 4);
   f.tor = c.take(size_t(Tk) * 4);
   f.xperm = c.take(size_t(Tk) * d->d * eb);
-  f.a = c.take(size_t(Tk) * d->F * eb);
+  f.a = c.take(size_t(Tk) * act_cols(o, d->F) * eb);
   f.o = c.take(size_t(Tk) * d->d * 4);
   f.as = c.take(size_t(d->T) * d->F_shared * eb);
   f.os = c.take(size_t(d->T) * d->d * 4);
@@ -267,10 +272,13 @@ int do_permute(const moe_dims* d, const moe_opts* o, const void* x, const int32_
   return MOE_OK;
 }
 
+// pair: the activation as bf16 (hi, lo) pairs, a_buf [max_rows, 2F] (bf16 only)
 int do_ffn(const moe_opts* o, int64_t d, int64_t G, int64_t max_rows, int64_t F, int act,
            const void* xperm, const int32_t* offsets, const void* W13, const void* W2,
-           void* h_save, void* a_buf, float* out, void* ws, const FfnWs& fw, hipStream_t st) {
+           void* h_save, void* a_buf, float* out, void* ws, const FfnWs& fw, hipStream_t st,
+           bool pair = false) {
   const bool bf16 = o->dtype == MOE_DTYPE_BF16;
+  pair = pair && bf16;
   const int64_t nu = act == MOE_ACT_SWIGLU ? 2 * F : F;
   GemmArgs g{};
   g.A = xperm;
@@ -287,13 +295,20 @@ int do_ffn(const moe_opts* o, int64_t d, int64_t G, int64_t max_rows, int64_t F,
   g.h_save = h_save;
   g.n_b = int(nu);
   g.tile_start = at<int32_t>(ws, fw.tile_up);
+  if (pair) {
+    g.out_ld = int(2 * F);
+    g.lo_off = int(F);
+  }
   MOE_TRY(bf16 ? launch_grouped_gemm_bf16(g, st) : launch_grouped_gemm_f32(g, st));
   GemmArgs g2 = g;
   g2.A = a_buf;
   g2.B = W2;
   g2.b_group_stride = d * F;
   g2.N = int(d);
-  g2.K = int(F);
+  g2.K = int(pair ? 2 * F : F);
+  g2.b_kwrap = pair ? int(F) : 0;
+  g2.out_ld = 0;
+  g2.lo_off = 0;
   g2.up_off = 0;
   g2.epi = EPI_STORE_F32;
   g2.out = out;
@@ -557,12 +572,12 @@ int moe_expert_ffn(const moe_dims* d, const moe_opts* o, int64_t n_groups, int64
   if (!aligned16(x_perm) || !aligned16(W13) || !aligned16(W2) || !aligned16(out))
     return MOE_ERR_INVALID_ARG;
   Carver c;
-  const FfnWs fw = plan_ffn(c, n_groups, max_rows, F, elem_bytes(o), a_save == nullptr);
+  const FfnWs fw = plan_ffn(c, n_groups, max_rows, act_cols(o, F), elem_bytes(o), a_save == nullptr);
   if ((s = check_ws(ws, ws_bytes, c.off))) return s;
   if (max_rows == 0) return MOE_OK;
   void* a_buf = a_save ? a_save : at<void>(ws, fw.act);
   return do_ffn(o, d->d, n_groups, max_rows, F, o->act, x_perm, offsets, W13, W2, h_save, a_buf,
-                out, ws, fw, static_cast<hipStream_t>(stream));
+                out, ws, fw, static_cast<hipStream_t>(stream), act_pair(o));
 }
 
 int moe_combine(const moe_dims* d, const float* out_perm, const int32_t* row_of_slot,
@@ -648,7 +663,7 @@ int moe_layer_fwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
                  ws, f.perm, st);
   if (s) return joined(s);
   s = do_ffn(o, d->d, d->E, d->T * d->k, d->F, o->act, xperm, offsets, w->W13, w->W2,
-             sv ? sv->h : nullptr, abuf, obuf, ws, f.ffn, st);
+             sv ? sv->h : nullptr, abuf, obuf, ws, f.ffn, st, act_pair(o));
   if (s) return joined(s);
   if (side) MOE_TRY(stream_wait(st, side->s, side->join));
   MOE_TRY(launch_combine(obuf, ros, gate, shared, int(d->T), int(d->k), int(d->d), y, st));
@@ -797,7 +812,10 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
     // routed experts' dW2[e] = dO_e^T a_e needs only combine backward's dO: its
     // fp32 stores run here, beside the data gradients' weight reads and
     // products (the K-grouped mode reads no tile table)
-    MOE_TRY(gemm_on(o, gemm_wgrad(at<void>(ws, b.dO), sv->a, sv->offsets, E, D, F, grads->dW2), ts_s, bs));
+    // (with activation pairs the saved rows are [hi | lo]; dW2 uses hi)
+    GemmArgs gw2 = gemm_wgrad(at<void>(ws, b.dO), sv->a, sv->offsets, E, D, F, grads->dW2);
+    gw2.ldb = act_cols(o, F);
+    MOE_TRY(gemm_on(o, gw2, ts_s, bs));
     return MOE_OK;
   };
   auto routed_branch = [&]() -> int {
@@ -866,6 +884,7 @@ int moe_expert_ffn_mx(const moe_dims* d, const moe_opts* o, int64_t n_groups, in
       a_stride % 4)
     return MOE_ERR_INVALID_ARG;
   if (o->act != MOE_ACT_SWIGLU && o->act != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
+  if (o->act_pair != 0 && o->act_pair != 1) return MOE_ERR_INVALID_ARG;
   if (d->d % 256 || F % 256) return MOE_ERR_UNSUPPORTED;
   if (max_rows == 0) return MOE_OK;
   if (!xq || !xs || !offsets || !W13q || !W13s || !W2q || !W2s || !aq || !aqs || !out)

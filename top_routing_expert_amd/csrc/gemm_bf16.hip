@@ -82,6 +82,21 @@ __device__ __forceinline__ void st_u2(uint16_t* p, uint2 v) {
   else *reinterpret_cast<uint2*>(p) = v;
 }
 
+// Four activations of one row as bf16: hi = bf16(a) in rows of out_ld (or N)
+// elements, and with lo_off the remainders lo = bf16(a - hi) at lo_off + n
+// (a - hi is exact in fp32; hi + lo carries a to about 16 significant bits).
+template <bool NT>
+__device__ __forceinline__ void store_act(const GemmArgs& g, int64_t row, int n, float4 a) {
+  const uint32_t h01 = pack_bf2(a.x, a.y), h23 = pack_bf2(a.z, a.w);
+  uint16_t* orow = static_cast<uint16_t*>(g.out) + row * (g.out_ld ? g.out_ld : g.N);
+  st_u2<NT>(orow + n, make_uint2(h01, h23));
+  if (g.lo_off) {
+    const float l0 = a.x - __uint_as_float(h01 << 16), l1 = a.y - __uint_as_float(h01 & 0xffff0000u);
+    const float l2 = a.z - __uint_as_float(h23 << 16), l3 = a.w - __uint_as_float(h23 & 0xffff0000u);
+    st_u2<NT>(orow + g.lo_off + n, make_uint2(pack_bf2(l0, l1), pack_bf2(l2, l3)));
+  }
+}
+
 // 16 zero bytes: the load source of K rows past the end of a group.
 __device__ uint4 g_zero16;
 
@@ -212,6 +227,8 @@ void gg_bf16_kernel(GemmArgs g) {
   }
   // Row stride of a K-major B: [rows, ldb] in the K-grouped mode, [K, N] otherwise.
   const int64_t ldb = (MODE == GM_KGROUP && g.ldb) ? g.ldb : int64_t(g.N);
+  // K-contiguous B (forward layout): row stride, the K period when B wraps
+  const int64_t ldbk = (MODE == GM_NT && g.b_kwrap) ? int64_t(g.b_kwrap) : int64_t(g.K);
   TileCoord tc;
   int K;                                     // reduction length of this tile
   const uint16_t* A;
@@ -269,11 +286,11 @@ void gg_bf16_kernel(GemmArgs g) {
       kmajor_slot<BN>(w + WV * i, l, b_krow[i], col);
       b_src[i] = B + int64_t(b_krow[i]) * ldb + tc.n0 + col;
     } else {
-      b_src[i] = B + int64_t(i * g.up_off + tc.n0 + 8 * w + lrow) * K + 8 * lchunk;
+      b_src[i] = B + int64_t(i * g.up_off + tc.n0 + 8 * w + lrow) * ldbk + 8 * lchunk;
       b_krow[i] = 0;
     }
   }
-  const int64_t b_step = int64_t(8 * WV) * K;   // K-contiguous B: rows between a wave's instructions
+  const int64_t b_step = int64_t(8 * WV) * ldbk;   // K-contiguous B: rows between a wave's instructions
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(&g_zero16);
 
   // Issue a stage's loads: all of them (part < 0), or the quarter whose
@@ -292,6 +309,8 @@ void gg_bf16_kernel(GemmArgs g) {
         if (mine(i)) lds_load16(a_src[i] + k0, base + (w + WV * i) * 64);
     }
     uint4* bbase = base + BM * 8;
+    // column of B's stage: k0, or k0 mod the K period when B wraps (K = 2 * period)
+    const int kb = (MODE == GM_NT && g.b_kwrap && k0 >= g.b_kwrap) ? k0 - g.b_kwrap : k0;
     if constexpr (BKM) {
       const int64_t koff = int64_t(k0) * ldb;
 #pragma unroll
@@ -306,7 +325,7 @@ void gg_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
           if (mine(A_INS + p * B_INS + i))
-            lds_load16(b_src[p] + i * b_step + k0, bbase + p * BN * 8 + (w + WV * i) * 64);
+            lds_load16(b_src[p] + i * b_step + kb, bbase + p * BN * 8 + (w + WV * i) * 64);
     }
   };
 
@@ -500,9 +519,8 @@ void gg_bf16_kernel(GemmArgs g) {
           if (g.h_save)
             st_u2<NT_H>(static_cast<uint16_t*>(g.h_save) + row * g.n_b + n,
                         make_uint2(pack_bf2(v0.x, v0.y), pack_bf2(v0.z, v0.w)));
-          st_u2<NT_OUT>(static_cast<uint16_t*>(g.out) + row * g.N + n,
-                        make_uint2(pack_bf2(gelu_fast(v0.x), gelu_fast(v0.y)),
-                                   pack_bf2(gelu_fast(v0.z), gelu_fast(v0.w))));
+          store_act<NT_OUT>(g, row, n, make_float4(gelu_fast(v0.x), gelu_fast(v0.y),
+                                                   gelu_fast(v0.z), gelu_fast(v0.w)));
         } else {
           const float4 v1 = *reinterpret_cast<const float4*>(cw + (32 + rl) * CST + c4);
           if (g.h_save) {
@@ -510,9 +528,8 @@ void gg_bf16_kernel(GemmArgs g) {
             st_u2<NT_H>(hs + n, make_uint2(pack_bf2(v0.x, v0.y), pack_bf2(v0.z, v0.w)));
             st_u2<NT_H>(hs + g.up_off + n, make_uint2(pack_bf2(v1.x, v1.y), pack_bf2(v1.z, v1.w)));
           }
-          st_u2<NT_OUT>(static_cast<uint16_t*>(g.out) + row * g.N + n,
-                        make_uint2(pack_bf2(silu_fast(v0.x) * v1.x, silu_fast(v0.y) * v1.y),
-                                   pack_bf2(silu_fast(v0.z) * v1.z, silu_fast(v0.w) * v1.w)));
+          store_act<NT_OUT>(g, row, n, make_float4(silu_fast(v0.x) * v1.x, silu_fast(v0.y) * v1.y,
+                                                   silu_fast(v0.z) * v1.z, silu_fast(v0.w) * v1.w));
         }
       }
     }
@@ -565,6 +582,8 @@ hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   }
   if (g.max_rows == 0) return hipSuccess;
   if (g.N % 128 || g.K % GB_BK) return hipErrorInvalidValue;
+  if (g.b_kwrap && (g.mode != GM_NT || g.K != 2 * g.b_kwrap || g.b_kwrap % GB_BK))
+    return hipErrorInvalidValue;
   const int64_t avg = g.max_rows / g.G;
   const bool bm256 = avg >= 192;
   const int64_t mt = cdiv(g.max_rows, bm256 ? 256 : 128);

@@ -95,6 +95,14 @@ struct GemmArgs {
   int mode;                 // GemmMode
   int M_fixed;              // K mode: rows of each group's output
   int64_t ldb;              // K mode: row stride of B in elements (0: N)
+  // Activation pairs (bf16 forward layout): the GELU / SwiGLU epilogue writes
+  // hi = bf16(a) at column n and lo = bf16(a - hi) at column lo_off + n of
+  // rows of out_ld elements (lo_off = 0: hi only, rows of N).  The down
+  // projection then runs over K = 2F with b_kwrap = F: B's element (n, k) is
+  // B[n * F + k mod F], so the weights multiply both halves.
+  int out_ld;
+  int lo_off;
+  int b_kwrap;
 };
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st);
 hipError_t launch_grouped_gemm_f32(const GemmArgs& g, hipStream_t st);

@@ -45,6 +45,7 @@ class Preset:
     bias_gamma: float = 0.0     # fixed step of the loss-free bias update (0 = off)
     routing: str = "topk"       # "topk" | "uniform" | "noisy_topk" | "gshard" | "hash"
     priority: str = "token"     # capacity overflow order: "token" (index) | "slot" (top-1 first)
+    act_pair: bool = False      # routed activation into the down projection as a bf16 (hi, lo) pair
     # ---- synthetic input recipe (all standard deviations) ----
     x_std: float = 1.0
     wg_std: float = 0.02        # router weight W_g [d, E], fp32
@@ -75,10 +76,13 @@ PRESETS = {
                  wg_std=_inv_sqrt(64), w_std=_inv_sqrt(64)),
     # Switch-style top-1 layer: GELU experts of width 4096, capacity factor
     # 1.0, the raw softmax probability of the chosen expert as its gate,
-    # aux load-balance and z losses on.
+    # aux load-balance and z losses on.  The raw gates peak at about four
+    # times their RMS, which scales the single bf16 rounding of the activation
+    # past 2e-2 of RMS(y) on a few tokens, so the activation enters the down
+    # projection as a (hi, lo) bf16 pair.
     "c2": Preset("c2", T=8192, d=1024, E=32, k=1, F=4096, act="gelu", score="softmax",
                  renorm=False, gate_scale=1.0, capacity_factor=1.0, dtype="bf16",
-                 aux_coef=1e-2, z_coef=1e-3, wg_std=0.02, w_std=0.02),
+                 aux_coef=1e-2, z_coef=1e-3, wg_std=0.02, w_std=0.02, act_pair=True),
     # Mixtral-shaped 8-expert top-2 layer, no capacity limit.
     "c3": Preset("c3", T=4096, d=4096, E=8, k=2, F=14336, act="swiglu", score="softmax",
                  renorm=True, gate_scale=1.0, capacity_factor=0.0, dtype="bf16",
