@@ -227,6 +227,23 @@ int moe_permute(const moe_dims* dims, const moe_opts* opts, const void* x,
                 int32_t* row_of_slot, int32_t* token_of_row, void* x_perm,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* moe_permute without a workspace, for callers that cannot allocate device
+ * memory or pass scratch (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * moe_permute minus ws/ws_bytes.  Its scratch (the dispatch's per-block
+ * histogram and base tables, 2 x ceil(T*k/1024) x E int32, each rounded up to
+ * 256 bytes) lives in a 1 MiB device array inside the library, one per GPU,
+ * held until the process ends; larger problems (for instance E = 256 with
+ * T*k above 524288 slots) return MOE_ERR_UNSUPPORTED before anything is
+ * enqueued.  The array keeps the last call's contents and needs no clearing.
+ * Calls that overlap on one GPU (concurrent streams, host threads) share the
+ * array and race: serialise them.  Allocates nothing and calls no allocating
+ * routine. */
+int moe_permute_noalloc(const moe_dims* dims, const moe_opts* opts, const void* x,
+                        const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                        int32_t* row_of_slot, int32_t* token_of_row, void* x_perm,
+                        void* stream);
+
 /* Expert FFNs over expert-contiguous rows (the "Making MoEs go brrr" grouped
  * computation): for group g, rows offsets[g]..offsets[g+1]-1 of x_perm go
  * through act(x W13[g]^T) W2[g]^T with width F (act: SwiGLU with the gate/up

@@ -159,3 +159,19 @@ def test_mx_entry_points_reject_bad_arguments(L):
     assert f(*args(1000, 1004, p.F)) == B.MOE_ERR_INVALID_ARG    # x_stride < max_rows + 4
     assert f(*args(1006, 1008, p.F)) == B.MOE_ERR_INVALID_ARG    # x_stride % 4
     assert f(*args(1004, 1004, 320)) == B.MOE_ERR_UNSUPPORTED    # F % 256
+
+
+def test_noalloc_permute_limit(L):
+    """moe_permute_noalloc refuses, before touching any pointer or the device,
+    problems whose dispatch tables exceed its 1 MiB scratch: with 256 experts
+    that is above 512 blocks of 1024 slots (T*k > 524288)."""
+    dummy = C.c_void_p(256)
+
+    def call(T, x):
+        p = presets.get("c5", T=T)                      # E = 256, k = 8
+        return L.moe_permute_noalloc(C.byref(B.dims_of(p)), C.byref(B.opts_of(p)), x, dummy,
+                                     dummy, dummy, dummy, dummy, dummy, None)
+
+    assert call(65536, None) == B.MOE_ERR_INVALID_ARG    # T*k = 524288 fits: a null x is refused
+    assert call(65537, dummy) == B.MOE_ERR_UNSUPPORTED   # one block of slots too many
+    assert call(1 << 20, dummy) == B.MOE_ERR_UNSUPPORTED

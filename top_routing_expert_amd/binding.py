@@ -72,6 +72,7 @@ class Stats(C.Structure):
 
 
 ABI_FUNCTIONS = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute",
+                 "moe_permute_noalloc",
                  "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd",
                  "moe_bias_update", "moe_score_histogram", "moe_bias_from_histogram",
                  "moe_router_report", "moe_mx_quantize_weights", "moe_mx_quantize_act",
@@ -95,6 +96,7 @@ def lib() -> C.CDLL:
     L.moe_route.argtypes = [D, O, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, P(RouterInputs), VP,
                             C.c_size_t, VP]
     L.moe_permute.argtypes = [D, O, VP, VP, VP, VP, VP, VP, VP, VP, C.c_size_t, VP]
+    L.moe_permute_noalloc.argtypes = [D, O, VP, VP, VP, VP, VP, VP, VP, VP]
     L.moe_expert_ffn.argtypes = [D, O, I64, I64, I64, VP, VP, VP, VP, VP, VP, VP, VP, C.c_size_t, VP]
     L.moe_combine.argtypes = [D, VP, VP, VP, VP, VP, VP]
     L.moe_layer_fwd.argtypes = [D, O, P(Weights), P(RouterInputs), VP, VP, P(Saved), P(Stats), VP,
@@ -220,6 +222,26 @@ def permute(p: Preset, x, idx, ws: Optional[Workspace] = None):
         C.byref(dims_of(p, T)), C.byref(opts_of(p)), _ptr(x), _ptr(idx), _ptr(out["counts"]),
         _ptr(out["offsets"]), _ptr(out["row_of_slot"]), _ptr(out["token_of_row"]),
         _ptr(out["x_perm"]), _ptr(buf), nb, _stream()))
+    return out
+
+
+def permute_noalloc(p: Preset, x, idx, out: Optional[dict] = None):
+    """moe_permute_noalloc (no workspace): the same outputs as permute(); `out`
+    may hold preallocated output tensors (the call itself allocates nothing)."""
+    dev = x.device
+    T = x.shape[0]
+    _need(x, "x", (T, p.d), TORCH_DTYPE[p.dtype], dev)
+    _need(idx, "idx", (T, p.k), torch.int32, dev)
+    if out is None:
+        out = dict(counts=torch.empty(p.E, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(p.E + 1, dtype=torch.int32, device=dev),
+                   row_of_slot=torch.empty(T, p.k, dtype=torch.int32, device=dev),
+                   token_of_row=torch.empty(max(T * p.k, 1), dtype=torch.int32, device=dev),
+                   x_perm=torch.empty(max(T * p.k, 1), p.d, dtype=x.dtype, device=dev))
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(
+        C.byref(dims_of(p, T)), C.byref(opts_of(p)), _ptr(x), _ptr(idx), _ptr(out["counts"]),
+        _ptr(out["offsets"]), _ptr(out["row_of_slot"]), _ptr(out["token_of_row"]),
+        _ptr(out["x_perm"]), _stream()))
     return out
 
 
