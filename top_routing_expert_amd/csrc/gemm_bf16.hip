@@ -295,8 +295,7 @@ void gg_bf16_kernel(GemmArgs g) {
 
   // Issue a stage's loads: all of them (part < 0), or the quarter whose
   // instruction index is part mod 4.
-  auto issue = [&](int stage, int k0, int part = -1) {
-    uint4* base = lds + stage * STAGE;
+  auto issue = [&](uint4* base, int k0, int part = -1) {
     auto mine = [&](int idx) { return part < 0 || (idx & 3) == part; };
     if constexpr (AK) {
       const int64_t koff = int64_t(k0) * g.M_fixed;
@@ -374,7 +373,7 @@ void gg_bf16_kernel(GemmArgs g) {
   // has just released.
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < KT) issue(j, kcol(j));
+    if (j < KT) issue(lds + j * STAGE, kcol(j));
   // Fragments of K-step s+1 are read from LDS while the MFMAs of step s run.
   constexpr int DS_PER_STEP = MI * (AK ? 2 : 1) + NP * NI * (BKM ? 2 : 1);
   bf16x8 af[2][MI], bfr[2][NP][NI];
@@ -391,68 +390,76 @@ void gg_bf16_kernel(GemmArgs g) {
     lds_barrier();
     const bool more = kt + NS - 1 < KT;
     const int knext = more ? kcol(kt + NS - 1) : 0;
-    // Forward layout: a live wave spreads the next stage's loads over the
-    // first four fragment sub-steps (a quarter each, after that sub-step's
-    // LDS reads), so they do not arrive as one burst that competes with the
-    // reads (2-4% on large products; the K-major layouts lose with it).
-    if (more && (!IL || !live)) issue(nxt, knext);
-    const uint4* As = lds + cur * STAGE;
-    const char* Ab = reinterpret_cast<const char*>(As);
-    const char* Bb = Ab + BM * 128;
-    if (live)
+    // One stage: the next stage's loads into slot `wslot` and this stage's
+    // fragment reads from slot `rslot`.  The two slots never overlap; passing
+    // them as restrict parameters of one inlined call tells the compiler so,
+    // and it then no longer waits for the loads just issued before reading
+    // fragments (which it did before every transposed LDS read).
+    auto stage = [&](uint4* __restrict__ wslot, const uint4* __restrict__ rslot) {
+      // Forward layout: a live wave spreads the next stage's loads over the
+      // first four fragment sub-steps (a quarter each, after that sub-step's LDS
+      // reads), so they do not arrive as one burst that competes with the reads
+      // (2-4% on large products; the K-major layouts lose with it).
+      if (more && (!IL || !live)) issue(wslot, knext);
+      const uint4* As = rslot;
+      const char* Ab = reinterpret_cast<const char*>(As);
+      const char* Bb = Ab + BM * 128;
+      if (live)
 #pragma unroll
-    for (int s = 0; s <= 4; ++s) {
-      if (IL && s < 4 && more) issue(nxt, knext, s);
-      if (s < 4) {
-        const int pc = (2 * s + fg) ^ (fr & 7) ^ ((fr >> 3) & 1);
+      for (int s = 0; s <= 4; ++s) {
+        if (IL && s < 4 && more) issue(wslot, knext, s);
+        if (s < 4) {
+          const int pc = (2 * s + fg) ^ (fr & 7) ^ ((fr >> 3) & 1);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          if constexpr (AK) {
-            const char* p = Ab + a_lane + a_xo[mi] + 16 * s * (2 * BM);
-            af[s & 1][mi] = lds_read_tr_pair(p, p + 4 * (2 * BM));
-          } else {
-            af[s & 1][mi] = __builtin_bit_cast(bf16x8, As[(wm * (BM / 2) + mi * 32 + fr) * 8 + pc]);
-          }
-        }
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            if constexpr (BKM) {
-              const char* q = Bb + b_lane + b_xo[ni] + 16 * s * (2 * BN);
-              bfr[s & 1][p][ni] = lds_read_tr_pair(q, q + 4 * (2 * BN));
+          for (int mi = 0; mi < MI; ++mi) {
+            if constexpr (AK) {
+              const char* p = Ab + a_lane + a_xo[mi] + 16 * s * (2 * BM);
+              af[s & 1][mi] = lds_read_tr_pair(p, p + 4 * (2 * BM));
             } else {
-              bfr[s & 1][p][ni] = __builtin_bit_cast(
-                  bf16x8, As[(BM + p * BN + wn * WTN + ni * 32 + fr) * 8 + pc]);
+              af[s & 1][mi] = __builtin_bit_cast(bf16x8, As[(wm * (BM / 2) + mi * 32 + fr) * 8 + pc]);
             }
           }
-      }
-      if (s > 0) {
-        const int q = (s - 1) & 1;
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
+          for (int p = 0; p < NP; ++p)
 #pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
+            for (int ni = 0; ni < NI; ++ni) {
+              if constexpr (BKM) {
+                const char* q = Bb + b_lane + b_xo[ni] + 16 * s * (2 * BN);
+                bfr[s & 1][p][ni] = lds_read_tr_pair(q, q + 4 * (2 * BN));
+              } else {
+                bfr[s & 1][p][ni] = __builtin_bit_cast(
+                    bf16x8, As[(BM + p * BN + wn * WTN + ni * 32 + fr) * 8 + pc]);
+              }
+            }
+        }
+        if (s > 0) {
+          const int q = (s - 1) & 1;
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-              acc[p][mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  af[q][mi], bfr[q][p][ni], acc[p][mi][ni], 0, 0, 0);
+          for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+              for (int ni = 0; ni < NI; ++ni)
+                acc[p][mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    af[q][mi], bfr[q][p][ni], acc[p][mi][ni], 0, 0, 0);
+        }
+        // Keep this order in the schedule: the LDS reads of step s, then the
+        // MFMAs of step s-1 (otherwise the scheduler sinks every read next to
+        // its use and each MFMA group waits on LDS latency).
+        if (s < 4) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_STEP, 0);
+        if constexpr (IL) {
+          // this sub-step's quarter of the loads: (INS + 3 - s) / 4 instructions
+          if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 3) / 4, 0);
+          if (s == 1) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 2) / 4, 0);
+          if constexpr ((INS + 1) / 4 > 0)
+            if (s == 2) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 1) / 4, 0);
+          if constexpr (INS / 4 > 0)
+            if (s == 3) __builtin_amdgcn_sched_group_barrier(0x020, INS / 4, 0);
+        }
+        if (s > 0) __builtin_amdgcn_sched_group_barrier(0x008, NP * MI * NI, 0);
       }
-      // Keep this order in the schedule: the LDS reads of step s, then the
-      // MFMAs of step s-1 (otherwise the scheduler sinks every read next to
-      // its use and each MFMA group waits on LDS latency).
-      if (s < 4) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_STEP, 0);
-      if constexpr (IL) {
-        // this sub-step's quarter of the loads: (INS + 3 - s) / 4 instructions
-        if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 3) / 4, 0);
-        if (s == 1) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 2) / 4, 0);
-        if constexpr ((INS + 1) / 4 > 0)
-          if (s == 2) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 1) / 4, 0);
-        if constexpr (INS / 4 > 0)
-          if (s == 3) __builtin_amdgcn_sched_group_barrier(0x020, INS / 4, 0);
-      }
-      if (s > 0) __builtin_amdgcn_sched_group_barrier(0x008, NP * MI * NI, 0);
-    }
+    };
+    stage(lds + nxt * STAGE, lds + cur * STAGE);
     // Every MFMA of this stage is issued before the next wait and barrier.
     __builtin_amdgcn_sched_barrier(0);
     cur = cur + 1 == NS ? 0 : cur + 1;
