@@ -36,7 +36,7 @@
 //    workgroup from the device-resident row offsets: no planner launch and no
 //    host synchronisation.  Rows past a group's end are clamped to its last
 //    row on load and never stored; K rows past a group's end (weight
-//    gradients) are loaded from a zero block.
+//    gradients) read as zeros (beyond the buffer descriptor's size).
 //  * Workgroups are dealt round-robin to the 8 XCDs; block b takes logical
 //    tile (b % 8) * ceil(tiles / 8) + b / 8, so each XCD works through a
 //    contiguous run of tiles (same expert, consecutive n-tiles, m-tiles
@@ -97,15 +97,27 @@ __device__ __forceinline__ void store_act(const GemmArgs& g, int64_t row, int n,
   }
 }
 
-// 16 zero bytes: the load source of K rows past the end of a group.
-__device__ uint4 g_zero16;
+// Operands are read through raw buffer descriptors (base and size in scalar
+// registers): each load instruction carries a 32-bit per-lane offset, and the
+// K advance is a scalar offset or a rebased descriptor, so no 64-bit address
+// arithmetic runs per stage.  Loads at or beyond the descriptor's size return
+// zeros (K rows past the end of a group in the weight-gradient mode).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword 3: a raw (untyped, unswizzled) buffer on CDNA
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
+  return b <= 0 ? 0u : (b >= int64_t(0xffffffff) ? 0xffffffffu : uint32_t(b));
+}
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
-// lane l writes lds_wave_base + 16*l; the LDS pointer must be wave-uniform.  (A
-// plain function: the builtin called from a lambda inside a kernel template
-// breaks the host-side instantiation.)
-__device__ __forceinline__ void lds_load16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane l writes lds_wave_base + 16*l; the LDS pointer must be
+// wave-uniform.  (A plain function: the builtin called from a lambda inside a
+// kernel template breaks the host-side instantiation.)
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, voff, soff, 0, 0);
 }
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -262,69 +274,72 @@ void gg_bf16_kernel(GemmArgs g) {
   // (l%8) ^ swz(row); the group starts at a row with (row >> 3) & 1 == w & 1.
   const int lrow = l >> 3;
   const int lchunk = (l & 7) ^ lrow ^ (w & 1);
-  const uint16_t* a_src[A_INS];
-  int a_krow[A_INS];
+  // Per-lane byte offsets of each load instruction, relative to the tile's
+  // (row modes) or the stage's (K-major operands) descriptor base.
+  uint32_t a_off[A_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
     if constexpr (AK) {
-      int col;
-      kmajor_slot<BM>(w + WV * i, l, a_krow[i], col);
-      a_src[i] = A + int64_t(a_krow[i]) * g.M_fixed + tc.m0 + col;
+      int row, col;
+      kmajor_slot<BM>(w + WV * i, l, row, col);
+      a_off[i] = uint32_t((int64_t(row) * g.M_fixed + tc.m0 + col) * 2);
     } else {
-      const int mr = min(tc.m0 + 8 * (w + WV * i) + lrow, tc.M - 1);
-      a_src[i] = A + int64_t(tc.row0 + mr) * K + 8 * lchunk;
-      a_krow[i] = 0;
+      const int mr = min(tc.m0 + 8 * (w + WV * i) + lrow, tc.M - 1) - tc.m0;
+      a_off[i] = uint32_t((int64_t(mr) * K + 8 * lchunk) * 2);
     }
   }
-  constexpr int NBS = BKM ? B_INS : NP;
-  const uint16_t* b_src[NBS];
-  int b_krow[NBS];
+  constexpr int NBS = BKM ? B_INS : NP * B_INS;
+  uint32_t b_off[NBS];
 #pragma unroll
   for (int i = 0; i < NBS; ++i) {
     if constexpr (BKM) {
-      int col;
-      kmajor_slot<BN>(w + WV * i, l, b_krow[i], col);
-      b_src[i] = B + int64_t(b_krow[i]) * ldb + tc.n0 + col;
+      int row, col;
+      kmajor_slot<BN>(w + WV * i, l, row, col);
+      b_off[i] = uint32_t((int64_t(row) * ldb + tc.n0 + col) * 2);
     } else {
-      b_src[i] = B + int64_t(i * g.up_off + tc.n0 + 8 * w + lrow) * ldbk + 8 * lchunk;
-      b_krow[i] = 0;
+      const int p = i / B_INS, ii = i % B_INS;
+      b_off[i] = uint32_t((int64_t(p * g.up_off + 8 * (w + WV * ii) + lrow) * ldbk + 8 * lchunk) * 2);
     }
   }
-  const int64_t b_step = int64_t(8 * WV) * ldbk;   // K-contiguous B: rows between a wave's instructions
-  const uint16_t* zero = reinterpret_cast<const uint16_t*>(&g_zero16);
+  // Row modes: descriptors fixed per tile (A from the tile's first row, B from
+  // the group's weights at the tile's first column), K advanced by the scalar
+  // offset.  K-major operands: rebased per stage at row k0, sized to the rows
+  // left in the group.
+  const uint16_t* a_tile = AK ? A : A + int64_t(tc.row0 + tc.m0) * K;
+  const uint16_t* b_tile = BKM ? B : B + int64_t(tc.n0) * ldbk;
+  const rsrc_t a_rs = make_rsrc(a_tile, 0xffffffffu);
+  const rsrc_t b_rs = make_rsrc(b_tile, 0xffffffffu);
 
   // Issue a stage's loads: all of them (part < 0), or the quarter whose
   // instruction index is part mod 4.
   auto issue = [&](uint4* base, int k0, int part = -1) {
     auto mine = [&](int idx) { return part < 0 || (idx & 3) == part; };
     if constexpr (AK) {
-      const int64_t koff = int64_t(k0) * g.M_fixed;
+      const rsrc_t r = make_rsrc(A + int64_t(k0) * g.M_fixed,
+                                 clamp_bytes(int64_t(K - k0) * g.M_fixed * 2));
 #pragma unroll
-      for (int i = 0; i < A_INS; ++i)
-        lds_load16(k0 + a_krow[i] < K ? a_src[i] + koff : zero, base + (w + WV * i) * 64);
+      for (int i = 0; i < A_INS; ++i) lds_load16(r, a_off[i], 0, base + (w + WV * i) * 64);
     } else {
 #pragma unroll
       for (int i = 0; i < A_INS; ++i)
-        if (mine(i)) lds_load16(a_src[i] + k0, base + (w + WV * i) * 64);
+        if (mine(i)) lds_load16(a_rs, a_off[i], uint32_t(k0) * 2, base + (w + WV * i) * 64);
     }
     uint4* bbase = base + BM * 8;
-    // column of B's stage: k0, or k0 mod the K period when B wraps (K = 2 * period)
-    const int kb = (MODE == GM_NT && g.b_kwrap && k0 >= g.b_kwrap) ? k0 - g.b_kwrap : k0;
     if constexpr (BKM) {
-      const int64_t koff = int64_t(k0) * ldb;
+      const int64_t rows_left = MODE == GM_KGROUP ? int64_t(K - k0) : int64_t(0x7fffffff);
+      const rsrc_t r = make_rsrc(B + int64_t(k0) * ldb, clamp_bytes(rows_left * ldb * 2));
 #pragma unroll
-      for (int i = 0; i < B_INS; ++i) {
-        const uint16_t* s = b_src[i] + koff;
-        if constexpr (MODE == GM_KGROUP) s = k0 + b_krow[i] < K ? s : zero;
-        lds_load16(s, bbase + (w + WV * i) * 64);
-      }
+      for (int i = 0; i < B_INS; ++i) lds_load16(r, b_off[i], 0, bbase + (w + WV * i) * 64);
     } else {
+      // column of B's stage: k0, or k0 mod the K period when B wraps (K = 2 * period)
+      const int kb = (g.b_kwrap && k0 >= g.b_kwrap) ? k0 - g.b_kwrap : k0;
 #pragma unroll
       for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
           if (mine(A_INS + p * B_INS + i))
-            lds_load16(b_src[p] + i * b_step + kb, bbase + p * BN * 8 + (w + WV * i) * 64);
+            lds_load16(b_rs, b_off[p * B_INS + i], uint32_t(kb) * 2,
+                       bbase + p * BN * 8 + (w + WV * i) * 64);
     }
   };
 
