@@ -17,10 +17,15 @@
 //    a (BM/2) x (BN/4) sub-tile of every panel as (BM/64) x (BN/128) blocks of
 //    v_mfma_f32_32x32x16_bf16.  With BM = BN = 256 a wave issues 8 MFMAs per
 //    6 operand fragments.
-//  * Global -> LDS with global_load_lds_dwordx4 (no staging registers): each
-//    wave instruction fills 1 KB of LDS.  A ring of K stages of 64 (as many as
-//    fit 144 KB, at most 4): the loads of the next stages are in flight while
-//    a stage multiplies.
+//  * Global -> LDS with buffer_load_dwordx4 ... lds (no staging registers):
+//    each wave instruction fills 1 KB of LDS from a raw buffer descriptor and
+//    a 32-bit per-lane offset.  A ring of K stages of 64 (as many as fit
+//    144 KB, at most 4): the next stages' loads, issued as one burst after
+//    each stage's barrier, are in flight while a stage multiplies.
+//  * A stage's loads and its fragment reads sit in one inlined call whose
+//    write and read slots are restrict pointers: the compiler then knows the
+//    LDS-DMA writes cannot alias the fragment reads and does not wait for the
+//    loads before reading fragments.
 //  * A K-contiguous operand is staged as rows of 64 k (128 B) whose eight
 //    16-byte chunks are XOR-swizzled by (row & 7) ^ ((row >> 3) & 1); an MFMA
 //    fragment is one 16-byte LDS read per lane, conflict-free whether the LDS
@@ -202,7 +207,6 @@ void gg_bf16_kernel(GemmArgs g) {
   static_assert(NI >= 1 && A_INS >= 1 && B_INS >= 1, "tile too small for the wave count");
   constexpr int NS = gb_stages(BM, BN, NP);
   constexpr int INS = A_INS + NP * B_INS;   // load instructions per wave per stage
-  constexpr bool IL = MODE == GM_NT;        // loads interleaved with the sub-steps
   // NS stages of (BM + NP*BN) x 128 bytes (at most 144 KB), dynamic LDS.
   extern __shared__ uint4 lds[];
   __shared__ int32_t ts[257];
@@ -310,10 +314,8 @@ void gg_bf16_kernel(GemmArgs g) {
   const rsrc_t a_rs = make_rsrc(a_tile, 0xffffffffu);
   const rsrc_t b_rs = make_rsrc(b_tile, 0xffffffffu);
 
-  // Issue a stage's loads: all of them (part < 0), or the quarter whose
-  // instruction index is part mod 4.
-  auto issue = [&](uint4* base, int k0, int part = -1) {
-    auto mine = [&](int idx) { return part < 0 || (idx & 3) == part; };
+  // Issue a stage's loads.
+  auto issue = [&](uint4* base, int k0) {
     if constexpr (AK) {
       const rsrc_t r = make_rsrc(A + int64_t(k0) * g.M_fixed,
                                  clamp_bytes(int64_t(K - k0) * g.M_fixed * 2));
@@ -322,7 +324,7 @@ void gg_bf16_kernel(GemmArgs g) {
     } else {
 #pragma unroll
       for (int i = 0; i < A_INS; ++i)
-        if (mine(i)) lds_load16(a_rs, a_off[i], uint32_t(k0) * 2, base + (w + WV * i) * 64);
+        lds_load16(a_rs, a_off[i], uint32_t(k0) * 2, base + (w + WV * i) * 64);
     }
     uint4* bbase = base + BM * 8;
     if constexpr (BKM) {
@@ -337,9 +339,8 @@ void gg_bf16_kernel(GemmArgs g) {
       for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
-          if (mine(A_INS + p * B_INS + i))
-            lds_load16(b_rs, b_off[p * B_INS + i], uint32_t(kb) * 2,
-                       bbase + p * BN * 8 + (w + WV * i) * 64);
+          lds_load16(b_rs, b_off[p * B_INS + i], uint32_t(kb) * 2,
+                     bbase + p * BN * 8 + (w + WV * i) * 64);
     }
   };
 
@@ -411,18 +412,16 @@ void gg_bf16_kernel(GemmArgs g) {
     // and it then no longer waits for the loads just issued before reading
     // fragments (which it did before every transposed LDS read).
     auto stage = [&](uint4* __restrict__ wslot, const uint4* __restrict__ rslot) {
-      // Forward layout: a live wave spreads the next stage's loads over the
-      // first four fragment sub-steps (a quarter each, after that sub-step's LDS
-      // reads), so they do not arrive as one burst that competes with the reads
-      // (2-4% on large products; the K-major layouts lose with it).
-      if (more && (!IL || !live)) issue(wslot, knext);
+      // The next stage's loads go out as one burst right after the barrier,
+      // giving them the whole stage to land (spreading them over the
+      // sub-steps measured 2-4% slower once the loads were buffer loads).
+      if (more) issue(wslot, knext);
       const uint4* As = rslot;
       const char* Ab = reinterpret_cast<const char*>(As);
       const char* Bb = Ab + BM * 128;
       if (live)
 #pragma unroll
       for (int s = 0; s <= 4; ++s) {
-        if (IL && s < 4 && more) issue(wslot, knext, s);
         if (s < 4) {
           const int pc = (2 * s + fg) ^ (fr & 7) ^ ((fr >> 3) & 1);
 #pragma unroll
@@ -462,15 +461,6 @@ void gg_bf16_kernel(GemmArgs g) {
         // MFMAs of step s-1 (otherwise the scheduler sinks every read next to
         // its use and each MFMA group waits on LDS latency).
         if (s < 4) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_STEP, 0);
-        if constexpr (IL) {
-          // this sub-step's quarter of the loads: (INS + 3 - s) / 4 instructions
-          if (s == 0) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 3) / 4, 0);
-          if (s == 1) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 2) / 4, 0);
-          if constexpr ((INS + 1) / 4 > 0)
-            if (s == 2) __builtin_amdgcn_sched_group_barrier(0x020, (INS + 1) / 4, 0);
-          if constexpr (INS / 4 > 0)
-            if (s == 3) __builtin_amdgcn_sched_group_barrier(0x020, INS / 4, 0);
-        }
         if (s > 0) __builtin_amdgcn_sched_group_barrier(0x008, NP * MI * NI, 0);
       }
     };
