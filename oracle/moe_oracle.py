@@ -65,7 +65,7 @@ __all__ = [
     "router_bwd", "expert_bwd", "uniform_assignment", "hash_assignment", "fmix32", "softplus",
     "score_histogram", "quantile_bias", "load_report", "expert_output_norms",
     "e2m1_decode", "e4m3_decode", "e2m1_encode", "e4m3_encode", "mx_quantize", "mx_dequantize",
-    "expert_ffn_mx",
+    "expert_ffn_mx", "philox4x64", "uniform24", "box_muller", "router_draws",
     "NEAR_TIE_REL",
 ]
 
@@ -760,3 +760,87 @@ def expert_ffn_mx(xq, xs, offsets, W13q, W13s, W2q, W2s, act: str, aq=None, as_=
         W2 = mx_dequantize(W2q[e], W2s[e], 32, "e2m1")
         outs[r0:r1] = ad[r0:r1] @ W2.T
     return outs, a_full, aq, as_
+
+
+# ---------------------------------------------------------------------------
+# Counter-based draws for the stochastic routers.  The noisy top-k router adds
+# a standard-normal draw per (token, expert) [MoE-Explained, "What is
+# sparsity?", the H(x) equation]; GShard's random routing draws one uniform
+# per token to decide its second expert [MoE-Explained, "MoEs and
+# Transformers"].  The pages name no generator.  The reading taken: the
+# counter-based Philox4x64-10 of Salmon, Moraes, Dror and Shaw ("Parallel
+# random numbers: as easy as 1, 2, 3", SC 2011), keyed by (seed, 0); the
+# block for draw stream s (0 normals, 1 uniforms) of a call with offset o is
+# counter (b, o, s, 0), b = element index // 4, the element taking output word
+# index % 4.  A uniform is the word's top 24 bits times 2^-24 (in [0, 1),
+# exact in fp32).  Normals come in pairs from the words (0, 1) and (2, 3) of a
+# block by the Box-Muller transform (Box and Muller, "A note on the
+# generation of random normal deviates", 1958): with uniforms u, v,
+# r = sqrt(-2 ln(1 - u)), z0 = r cos(2 pi v), z1 = r sin(2 pi v).
+# ---------------------------------------------------------------------------
+_PHILOX_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)   # round multipliers
+_PHILOX_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)   # key schedule increments
+_U64 = np.uint64
+_M32 = _U64(0xFFFFFFFF)
+
+
+def _mulhilo64(a, b):
+    """Full 128-bit product of uint64 arrays as (hi, lo), by 32-bit limbs."""
+    a0, a1 = a & _M32, a >> _U64(32)
+    b0, b1 = b & _M32, b >> _U64(32)
+    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
+    mid = (p00 >> _U64(32)) + (p01 & _M32) + (p10 & _M32)
+    hi = p11 + (p01 >> _U64(32)) + (p10 >> _U64(32)) + (mid >> _U64(32))
+    lo = (mid << _U64(32)) | (p00 & _M32)
+    return hi, lo
+
+
+def philox4x64(counters, key, rounds: int = 10):
+    """Philox4x64 of each row of counters [n, 4] (uint64) under key (k0, k1):
+    each round multiplies counter words 0 and 2 by the two round multipliers,
+    and the new counter is (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+    lo(M0 c0)); the key then advances by the two Weyl increments."""
+    c = [np.asarray(counters, dtype=_U64)[:, i].copy() for i in range(4)]
+    k0, k1 = int(key[0]), int(key[1])
+    with np.errstate(over="ignore"):
+        for r in range(rounds):
+            hi0, lo0 = _mulhilo64(_U64(_PHILOX_M[0]), c[0])
+            hi1, lo1 = _mulhilo64(_U64(_PHILOX_M[1]), c[2])
+            c = [hi1 ^ c[1] ^ _U64(k0), lo1, hi0 ^ c[3] ^ _U64(k1), lo0]
+            k0 = (k0 + _PHILOX_W[0]) % (1 << 64)
+            k1 = (k1 + _PHILOX_W[1]) % (1 << 64)
+    return np.stack(c, axis=1)
+
+
+def _draw_words(n: int, seed: int, offset: int, stream: int):
+    """The first n output words of draw stream `stream`, in element order."""
+    nb = -(-n // 4)
+    ctr = np.zeros((nb, 4), dtype=_U64)
+    ctr[:, 0] = np.arange(nb, dtype=_U64)
+    ctr[:, 1] = _U64(offset)
+    ctr[:, 2] = _U64(stream)
+    return philox4x64(ctr, (seed, 0)).reshape(-1)[:n]
+
+
+def uniform24(words):
+    """Uniforms in [0, 1): the top 24 bits of each uint64 word times 2^-24."""
+    return (np.asarray(words, dtype=_U64) >> _U64(40)).astype(F64) * 2.0 ** -24
+
+
+def box_muller(u, v):
+    """Two independent standard normals per uniform pair (u, v)."""
+    r = np.sqrt(-2.0 * np.log(1.0 - u))
+    return r * np.cos(2.0 * np.pi * v), r * np.sin(2.0 * np.pi * v)
+
+
+def router_draws(T: int, E: int, seed: int, offset: int):
+    """The stochastic routers' draws for one call: noise [T, E] standard
+    normals (noisy top-k) and uniform [T] in [0, 1) (GShard's second expert),
+    element j of either taking word j % 4 of its stream's block j // 4."""
+    n = T * E
+    w = uniform24(_draw_words(n + (-n) % 4, seed, offset, 0)).reshape(-1, 4)
+    z0, z1 = box_muller(w[:, 0], w[:, 1])
+    z2, z3 = box_muller(w[:, 2], w[:, 3])
+    noise = np.stack([z0, z1, z2, z3], axis=1).reshape(-1)[:n].reshape(T, E)
+    uniform = uniform24(_draw_words(T, seed, offset, 1))
+    return noise, uniform

@@ -865,3 +865,114 @@ def test_expert_ffn_mx_composition():
         aqe, ase = orc.mx_quantize(ar.numpy(), 64, "e4m3")
         ad = torch.from_numpy(orc.mx_dequantize(aqe, ase, 64, "e4m3"))
         np.testing.assert_allclose(o[r0:r1], (ad @ W2d.T).numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Counter-based draws (Philox4x64-10 and Box-Muller)
+# ---------------------------------------------------------------------------
+def test_mulhilo64_against_integers():
+    """The limb-wise 128-bit product against Python integers, extremes included."""
+    rng = np.random.default_rng(70)
+    edge = np.array([0, 1, 2**32 - 1, 2**32, 2**63, 2**64 - 1], dtype=np.uint64)
+    a = np.concatenate([edge, np.repeat(edge, len(edge)),
+                        rng.integers(0, 2**64, size=3000, dtype=np.uint64)])
+    b = np.concatenate([edge[::-1], np.tile(edge, len(edge)),
+                        rng.integers(0, 2**64, size=3000, dtype=np.uint64)])
+    with np.errstate(over="ignore"):
+        hi, lo = orc.moe_oracle._mulhilo64(a, b)
+    for x, y, h, l in zip(a.tolist(), b.tolist(), hi.tolist(), lo.tolist()):
+        assert (h << 64) | l == x * y
+
+
+def _ctr_add(ctr, i):
+    """The 256-bit counter (word 0 least significant) plus i."""
+    v = sum(int(w) << (64 * n) for n, w in enumerate(ctr)) + i
+    return [(v >> (64 * n)) % 2**64 for n in range(4)]
+
+
+@pytest.mark.parametrize("key,ctr", [
+    ((0, 0), (0, 0, 0, 0)),
+    ((2**64 - 1, 2**64 - 1), (2**64 - 1, 2**64 - 1, 2**64 - 1, 2**64 - 2)),
+    ((0x243F6A8885A308D3, 0x13198A2E03707344), (2**64 - 3, 5, 0, 9)),
+    ((12345, 0), (2**64 - 1, 6, 1, 0)),
+])
+def test_philox_matches_numpy(key, ctr):
+    """numpy's Philox bit generator is Philox4x64-10 from the same paper; it
+    advances its 256-bit counter by one (carrying word 0 into 1, 2, 3) before
+    each block and returns the block's four words in order."""
+    bg = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(ctr, dtype=np.uint64))
+    raw = bg.random_raw(4 * 6).reshape(6, 4)
+    ctrs = np.array([_ctr_add(ctr, i + 1) for i in range(6)], dtype=np.uint64)
+    np.testing.assert_array_equal(orc.philox4x64(ctrs, key), raw)
+
+
+def _numpy_stream_words(seed, offset, stream, n):
+    """Words of draw stream `stream` from numpy's Philox: started one below
+    counter (0, offset, stream, 0), its blocks are b = 0, 1, 2, ... (offset >= 1)."""
+    bg = np.random.Philox(key=np.array([seed, 0], dtype=np.uint64),
+                          counter=np.array([2**64 - 1, offset - 1, stream, 0], dtype=np.uint64))
+    return bg.random_raw(n + (-n) % 4)[:n]
+
+
+def test_router_uniforms_are_numpy_philox_words():
+    seed, offset, T = 987654321, 7, 1001
+    _, u = orc.router_draws(T, 3, seed, offset)
+    w = _numpy_stream_words(seed, offset, 1, T)
+    np.testing.assert_array_equal(u, (w >> np.uint64(40)).astype(np.float64) / 2**24)
+    assert u.min() >= 0.0 and u.max() < 1.0
+
+
+def test_router_noise_pairs_against_numpy_words():
+    """Each pair (z0, z1) of a block satisfies z0^2 + z1^2 = -2 ln(1 - u) and
+    angle(z0, z1) = 2 pi v for the pair's first and second uniforms, taken from
+    numpy's Philox words (the polar form of the Box-Muller transform)."""
+    seed, offset, T, E = 2**63 + 11, 3, 37, 9           # 333 normals: a ragged last block
+    z, _ = orc.router_draws(T, E, seed, offset)
+    n = T * E
+    w = _numpy_stream_words(seed, offset, 0, n + (-n) % 4)
+    u = (w >> np.uint64(40)).astype(np.float64) / 2**24
+    zf = np.concatenate([z.reshape(-1), np.full((-n) % 4, np.nan)])
+    for j in range(0, n - 1, 2):
+        z0, z1 = zf[j], zf[j + 1]
+        assert math.isclose(z0 * z0 + z1 * z1, -2 * math.log(1 - u[j]), rel_tol=1e-12, abs_tol=1e-15)
+        ang = math.atan2(z1, z0) / (2 * math.pi) % 1.0
+        assert abs(ang - u[j + 1]) < 1e-12 or abs(abs(ang - u[j + 1]) - 1) < 1e-12
+
+
+def test_box_muller_closed_forms():
+    r1 = 1 - math.exp(-0.5)                                  # radius 1
+    for u, v, want in [(0.0, 0.3, (0.0, 0.0)), (r1, 0.0, (1.0, 0.0)), (r1, 0.25, (0.0, 1.0)),
+                       (r1, 0.5, (-1.0, 0.0)), (r1, 0.125, (math.sqrt(0.5), math.sqrt(0.5))),
+                       (1 - math.exp(-2), 0.75, (0.0, -2.0))]:
+        z0, z1 = orc.box_muller(np.array([u]), np.array([v]))
+        assert abs(z0[0] - want[0]) < 1e-12 and abs(z1[0] - want[1]) < 1e-12, (u, v)
+
+
+def test_router_draws_distribution():
+    """Normals: Kolmogorov-Smirnov against the standard normal, moments, and no
+    correlation between the two members of a pair or between neighbouring
+    tokens; uniforms: Kolmogorov-Smirnov against U[0, 1)."""
+    import scipy.stats as ss
+    z, u = orc.router_draws(4096, 64, 31337, 1)
+    zf = z.reshape(-1)
+    assert ss.kstest(zf, "norm").pvalue > 1e-3
+    assert abs(zf.mean()) < 5 / math.sqrt(zf.size) and abs(zf.var() - 1) < 0.01
+    assert abs(np.corrcoef(zf[0::2], zf[1::2])[0, 1]) < 0.01
+    assert abs(np.corrcoef(z[:-1].reshape(-1), z[1:].reshape(-1))[0, 1]) < 0.01
+    assert ss.kstest(u, "uniform").pvalue > 1e-3
+
+
+def test_router_draws_layout_and_streams():
+    """Draws depend on the flat element index only (not on the [T, E] split),
+    and seed, offset and stream each give a different sequence."""
+    z1, u1 = orc.router_draws(12, 5, 8, 2)
+    z2, u2 = orc.router_draws(6, 10, 8, 2)
+    np.testing.assert_array_equal(z1.reshape(-1), z2.reshape(-1))
+    np.testing.assert_array_equal(u1[:6], u2)
+    z3, u3 = orc.router_draws(12, 5, 9, 2)
+    z4, u4 = orc.router_draws(12, 5, 8, 3)
+    assert not np.any(z3 == z1) and not np.any(z4 == z1)
+    assert not np.any(u3 == u1) and not np.any(u4 == u1)
+    w0 = orc.moe_oracle._draw_words(16, 8, 2, 0)
+    w1 = orc.moe_oracle._draw_words(16, 8, 2, 1)
+    assert not np.any(w0 == w1)
