@@ -131,7 +131,8 @@ typedef struct {
 
 /* Per-call inputs of the variant routers (device pointers, fp32 unless noted).
  * Only the ones opts.routing uses are read; the rest may be NULL.  Random draws
- * are inputs so that a call is reproducible. */
+ * are inputs so that a call is reproducible; moe_router_draws fills them on the
+ * device from a seed and a per-call offset. */
 typedef struct {
   const float* W_noise;      /* [d, E] noise projection (noisy top-k) */
   const float* noise;        /* [T, E] standard-normal draws (noisy top-k) */
@@ -215,6 +216,24 @@ int moe_route(const moe_dims* dims, const moe_opts* opts, const void* x, const f
               const float* logit_offset, const float* sel_bias, int32_t* topk_idx,
               float* topk_gate, float* scores, float* logits, int32_t* counts, float* losses,
               const moe_router_inputs* ri, void* ws, size_t ws_bytes, void* stream);
+
+/* Draws of the stochastic routers from a seed (the StandardNormal term of noisy
+ * top-k gating, "What is sparsity?", the H(x) equation; the uniform of GShard's
+ * random second expert, "MoEs and Transformers"), for moe_router_inputs.noise
+ * and .uniform.  Counter-based, so any element can be recomputed alone and a
+ * call is reproducible: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC 2011) keyed by (seed, 0); stream s
+ * (0 normals, 1 uniforms) draws block b from counter (b, offset, s, 0), and
+ * element j takes word j % 4 of block j / 4.  uniform [T]: a word's top 24
+ * bits times 2^-24, in [0, 1).  noise [T, E] row-major: words (0, 1) and (2, 3)
+ * of a block give two normals each by the Box-Muller transform, r = sqrt(-2
+ * ln(1 - u)), (r cos 2 pi v, r sin 2 pi v), u and v uniforms as above,
+ * evaluated in fp32.  Use a new offset (e.g. the step number) per call.
+ * Reads dims->T and dims->E only; noise and uniform are each nullable (both
+ * NULL, or T = 0: nothing is launched).  MOE_ERR_INVALID_ARG for T < 0 or
+ * E < 1; MOE_ERR_UNSUPPORTED for T*E > 2^40. */
+int moe_router_draws(const moe_dims* dims, uint64_t seed, uint64_t offset, float* noise,
+                     float* uniform, void* stream);
 
 /* Dispatch ("MoEs and Transformers": expert capacity, overflow to the residual).
  * counts[e] = slots choosing e; expert e keeps its first C slots in ascending

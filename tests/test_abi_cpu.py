@@ -175,3 +175,22 @@ def test_noalloc_permute_limit(L):
     assert call(65536, None) == B.MOE_ERR_INVALID_ARG    # T*k = 524288 fits: a null x is refused
     assert call(65537, dummy) == B.MOE_ERR_UNSUPPORTED   # one block of slots too many
     assert call(1 << 20, dummy) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_router_draws_argument_errors(L):
+    """moe_router_draws validates before any device call: negative T or no
+    experts are refused, T*E above 2^40 is unsupported, and a call with no
+    output buffer (or no tokens) launches nothing and succeeds."""
+    dummy = C.c_void_p(256)
+
+    def call(T, E, noise, uniform):
+        d = B.Dims(T, 0, E, 0, 0, 0)
+        return L.moe_router_draws(C.byref(d), C.c_uint64(1), C.c_uint64(2), noise, uniform, None)
+
+    assert call(-1, 8, dummy, dummy) == B.MOE_ERR_INVALID_ARG
+    assert call(16, 0, dummy, dummy) == B.MOE_ERR_INVALID_ARG
+    assert call(1 << 33, 256, dummy, None) == B.MOE_ERR_UNSUPPORTED
+    assert call(16, 8, None, None) == B.MOE_OK
+    assert call(0, 8, dummy, dummy) == B.MOE_OK
+    assert L.moe_router_draws(None, C.c_uint64(1), C.c_uint64(2), dummy, dummy, None) == \
+        B.MOE_ERR_INVALID_ARG

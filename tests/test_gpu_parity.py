@@ -480,6 +480,31 @@ def test_variant_router_parity(name, over):
     counts of the routed slots exact, dispatch (token or slot priority) exact
     on the GPU's own indices."""
     p, inp, x, w, ri = _variant_case(name, over)
+    _check_variant_route(p, inp, x, w, ri, f"{name} {over}")
+
+
+@pytest.mark.parametrize("name,over", [("c4", dict(routing="noisy_topk")),
+                                       ("c3", dict(routing="gshard")),
+                                       ("c1", dict(routing="noisy_topk"))])
+def test_variant_router_library_draws(name, over):
+    """The noisy and random routers on draws made by moe_router_draws (seed 99,
+    offset 1) into device buffers: the same checks against the oracle fed those
+    draws (whose own parity with the oracle's generator is tested apart)."""
+    p, inp, x, w, ri0 = _variant_case(name, over)
+    ri = B.LayerRouterInputs(W_noise=ri0.W_noise, token_ids=ri0.token_ids,
+                             noise=None if ri0.noise is None else torch.empty_like(ri0.noise),
+                             uniform=None if ri0.uniform is None else torch.empty_like(ri0.uniform))
+    B.router_draws(p.T, p.E, 99, 1, DEV, noise=ri.noise is not None, uniform=ri.uniform is not None,
+                   out=dict(noise=ri.noise, uniform=ri.uniform))
+    torch.cuda.synchronize()
+    inp = dict(inp)
+    for n in ("noise", "uniform"):
+        if getattr(ri, n) is not None:
+            inp[n] = getattr(ri, n).cpu().numpy()
+    _check_variant_route(p, inp, x, w, ri, f"{name} {over} library draws")
+
+
+def _check_variant_route(p, inp, x, w, ri, label):
     out = B.route(p, x, w.Wg, w.offset, w.sel_bias, want_logits=True, ri=ri)
     torch.cuda.synchronize()
     ref = _oracle_route(p, inp)
@@ -511,7 +536,7 @@ def test_variant_router_parity(name, over):
     np.testing.assert_array_equal(pm["row_of_slot"].cpu().numpy(), ros)
     R = int(offsets[-1])
     np.testing.assert_array_equal(pm["token_of_row"].cpu().numpy()[:R], tor[:R])
-    print(f"{name} {over}: near-ties {int(flag.sum())}, keep-threshold ties {int(kflag.sum())}, "
+    print(f"{label}: near-ties {int(flag.sum())}, keep-threshold ties {int(kflag.sum())}, "
           f"skipped {int((~active_g).sum())}, kept rows {R}")
 
 

@@ -76,7 +76,7 @@ ABI_FUNCTIONS = ("moe_capacity", "moe_workspace_size", "moe_route", "moe_permute
                  "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd",
                  "moe_bias_update", "moe_score_histogram", "moe_bias_from_histogram",
                  "moe_router_report", "moe_mx_quantize_weights", "moe_mx_quantize_act",
-                 "moe_expert_ffn_mx", "moe_strerror")
+                 "moe_expert_ffn_mx", "moe_router_draws", "moe_strerror")
 
 _lib: Optional[C.CDLL] = None
 
@@ -111,6 +111,7 @@ def lib() -> C.CDLL:
     L.moe_mx_quantize_act.argtypes = [O, VP, I64, I64, I64, VP, VP, VP]
     L.moe_expert_ffn_mx.argtypes = [D, O, I64, I64, I64, VP, VP, I64, VP, VP, VP, VP, VP, VP, VP,
                                     I64, VP, VP]
+    L.moe_router_draws.argtypes = [D, C.c_uint64, C.c_uint64, VP, VP, VP]
     L.moe_strerror.argtypes = [C.c_int]
     L.moe_strerror.restype = C.c_char_p
     for f in ABI_FUNCTIONS[:-1]:
@@ -202,6 +203,29 @@ def route(p: Preset, x, Wg, offset=None, sel_bias=None, *, want_scores=False, wa
         _ptr(out["idx"]), _ptr(out["gate"]), _ptr(out["scores"]), _ptr(out["logits"]),
         _ptr(out["counts"]), _ptr(out["losses"]), _ri_c(ri), _ptr(buf), nb, _stream()))
     return out
+
+
+def router_draws(T: int, E: int, seed: int, offset: int, device, *, noise: bool = True,
+                 uniform: bool = True, out: Optional[dict] = None):
+    """moe_router_draws: the stochastic routers' draws for one call, generated on
+    the device.  Returns dict(noise [T, E] f32 or None, uniform [T] f32 or None);
+    `out` may hold preallocated tensors of those shapes (e.g. a LayerRouterInputs'
+    buffers, refilled each step with a new offset)."""
+    dev = torch.device(device)
+    out = dict(out or {})
+    if noise and out.get("noise") is None:
+        out["noise"] = torch.empty(T, E, dtype=torch.float32, device=dev)
+    if uniform and out.get("uniform") is None:
+        out["uniform"] = torch.empty(T, dtype=torch.float32, device=dev)
+    nz, un = (out.get("noise") if noise else None), (out.get("uniform") if uniform else None)
+    if nz is not None:
+        _need(nz, "noise", (T, E), torch.float32, dev)
+    if un is not None:
+        _need(un, "uniform", (T,), torch.float32, dev)
+    d = Dims(T, 0, E, 0, 0, 0)
+    _check("moe_router_draws", lib().moe_router_draws(
+        C.byref(d), C.c_uint64(seed), C.c_uint64(offset), _ptr(nz), _ptr(un), _stream()))
+    return dict(noise=nz, uniform=un)
 
 
 def permute(p: Preset, x, idx, ws: Optional[Workspace] = None):
@@ -438,6 +462,17 @@ class Layer:
             C.c_void_p(self.y.data_ptr()), C.byref(self._saved_c) if self.train else None, None,
             C.c_void_p(self.ws.data_ptr()), self.ws_bytes, _stream()))
         return self.y
+
+    def draw(self, seed: int, offset: int) -> None:
+        """Refill the bound router inputs' noise / uniform buffers (whichever
+        the routing uses) with moe_router_draws(seed, offset), in place; call
+        once per step with a new offset, before fwd (bwd reads the same draws)."""
+        if self.ri is None:
+            raise ValueError("no router inputs bound to this layer")
+        p = self.p
+        router_draws(self.T, p.E, seed, offset, self.device,
+                     noise=self.ri.noise is not None, uniform=self.ri.uniform is not None,
+                     out=dict(noise=self.ri.noise, uniform=self.ri.uniform))
 
     def bwd(self, x: torch.Tensor, dy: torch.Tensor) -> dict:
         p = self.p
