@@ -51,7 +51,8 @@ __global__ void wg_split_kernel(const float* __restrict__ Wg, int d, int E, int 
 // holds KS partial logit sums for the block's 32 tokens.  Each token is
 // handled by a group of LG = 16 lanes (one DPP row, four tokens per wave at
 // a time), each owning VPL experts e = lane_in_group + LG * v; all per-token
-// reductions stay inside the row.  LDS scratch: red_p/red_c [NW * EP],
+// reductions stay inside the row.  LDS scratch: red_p [NW * EP], red_c [EP]
+// (the block's routed-slot counts, integer LDS atomics: exact in any order),
 // red_s [2 * NW].
 template <int EP, int KS, int NW>
 __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[ROUTE_BT][EP + 1],
@@ -67,17 +68,11 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
   const int gi = l / LG, lg = l % LG;
   const int E = a.E, k = a.k;
 
-  float off[VPL], bia[VPL];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int e = lg + LG * v;
-    off[v] = (a.offset && e < E) ? a.offset[e] : 0.0f;
-    bia[v] = (a.bias && e < E) ? a.bias[e] : 0.0f;
-  }
   float pacc[VPL];
-  int32_t cacc[VPL];
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) { pacc[v] = 0.0f; cacc[v] = 0; }
+  for (int v = 0; v < VPL; ++v) pacc[v] = 0.0f;
+  for (int e = tid; e < EP; e += NW * 64) red_c[e] = 0;
+  __syncthreads();
   float lse2 = 0.0f;
   int32_t nf = 0;
 
@@ -94,7 +89,7 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
       float zz = 0.0f;
 #pragma unroll
       for (int q = 0; q < KS; ++q) zz += zs[q][tl][e];
-      zz += off[v];
+      zz += (a.offset && e < E) ? a.offset[e] : 0.0f;
       if (a.noise && valid && e < E) {
         // H = z + noise * softplus(x . W_noise)
         const float zn = a.noise_logit[int64_t(t) * E + e];
@@ -113,21 +108,27 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
           if (lg + LG * v < E) a.logits[int64_t(t) * E + lg + LG * v] = z[v];
       continue;
     }
+    if (a.logits && valid)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (lg + LG * v < E) a.logits[int64_t(t) * E + lg + LG * v] = z[v];
     m = row_max<LG>(m);
     float sexp = 0.0f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
       if (lg + LG * v < E) sexp += expf(z[v] - m);
     sexp = row_sum<LG>(sexp);
+    // divisions as one reciprocal per token (within an ulp of the quotients)
+    const float rsexp = 1.0f / sexp;
     float ssum = 0.0f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int e = lg + LG * v;
       float sv;
       if (a.score == 0) {
-        sv = expf(z[v] - m) / sexp;
+        sv = expf(z[v] - m) * rsexp;
       } else if (a.score == 1) {
-        sv = 1.0f / (1.0f + expf(-z[v]));
+        sv = __builtin_amdgcn_rcpf(1.0f + expf(-z[v]));
       } else {
         sv = sqrtf(fmaxf(z[v], 0.0f) + log1pf(expf(-fabsf(z[v]))));
       }
@@ -135,13 +136,17 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
       ssum += s[v];
     }
     ssum = row_sum<LG>(ssum);
+    const float rssum = 1.0f / ssum;
     const float lse = m + logf(sexp);
 
-    uint64_t key[VPL];
+    // Selection keys: order_key(s + bias) + 1 (at least 1 for every real
+    // expert, NaN included), 0 for padding and for experts already taken.
+    // The expert index, the tie-breaker, is implied by the register slot.
+    uint32_t key[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int e = lg + LG * v;
-      key[v] = e < E ? (uint64_t(order_key(s[v] + bia[v])) << 32) | uint32_t(~uint32_t(e)) : 0ull;
+      key[v] = e < E ? order_key(s[v] + ((a.bias) ? a.bias[e] : 0.0f)) + 1u : 0u;
     }
     // k selection rounds, kept rolled (the per-expert work inside is
     // unrolled): lane j of the token's group keeps round j's expert and gate,
@@ -157,9 +162,17 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
       } else if (a.routing == 4) {
         e = valid ? int((int64_t(fmix32(uint32_t(a.token_ids[t]))) + j) % E) : 0;
       } else {
-        uint64_t best = 0;
+        // this lane's best (ascending v with a strict test: the lowest expert
+        // wins a tie), then the group's: larger key, then lower expert
+        uint32_t bk = 0;
+        int bv = 0;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+        for (int v = 0; v < VPL; ++v)
+          if (key[v] > bk) {
+            bk = key[v];
+            bv = v;
+          }
+        uint64_t best = bk ? (uint64_t(bk) << 32) | uint32_t(~uint32_t(lg + LG * bv)) : 0ull;
         best = row_max_u64<LG>(best);
         e = int(~uint32_t(best));
       }
@@ -169,7 +182,6 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
         if (lg + LG * v == e) {
           sv = s[v];
           key[v] = 0;
-          cacc[v] += valid ? 1 : 0;
         }
       // the owner's score (the other lanes add zeros: exact)
       const float ge = row_sum<LG>(sv);
@@ -187,15 +199,10 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
     // Random second expert (k = 2): keep it iff u < 2 s2 / (s1 + s2); a skipped
     // slot is reported as E + expert and not counted.
     bool skip2 = false;
-    if (a.routing == 3 && valid) {
-      skip2 = !(a.uniform[t] < 2.0f * g1 / (g0 + g1));
-      if (skip2)
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-          if (lg + LG * v == e1) cacc[v] -= 1;
-    }
+    if (a.routing == 3 && valid) skip2 = !(a.uniform[t] < 2.0f * g1 / (g0 + g1));
     if (valid) {
       if (lg < k) {
+        if (!(lg == 1 && skip2)) atomicAdd(&red_c[my_e], 1);
         const float g = a.renorm ? (my_g / gs) * a.gate_scale : my_g * a.gate_scale;
         a.idx[int64_t(t) * k + lg] = my_e + ((lg == 1 && skip2) ? E : 0);
         a.gate[int64_t(t) * k + lg] = g;
@@ -205,8 +212,7 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
         const int e = lg + LG * v;
         if (e < E) {
           if (a.scores) a.scores[int64_t(t) * E + e] = s[v];
-          if (a.logits) a.logits[int64_t(t) * E + e] = z[v];
-          pacc[v] += s[v] / ssum;
+          pacc[v] += s[v] * rssum;
         }
       }
       lse2 += lse * lse;
@@ -217,19 +223,13 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
 #pragma unroll
   for (int msk = LG; msk < 64; msk <<= 1) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      pacc[v] += shfl_xor(pacc[v], msk);
-      cacc[v] += shfl_xor(cacc[v], msk);
-    }
+    for (int v = 0; v < VPL; ++v) pacc[v] += shfl_xor(pacc[v], msk);
     lse2 += shfl_xor(lse2, msk);
     nf += shfl_xor(nf, msk);
   }
   if (gi == 0) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      red_p[w * EP + lg + LG * v] = pacc[v];
-      red_c[w * EP + lg + LG * v] = cacc[v];
-    }
+    for (int v = 0; v < VPL; ++v) red_p[w * EP + lg + LG * v] = pacc[v];
   }
   if (l == 0) {
     red_s[w] = lse2;
@@ -239,14 +239,10 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
   const int blk = blockIdx.x;
   for (int e = tid; e < EP; e += blockDim.x) {
     float ps = 0.0f;
-    int32_t cs = 0;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      ps += red_p[ww * EP + e];
-      cs += red_c[ww * EP + e];
-    }
+    for (int ww = 0; ww < NW; ++ww) ps += red_p[ww * EP + e];
     a.part_p[int64_t(blk) * EP + e] = ps;
-    a.part_cnt[int64_t(blk) * EP + e] = cs;
+    a.part_cnt[int64_t(blk) * EP + e] = red_c[e];
   }
   if (tid == 0) {
     float ls = 0.0f;
@@ -276,7 +272,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
   constexpr int KS = NW / NB;
   __shared__ float zs[KS][ROUTE_BT][EP + 1];
   __shared__ float red_p[NW * EP];
-  __shared__ int32_t red_c[NW * EP];
+  __shared__ int32_t red_c[EP];
   __shared__ float red_s[2 * NW];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -293,25 +289,35 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-  uint4 xa[4], wv[3][4];
-  auto load = [&](int kc) {
+  // Rows of padding experts (eb*32 + row >= E) are zero in every plane: their
+  // lanes load nothing and multiply zeros.
+  const bool wlive = eb * 32 + row < a.E;
+  uint4 xa[4], wv[3][4], xb[4], wb[3][4];
+  auto load = [&](int kc, uint4 (&xo)[4], uint4 (&wo)[3][4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xa[q] = ld16(xr + kc + 8 * q);
+    for (int q = 0; q < 4; ++q) xo[q] = ld16(xr + kc + 8 * q);
 #pragma unroll
     for (int p = 0; p < 3; ++p)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wv[p][q] = ld16(wr + p * plane + kc + 8 * q);
+      for (int q = 0; q < 4; ++q)
+        wo[p][q] = wlive ? ld16(wr + p * plane + kc + 8 * q) : make_uint4(0, 0, 0, 0);
   };
-  load(0);
+  // Two chunks in flight: chunk c+2 is loaded while chunk c multiplies.
+  load(0, xa, wv);
+  if (64 < dpart) load(64, xb, wb);
   for (int kc = 0; kc < dpart; kc += 64) {
     uint4 xc[4], wc[3][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       xc[q] = xa[q];
+      xa[q] = xb[q];
 #pragma unroll
-      for (int p = 0; p < 3; ++p) wc[p][q] = wv[p][q];
+      for (int p = 0; p < 3; ++p) {
+        wc[p][q] = wv[p][q];
+        wv[p][q] = wb[p][q];
+      }
     }
-    if (kc + 64 < dpart) load(kc + 64);
+    if (kc + 128 < dpart) load(kc + 128, xb, wb);
 #pragma unroll
     for (int p = 0; p < 3; ++p)
 #pragma unroll
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(256) void route_simt_kernel(RouteArgs a) {
   constexpr int NW = 4;
   __shared__ float zs[1][ROUTE_BT][EP + 1];
   __shared__ float red_p[NW * EP];
-  __shared__ int32_t red_c[NW * EP];
+  __shared__ int32_t red_c[EP];
   __shared__ float red_s[2 * NW];
   const int t0 = blockIdx.x * ROUTE_BT;
   for (int o = threadIdx.x; o < ROUTE_BT * EP; o += blockDim.x) {
@@ -360,27 +366,28 @@ __global__ __launch_bounds__(256) void route_simt_kernel(RouteArgs a) {
 // ---------------------------------------------------------------------------
 // One block of 1024 threads: per-expert totals over the route blocks and the
 // two losses.  L_aux = aux_coef * E * sum_e (count_e / (T k)) * (P_e / T);
-// L_z = z_coef * sum_t lse_t^2 / T.  Lane q of expert e sums blocks
-// b = q, q + L, ... in order; lanes, then experts, are combined in a fixed
-// order, in double.
+// L_z = z_coef * sum_t lse_t^2 / T.  Lane (g, q) sums experts 4g..4g+3 over
+// blocks b = q, q + L, ... in order with 16-byte loads (L = 4096 / EP lanes
+// per group, eight loads of each kind in flight); the lanes of a group are
+// then added in q order, and the experts in a fixed tree, in double.
 __global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nblk, float aux_coef,
                                                             float z_coef, int32_t* counts,
                                                             float* losses, int32_t* n_nonfinite) {
-  __shared__ double sp[1024];
-  __shared__ int64_t sc[1024];
+  __shared__ double sp[1024];      // per-lane P sums (one expert column at a time), then terms
+  __shared__ int32_t sc[4 * 1024]; // per-lane counts
   __shared__ double sl[1024];
   __shared__ int64_t sn[1024];
   const int tid = threadIdx.x;
-  const int EP = a.EP, L = 1024 / EP;
-  const int e = tid % EP, q = tid / EP;
-  double P = 0.0;
-  int64_t c = 0;
-  if (e < a.E) {
+  const int EP = a.EP, G = EP / 4, L = 1024 / G;
+  const int g = tid % G, q = tid / G;
+  double P[4] = {0.0, 0.0, 0.0, 0.0};
+  int32_t c[4] = {0, 0, 0, 0};
 #pragma unroll 8
-    for (int b = q; b < nblk; b += L) {
-      P += double(a.part_p[int64_t(b) * EP + e]);
-      c += a.part_cnt[int64_t(b) * EP + e];
-    }
+  for (int b = q; b < nblk; b += L) {
+    const float4 pv = *reinterpret_cast<const float4*>(a.part_p + int64_t(b) * EP + 4 * g);
+    const int4 cv = *reinterpret_cast<const int4*>(a.part_cnt + int64_t(b) * EP + 4 * g);
+    P[0] += double(pv.x); P[1] += double(pv.y); P[2] += double(pv.z); P[3] += double(pv.w);
+    c[0] += cv.x; c[1] += cv.y; c[2] += cv.z; c[3] += cv.w;
   }
   double l2 = 0.0;
   int64_t nf = 0;
@@ -389,18 +396,26 @@ __global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nbl
     l2 += double(a.part_lse2[b]);
     nf += a.part_nf[b];
   }
-  sp[tid] = P;
-  sc[tid] = c;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sc[j * 1024 + tid] = c[j];
   sl[tid] = l2;
   sn[tid] = nf;
-  __syncthreads();
-  // lanes of each expert -> lane 0 (fixed order); lse / nonfinite tree
-  if (q == 0) {
-    for (int qq = 1; qq < L; ++qq) {
-      sp[e] += sp[qq * EP + e];
-      sc[e] += sc[qq * EP + e];
-    }
+  // lanes of each group in q order: expert 4g + j accumulates in register Pe
+  // of thread (g, j) (threads with q < 4), one expert column per pass
+  double Pe = 0.0;
+  int32_t ce = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    __syncthreads();
+    sp[tid] = P[j];
+    __syncthreads();
+    if (q == j)
+      for (int qq = 0; qq < L; ++qq) {
+        Pe += sp[qq * G + g];
+        ce += sc[j * 1024 + qq * G + g];
+      }
   }
+  __syncthreads();
   for (int s = 512; s > 0; s >>= 1) {
     if (tid < s) {
       sl[tid] += sl[tid + s];
@@ -408,14 +423,17 @@ __global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nbl
     }
     __syncthreads();
   }
-  // per-expert terms, then a fixed-order tree over experts (reusing sp as the term buffer)
+  // per-expert terms (expert 4g + q lives in thread (g, q), q < 4), then a
+  // fixed-order tree over experts (reusing sp as the term buffer)
+  const int e = 4 * g + q;
   double term = 0.0;
-  if (tid < a.E) {
-    if (counts) counts[tid] = int32_t(sc[tid]);
-    term = (double(sc[tid]) / (double(a.T) * a.k)) * (sp[tid] / a.T);
+  if (q < 4 && e < a.E) {
+    if (counts) counts[e] = ce;
+    term = (double(ce) / (double(a.T) * a.k)) * (Pe / a.T);
   }
+  sp[tid] = 0.0;
   __syncthreads();
-  sp[tid] = tid < EP ? term : 0.0;
+  if (q < 4) sp[e] = term;
   __syncthreads();
   for (int s = 512; s > 0; s >>= 1) {
     if (tid < s) sp[tid] += sp[tid + s];
@@ -445,12 +463,12 @@ hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, int pad_rows, 
 // three plane products x . q_p at columns p*EP + e (p = 0, 1, 2), added here
 // in plane order.
 template <int EP>
-__global__ __launch_bounds__(512) void route_from_partials_kernel(RouteArgs a, const float* z3,
-                                                                  int ldz) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void route_from_partials_kernel(RouteArgs a, const float* z3, int ldz) {
   constexpr int NW = 8;
   __shared__ float zs[1][ROUTE_BT][EP + 1];
   __shared__ float red_p[NW * EP];
-  __shared__ int32_t red_c[NW * EP];
+  __shared__ int32_t red_c[EP];
   __shared__ float red_s[2 * NW];
   const int t0 = blockIdx.x * ROUTE_BT;
   // every load of the block's slab is issued before the first use
