@@ -119,13 +119,22 @@ def main():
     # Primary: cold caches.  A 512 MB write before each step evicts L2 and the
     # 256 MB Infinity Cache; HIP events bracket the step alone; a device-side
     # spin after the flush lets the host enqueue the step before it starts.
+    # The spin is sized from the host's enqueue time of one step (twice it,
+    # plus 0.2 ms): a longer idle spin lets the clocks drop before the step
+    # (a 3 ms spin cost 0.7 ms per c3 step), a shorter one could only add
+    # host gaps inside the timed region.
     flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    step()
+    host_step = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    spin_s = 2.0 * host_step + 2e-4
     for i in range(args.steps):
         flush.fill_(float(i))
-        torch.cuda._sleep(int(2.4e9 * 3e-3))
+        torch.cuda._sleep(int(2.4e9 * spin_s))
         ev[i][0].record()
         step()
         ev[i][1].record()
@@ -135,7 +144,8 @@ def main():
     dt = float(np.sum(cold)) / args.steps * 1e-3
     tok_s = p.T / dt
     log(f"[bench] cold caches: {dt * 1e3:.3f} ms/step (mean of {len(cold)}), "
-        f"{tok_s / 1e6:.3f} M tokens/s")
+        f"{tok_s / 1e6:.3f} M tokens/s (host enqueue {host_step * 1e3:.3f} ms, "
+        f"spin {spin_s * 1e3:.3f} ms)")
 
     # Warm: the same number of steps back to back, wall clock.
     torch.cuda.synchronize()
