@@ -92,4 +92,34 @@ __device__ __forceinline__ float4 unpack_bf4(uint2 u) {
                      bf2f(uint16_t(u.y & 0xffffu)), bf2f(uint16_t(u.y >> 16)));
 }
 
+// Operands are read through raw buffer descriptors (base and size in scalar
+// registers): each load instruction carries a 32-bit per-lane offset, and the
+// K advance is a scalar offset or a rebased descriptor, so no 64-bit address
+// arithmetic runs per stage.  Loads at or beyond the descriptor's size return
+// zeros (K rows past the end of a group in the weight-gradient mode).  These
+// loads count on vmcnt only, so the waits for LDS reads never wait for them
+// (the global-to-LDS form also counts on lgkmcnt).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword 3: a raw (untyped, unswizzled) buffer on CDNA
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
+  return b <= 0 ? 0u : (b >= int64_t(0xffffffff) ? 0xffffffffu : uint32_t(b));
+}
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane l writes lds_wave_base + 16*l; the LDS pointer must be
+// wave-uniform.  (A plain function: the builtin called from a lambda inside a
+// kernel template breaks the host-side instantiation.)
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16, voff, soff, 0, 0);
+}
+// 4 bytes per lane: lane l writes the dword at lds_wave_base + 4*l.
+__device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds_wave_base), 4, voff, soff, 0, 0);
+}
+
 }  // namespace moe

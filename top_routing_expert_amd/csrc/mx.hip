@@ -165,14 +165,6 @@ __global__ __launch_bounds__(256) void mx8_quantize_kernel(const void* __restric
 constexpr int MX_BN = 256;       // tile columns: 4 waves along n, 64 columns each
 constexpr int MX_NS = 6;         // ring slots, one 64-k stage each
 
-__device__ uint4 g_zero_mx[16];  // a harmless source for the padding scale loads
-
-__device__ __forceinline__ void lds_load(const void* src, void* lds, int bytes) {
-  if (bytes == 16) __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-  else if (bytes == 4) __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
-  else __builtin_amdgcn_global_load_lds(src, lds, 1, 0, 0);
-}
-
 template <int N>
 __device__ __forceinline__ void mx_wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -250,54 +242,57 @@ void gg_mx_kernel(MxArgs g) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int wm = w >> 2, wn = w & 3;
 
-  // ---- load sources (instruction q = w + 8i of each region)
-  const uint8_t* a_src[A_INS];
+  // ---- load sources (instruction q = w + 8i of each region): per-lane byte
+  // offsets within each stage's buffer descriptors (rebased per 64-k stage)
+  uint32_t a_off[A_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
     const int row = 16 * (w + WV * i) + (l >> 2);
     const int c = (l & 3) ^ swz_a(row);
     const int mr = min(tc.m0 + row, tc.M - 1);
-    a_src[i] = g.A + (int64_t(tc.row0) + mr) * 64 + 16 * c;
+    a_off[i] = uint32_t((int64_t(tc.row0) + mr) * 64 + 16 * c);
   }
-  const uint8_t* b_src[B_INS];
+  uint32_t b_off[B_INS];
   const uint8_t* Bg = g.B + int64_t(tc.grp) * g.nb_rows * (K / 2);
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
     const int row = 32 * (w + WV * i) + (l >> 1);          // 0 .. NP*BN-1
     const int p = row / BN, col = row % BN;
     const int c = (l & 1) ^ swz_b(row);
-    b_src[i] = Bg + int64_t(p * g.up_off + tc.n0 + col) * 32 + 16 * c;
+    b_off[i] = uint32_t((p * g.up_off + tc.n0 + col) * 32 + 16 * c);
   }
   // scale loads (4 bytes per lane): waves 0 and 1 bring the A scales of the
   // tile's rows from the aligned start a4 (a_off = misalignment); the next
   // NP*2 waves bring the B scales (one 256-column run of scale row 2s + h of
-  // panel p); the rest load padding.
+  // panel p); the rest issue a load outside an empty descriptor, which
+  // writes zeros to the padding and keeps every wave's load count equal.
   const int nA = 2, nB = NP * 2;
   const int64_t a_first = int64_t(tc.row0) + tc.m0;
   const int64_t a4 = a_first & ~int64_t(3);
-  const int a_off = int(a_first - a4);
+  const int a_off_s = int(a_first - a4);
   const int64_t a_last = (g.a_stride & ~int64_t(3)) - 4;   // last whole dword of a scale row
   const uint8_t* Bsg = g.Bs + int64_t(tc.grp) * (K / 32) * g.nb_rows;
   const int64_t a_kstep = g.a_stride * 64, b_kstep = int64_t(g.nb_rows) * 32;   // bytes per 64-k block
-  auto issue = [&](int stage, int ks) {
-    char* base = lds + stage * STAGE;
+  const int sj = w - nA;
+  const uint32_t s_off = w < nA ? uint32_t(min(a4 + 256 * w + 4 * l, a_last))
+                         : w < nA + nB ? uint32_t((sj & 1) * g.nb_rows + (sj >> 1) * g.up_off + tc.n0 + 4 * l)
+                                       : 0u;
+  auto issue = [&](char* base, int ks) {
+    const rsrc_t ra = make_rsrc(g.A + a_kstep * ks, clamp_bytes(a_kstep));
 #pragma unroll
-    for (int i = 0; i < A_INS; ++i)
-      lds_load(a_src[i] + a_kstep * ks, base + (w + WV * i) * 1024, 16);
+    for (int i = 0; i < A_INS; ++i) lds_load16(ra, a_off[i], 0, base + (w + WV * i) * 1024);
+    const rsrc_t rb = make_rsrc(Bg + b_kstep * ks, clamp_bytes(b_kstep));
 #pragma unroll
-    for (int i = 0; i < B_INS; ++i)
-      lds_load(b_src[i] + b_kstep * ks, base + A_BYTES + (w + WV * i) * 1024, 16);
+    for (int i = 0; i < B_INS; ++i) lds_load16(rb, b_off[i], 0, base + A_BYTES + (w + WV * i) * 1024);
     char* sb = base + A_BYTES + B_BYTES;
-    if (w < nA) {
-      const int64_t o = min(a4 + 256 * w + 4 * l, a_last);
-      lds_load(g.As + int64_t(ks) * g.a_stride + o, sb + 256 * w, 4);
-    } else if (w < nA + nB) {
-      const int j = w - nA, p = j >> 1, h = j & 1;
-      lds_load(Bsg + int64_t(2 * ks + h) * g.nb_rows + p * g.up_off + tc.n0 + 4 * l,
-               sb + AS_BYTES + 256 * j, 4);
-    } else {
-      lds_load(reinterpret_cast<const uint8_t*>(g_zero_mx) + 4 * (l & 15), sb + AS_BYTES + BS_BYTES, 4);
-    }
+    if (w < nA)
+      lds_load4(make_rsrc(g.As + int64_t(ks) * g.a_stride, clamp_bytes(g.a_stride)), s_off, 0,
+                sb + 256 * w);
+    else if (w < nA + nB)
+      lds_load4(make_rsrc(Bsg + int64_t(2 * ks) * g.nb_rows, clamp_bytes(2 * int64_t(g.nb_rows))),
+                s_off, 0, sb + AS_BYTES + 256 * sj);
+    else
+      lds_load4(make_rsrc(g.As, 0), 0, 0, sb + AS_BYTES + BS_BYTES);
   };
 
   floatx16 acc[NP][MI][NI];
@@ -317,8 +312,7 @@ void gg_mx_kernel(MxArgs g) {
   // 64-k stages: one wait and one barrier per 128 k, the next two stages
   // issued into the slots the previous step released, four stages in flight.
   // K is a multiple of 256, so KS is even.
-  auto compute = [&](int slot) {
-    const char* base = lds + slot * STAGE;
+  auto compute = [&](const char* base) {
     const char* Ab = base;
     const char* Bb = base + A_BYTES;
     const uint8_t* Sa = reinterpret_cast<const uint8_t*>(base + A_BYTES + B_BYTES);
@@ -332,7 +326,7 @@ void gg_mx_kernel(MxArgs g) {
       const uint4 lo = *reinterpret_cast<const uint4*>(Ab + row * 64 + 16 * (fh ^ z));
       const uint4 hi = *reinterpret_cast<const uint4*>(Ab + row * 64 + 16 * ((2 + fh) ^ z));
       af[mi] = v8i32_t{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-      sa[mi] = Sa[a_off + row];
+      sa[mi] = Sa[a_off_s + row];
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p)
@@ -351,17 +345,25 @@ void gg_mx_kernel(MxArgs g) {
   };
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    if (j < KS) issue(j, kidx(j));
+    if (j < KS) issue(lds + j * STAGE, kidx(j));
   for (int kt = 0; kt < KS; kt += 2) {
     // stages kt, kt+1 have landed once at most the loads of the stages issued
     // after them are outstanding (loads complete in order)
     if (min(KS, kt + 4) - (kt + 2) >= 2) mx_wait_vmcnt<2 * INS>();
     else mx_wait_vmcnt<0>();
     mx_barrier();
-    if (kt + 4 < KS) issue((kt + 4) % MX_NS, kidx(kt + 4));
-    if (kt + 5 < KS) issue((kt + 5) % MX_NS, kidx(kt + 5));
-    compute(kt % MX_NS);
-    compute((kt + 1) % MX_NS);
+    // The slots written and the slots read never overlap; passing them as
+    // restrict parameters of one inlined call lets the compiler read this
+    // step's fragments without waiting for the loads just issued.
+    auto step = [&](char* __restrict__ w0, char* __restrict__ w1, const char* __restrict__ r0,
+                    const char* __restrict__ r1) {
+      if (kt + 4 < KS) issue(w0, kidx(kt + 4));
+      if (kt + 5 < KS) issue(w1, kidx(kt + 5));
+      compute(r0);
+      compute(r1);
+    };
+    step(lds + ((kt + 4) % MX_NS) * STAGE, lds + ((kt + 5) % MX_NS) * STAGE,
+         lds + (kt % MX_NS) * STAGE, lds + ((kt + 1) % MX_NS) * STAGE);
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
