@@ -366,28 +366,27 @@ __global__ __launch_bounds__(256) void route_simt_kernel(RouteArgs a) {
 // ---------------------------------------------------------------------------
 // One block of 1024 threads: per-expert totals over the route blocks and the
 // two losses.  L_aux = aux_coef * E * sum_e (count_e / (T k)) * (P_e / T);
-// L_z = z_coef * sum_t lse_t^2 / T.  Lane (g, q) sums experts 4g..4g+3 over
-// blocks b = q, q + L, ... in order with 16-byte loads (L = 4096 / EP lanes
-// per group, eight loads of each kind in flight); the lanes of a group are
-// then added in q order, and the experts in a fixed tree, in double.
+// L_z = z_coef * sum_t lse_t^2 / T.  Lane q of expert e sums blocks
+// b = q, q + L, ... in order; lanes, then experts, are combined in a fixed
+// order, in double.
 __global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nblk, float aux_coef,
                                                             float z_coef, int32_t* counts,
                                                             float* losses, int32_t* n_nonfinite) {
-  __shared__ double sp[1024];      // per-lane P sums (one expert column at a time), then terms
-  __shared__ int32_t sc[4 * 1024]; // per-lane counts
+  __shared__ double sp[1024];
+  __shared__ int64_t sc[1024];
   __shared__ double sl[1024];
   __shared__ int64_t sn[1024];
   const int tid = threadIdx.x;
-  const int EP = a.EP, G = EP / 4, L = 1024 / G;
-  const int g = tid % G, q = tid / G;
-  double P[4] = {0.0, 0.0, 0.0, 0.0};
-  int32_t c[4] = {0, 0, 0, 0};
+  const int EP = a.EP, L = 1024 / EP;
+  const int e = tid % EP, q = tid / EP;
+  double P = 0.0;
+  int64_t c = 0;
+  if (e < a.E) {
 #pragma unroll 8
-  for (int b = q; b < nblk; b += L) {
-    const float4 pv = *reinterpret_cast<const float4*>(a.part_p + int64_t(b) * EP + 4 * g);
-    const int4 cv = *reinterpret_cast<const int4*>(a.part_cnt + int64_t(b) * EP + 4 * g);
-    P[0] += double(pv.x); P[1] += double(pv.y); P[2] += double(pv.z); P[3] += double(pv.w);
-    c[0] += cv.x; c[1] += cv.y; c[2] += cv.z; c[3] += cv.w;
+    for (int b = q; b < nblk; b += L) {
+      P += double(a.part_p[int64_t(b) * EP + e]);
+      c += a.part_cnt[int64_t(b) * EP + e];
+    }
   }
   double l2 = 0.0;
   int64_t nf = 0;
@@ -396,26 +395,18 @@ __global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nbl
     l2 += double(a.part_lse2[b]);
     nf += a.part_nf[b];
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) sc[j * 1024 + tid] = c[j];
+  sp[tid] = P;
+  sc[tid] = c;
   sl[tid] = l2;
   sn[tid] = nf;
-  // lanes of each group in q order: expert 4g + j accumulates in register Pe
-  // of thread (g, j) (threads with q < 4), one expert column per pass
-  double Pe = 0.0;
-  int32_t ce = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    __syncthreads();
-    sp[tid] = P[j];
-    __syncthreads();
-    if (q == j)
-      for (int qq = 0; qq < L; ++qq) {
-        Pe += sp[qq * G + g];
-        ce += sc[j * 1024 + qq * G + g];
-      }
-  }
   __syncthreads();
+  // lanes of each expert -> lane 0 (fixed order); lse / nonfinite tree
+  if (q == 0) {
+    for (int qq = 1; qq < L; ++qq) {
+      sp[e] += sp[qq * EP + e];
+      sc[e] += sc[qq * EP + e];
+    }
+  }
   for (int s = 512; s > 0; s >>= 1) {
     if (tid < s) {
       sl[tid] += sl[tid + s];
@@ -423,17 +414,14 @@ __global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nbl
     }
     __syncthreads();
   }
-  // per-expert terms (expert 4g + q lives in thread (g, q), q < 4), then a
-  // fixed-order tree over experts (reusing sp as the term buffer)
-  const int e = 4 * g + q;
+  // per-expert terms, then a fixed-order tree over experts (reusing sp as the term buffer)
   double term = 0.0;
-  if (q < 4 && e < a.E) {
-    if (counts) counts[e] = ce;
-    term = (double(ce) / (double(a.T) * a.k)) * (Pe / a.T);
+  if (tid < a.E) {
+    if (counts) counts[tid] = int32_t(sc[tid]);
+    term = (double(sc[tid]) / (double(a.T) * a.k)) * (sp[tid] / a.T);
   }
-  sp[tid] = 0.0;
   __syncthreads();
-  if (q < 4) sp[e] = term;
+  sp[tid] = tid < EP ? term : 0.0;
   __syncthreads();
   for (int s = 512; s > 0; s >>= 1) {
     if (tid < s) sp[tid] += sp[tid + s];
