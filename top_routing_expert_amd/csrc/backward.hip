@@ -314,30 +314,43 @@ __global__ void sum_partials_kernel(const float* __restrict__ P, int nz, int64_t
 
 // ---------------------------------------------------------------------------
 // dx[t] = sum over kept slots j (slot order) of dXp[row_tj] + extra1[t] + extra2[t].
+// One wave per token: as in the forward combine, each slot row is read through
+// its own buffer descriptor (empty for a dropped slot), so the loads of all KM
+// slots of a 256-float slab are issued together.
+template <int KM>
 __global__ __launch_bounds__(256) void unpermute_sum_kernel(
     const float* __restrict__ dxp, const int32_t* __restrict__ ros, const float* __restrict__ e1,
     const float* __restrict__ e2, int T, int k, int d, float* __restrict__ dx) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   if (t >= T) return;
-  int rows[BWD_KMAX];
+  const int my_row = l < k ? ros[int64_t(t) * k + l] : -1;
+  int rows[KM];
+  rsrc_t rs[KM];
 #pragma unroll
-  for (int j = 0; j < BWD_KMAX; ++j) rows[j] = j < k ? ros[int64_t(t) * k + j] : -1;
+  for (int j = 0; j < KM; ++j) {
+    rows[j] = __builtin_amdgcn_readlane(my_row, j);
+    rs[j] = make_rsrc(rows[j] >= 0 ? dxp + int64_t(rows[j]) * d : dxp,
+                      rows[j] >= 0 ? uint32_t(d) * 4 : 0u);
+  }
   for (int c = l; c < (d >> 2); c += 64) {
+    floatx4 v[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      v[j] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs[j], uint32_t(c) * 16, 0, 0));
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < BWD_KMAX; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (rows[j] < 0) continue;
-      const float4 v = reinterpret_cast<const float4*>(dxp + int64_t(rows[j]) * d)[c];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      acc.x += v[j][0]; acc.y += v[j][1]; acc.z += v[j][2]; acc.w += v[j][3];
     }
     if (e1) {
-      const float4 v = reinterpret_cast<const float4*>(e1 + int64_t(t) * d)[c];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      const float4 u = reinterpret_cast<const float4*>(e1 + int64_t(t) * d)[c];
+      acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
     }
     if (e2) {
-      const float4 v = reinterpret_cast<const float4*>(e2 + int64_t(t) * d)[c];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      const float4 u = reinterpret_cast<const float4*>(e2 + int64_t(t) * d)[c];
+      acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
     }
     reinterpret_cast<float4*>(dx + int64_t(t) * d)[c] = acc;
   }
@@ -447,7 +460,12 @@ hipError_t launch_sum_partials(const float* P, int nz, int64_t n, float* out, hi
 
 hipError_t launch_unpermute_sum(const float* dxp, const int32_t* ros, const float* e1,
                                 const float* e2, int T, int k, int d, float* dx, hipStream_t st) {
-  unpermute_sum_kernel<<<unsigned(cdiv(T, 4)), 256, 0, st>>>(dxp, ros, e1, e2, T, k, d, dx);
+  const dim3 grid(unsigned(cdiv(T, 4))), block(256);
+  if (k <= 1) unpermute_sum_kernel<1><<<grid, block, 0, st>>>(dxp, ros, e1, e2, T, k, d, dx);
+  else if (k <= 2) unpermute_sum_kernel<2><<<grid, block, 0, st>>>(dxp, ros, e1, e2, T, k, d, dx);
+  else if (k <= 4) unpermute_sum_kernel<4><<<grid, block, 0, st>>>(dxp, ros, e1, e2, T, k, d, dx);
+  else if (k <= 8) unpermute_sum_kernel<8><<<grid, block, 0, st>>>(dxp, ros, e1, e2, T, k, d, dx);
+  else unpermute_sum_kernel<16><<<grid, block, 0, st>>>(dxp, ros, e1, e2, T, k, d, dx);
   return hipGetLastError();
 }
 

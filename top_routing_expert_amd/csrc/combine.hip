@@ -6,12 +6,18 @@
 // gate-weighted sum of expert outputs; dropped slots add nothing, the token
 // travels on through the caller's residual, "MoEs and Transformers").
 #include "common.hpp"
+#include "gemm_common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 // One wave per token; each lane owns 4 consecutive floats per 256-float slab.
-// The slot loop is sequential, so the sum order is fixed.
+// A token's slot rows are the same for the whole wave, so each slot row is
+// read through its own buffer descriptor (an empty one for a dropped slot,
+// whose loads return zeros): the loads of all KM slots of a slab go out
+// together with no branch, instead of one load round trip per slot.  The
+// slot sum keeps its fixed order and skips dropped slots.
+template <int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ row_of_slot,
                                                       const float* __restrict__ gate,
@@ -20,23 +26,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + w;
   if (t >= T) return;
-  int rows[16];
-  float gs[16];
-  for (int j = 0; j < 16; ++j) {
-    rows[j] = j < k ? row_of_slot[int64_t(t) * k + j] : -1;
-    gs[j] = j < k ? gate[int64_t(t) * k + j] : 0.0f;
+  // lane j fetches slot j's row and gate; every lane then takes them as scalars
+  const int my_row = l < k ? row_of_slot[int64_t(t) * k + l] : -1;
+  const float my_g = l < k ? gate[int64_t(t) * k + l] : 0.0f;
+  int rows[KM];
+  float gs[KM];
+  rsrc_t rs[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    rows[j] = __builtin_amdgcn_readlane(my_row, j);
+    gs[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), j));
+    rs[j] = make_rsrc(rows[j] >= 0 ? o + int64_t(rows[j]) * d : o, rows[j] >= 0 ? uint32_t(d) * 4 : 0u);
   }
   const int nv = d >> 2;
   for (int c = l; c < nv; c += 64) {
+    floatx4 v[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      v[j] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs[j], uint32_t(c) * 16, 0, 0));
     float4 acc = shared ? reinterpret_cast<const float4*>(shared + int64_t(t) * d)[c]
                         : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
       if (rows[j] < 0) continue;
-      const float4 v = reinterpret_cast<const float4*>(o + int64_t(rows[j]) * d)[c];
-      acc.x = fmaf(gs[j], v.x, acc.x);
-      acc.y = fmaf(gs[j], v.y, acc.y);
-      acc.z = fmaf(gs[j], v.z, acc.z);
-      acc.w = fmaf(gs[j], v.w, acc.w);
+      acc.x = fmaf(gs[j], v[j][0], acc.x);
+      acc.y = fmaf(gs[j], v[j][1], acc.y);
+      acc.z = fmaf(gs[j], v[j][2], acc.z);
+      acc.w = fmaf(gs[j], v[j][3], acc.w);
     }
     reinterpret_cast<float4*>(y + int64_t(t) * d)[c] = acc;
   }
@@ -104,8 +120,12 @@ hipError_t launch_zero_i32(int32_t* out, int64_t n, hipStream_t st) {
 
 hipError_t launch_combine(const float* o, const int32_t* row_of_slot, const float* gate,
                           const float* shared, int T, int k, int d, float* y, hipStream_t st) {
-  combine_kernel<<<dim3(unsigned(cdiv(T, 4))), dim3(256), 0, st>>>(o, row_of_slot, gate, shared, T,
-                                                                    k, d, y);
+  const dim3 grid(unsigned(cdiv(T, 4))), block(256);
+  if (k <= 1) combine_kernel<1><<<grid, block, 0, st>>>(o, row_of_slot, gate, shared, T, k, d, y);
+  else if (k <= 2) combine_kernel<2><<<grid, block, 0, st>>>(o, row_of_slot, gate, shared, T, k, d, y);
+  else if (k <= 4) combine_kernel<4><<<grid, block, 0, st>>>(o, row_of_slot, gate, shared, T, k, d, y);
+  else if (k <= 8) combine_kernel<8><<<grid, block, 0, st>>>(o, row_of_slot, gate, shared, T, k, d, y);
+  else combine_kernel<16><<<grid, block, 0, st>>>(o, row_of_slot, gate, shared, T, k, d, y);
   return hipGetLastError();
 }
 
