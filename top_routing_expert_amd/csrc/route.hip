@@ -152,7 +152,7 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
     // unrolled): lane j of the token's group keeps round j's expert and gate,
     // which it writes below; the first two gates are kept for the random
     // second-expert rule.
-    int my_e = 0, e1 = 0;
+    int my_e = 0;
     float my_g = 0.0f, g0 = 0.0f, g1 = 0.0f, gs = 0.0f;
 #pragma unroll 1
     for (int j = 0; j < k; ++j) {
@@ -190,10 +190,7 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[R
         my_g = ge;
       }
       if (j == 0) g0 = ge;
-      if (j == 1) {
-        g1 = ge;
-        e1 = e;
-      }
+      if (j == 1) g1 = ge;
       gs += ge;
     }
     // Random second expert (k = 2): keep it iff u < 2 s2 / (s1 + s2); a skipped
