@@ -85,6 +85,10 @@ def _bounded(got, ref, cond, what):
     dict(routing="noisy_topk", aux_coef=0.1, z_coef=0.05, F_shared=64),
     dict(routing="gshard", priority="slot", capacity_factor=0.9, aux_coef=0.1),
     dict(routing="hash", score="sigmoid", aux_coef=0.1),
+    # 9..16 slots per token (the 16-slot combine, combine-backward and
+    # unpermute kernels), with drops
+    dict(E=32, k=12, aux_coef=0.05, capacity_factor=0.7),
+    dict(E=32, k=16, score="sigmoid", aux_coef=0.05),
 ])
 def test_layer_bwd_fp32(over):
     p = presets.get("c1", train=True, **over)

@@ -578,7 +578,10 @@ def test_variant_router_layer(name, over):
 
 @pytest.mark.parametrize("over", [dict(T=200), dict(T=1), dict(k=8, renorm=False),
                                   dict(E=1, k=1, renorm=False), dict(score="sigmoid", F_shared=64),
-                                  dict(score="sqrt_softplus", act="gelu", T=333, capacity_factor=0.7)])
+                                  dict(score="sqrt_softplus", act="gelu", T=333, capacity_factor=0.7),
+                                  # the 9..16-slot kernels: every expert chosen, and k = 16 with drops
+                                  dict(E=16, k=16, renorm=False),
+                                  dict(E=32, k=16, score="sigmoid", capacity_factor=0.6)])
 def test_layer_fwd_fp32_edge_cases(over):
     p = presets.get("c1", **over)
     inp = synth.make_inputs(p, seed=4)

@@ -32,7 +32,10 @@ __device__ __forceinline__ float wave_max(float v) {
 //   dO[row] = gate[t,j] * dy[t]   (x element type, feeds the expert dgrad/wgrad)
 //   dg[t,j] = <dy[t], o[row]>     (fp32; 0 for a dropped slot)
 // and dy_x[t] = dy[t] in the x element type (the shared expert's gradient).
-template <bool BF16>
+// As in the forward combine, each slot row of o is read through its own
+// buffer descriptor (empty for a dropped slot), so the KM slot loads of a
+// slab are in flight together; each lane visits its slabs in order.
+template <bool BF16, int KM>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const float* __restrict__ dy, const float* __restrict__ o, const int32_t* __restrict__ ros,
     const float* __restrict__ gate, int T, int k, int d, void* __restrict__ dO,
@@ -40,59 +43,48 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   if (t >= T) return;
-  int rows[BWD_KMAX];
-  float gs[BWD_KMAX], dot[BWD_KMAX];
+  const int my_row = l < k ? ros[int64_t(t) * k + l] : -1;
+  const float my_g = l < k ? gate[int64_t(t) * k + l] : 0.0f;
+  int rows[KM];
+  float gs[KM], dot[KM];
+  rsrc_t rs[KM];
 #pragma unroll
-  for (int j = 0; j < BWD_KMAX; ++j) {
-    rows[j] = j < k ? ros[int64_t(t) * k + j] : -1;
-    gs[j] = j < k ? gate[int64_t(t) * k + j] : 0.0f;
+  for (int j = 0; j < KM; ++j) {
+    rows[j] = __builtin_amdgcn_readlane(my_row, j);
+    gs[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), j));
+    rs[j] = make_rsrc(rows[j] >= 0 ? o + int64_t(rows[j]) * d : o, rows[j] >= 0 ? uint32_t(d) * 4 : 0u);
     dot[j] = 0.0f;
   }
   const float4* dyr = reinterpret_cast<const float4*>(dy + int64_t(t) * d);
   const int n4 = d >> 2;
-  // four 16-byte chunks per lane per pass, all loads of a pass issued before use
-  for (int c0 = l; c0 < n4; c0 += 256) {
-    float4 v[4];
+  for (int c = l; c < n4; c += 64) {
+    const float4 v = dyr[c];
+    floatx4 ov[KM];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      v[u] = c0 + 64 * u < n4 ? dyr[c0 + 64 * u] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < KM; ++j)
+      ov[j] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs[j], uint32_t(c) * 16, 0, 0));
     if (dy_x) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + 64 * u;
-        if (c >= n4) continue;
-        if constexpr (BF16)
-          reinterpret_cast<uint2*>(static_cast<uint16_t*>(dy_x) + int64_t(t) * d)[c] =
-              make_uint2(pack_bf2(v[u].x, v[u].y), pack_bf2(v[u].z, v[u].w));
-        else
-          reinterpret_cast<float4*>(static_cast<float*>(dy_x) + int64_t(t) * d)[c] = v[u];
-      }
+      if constexpr (BF16)
+        reinterpret_cast<uint2*>(static_cast<uint16_t*>(dy_x) + int64_t(t) * d)[c] =
+            make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+      else
+        reinterpret_cast<float4*>(static_cast<float*>(dy_x) + int64_t(t) * d)[c] = v;
     }
 #pragma unroll
-    for (int j = 0; j < BWD_KMAX; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (rows[j] < 0) continue;
-      const float4* orow = reinterpret_cast<const float4*>(o + int64_t(rows[j]) * d);
-      float4 ov[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        ov[u] = c0 + 64 * u < n4 ? orow[c0 + 64 * u] : make_float4(0.f, 0.f, 0.f, 0.f);
+      dot[j] += v.x * ov[j][0] + v.y * ov[j][1] + v.z * ov[j][2] + v.w * ov[j][3];
       const float g = gs[j];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + 64 * u;
-        if (c >= n4) continue;
-        dot[j] += v[u].x * ov[u].x + v[u].y * ov[u].y + v[u].z * ov[u].z + v[u].w * ov[u].w;
-        if constexpr (BF16)
-          reinterpret_cast<uint2*>(static_cast<uint16_t*>(dO) + int64_t(rows[j]) * d)[c] =
-              make_uint2(pack_bf2(g * v[u].x, g * v[u].y), pack_bf2(g * v[u].z, g * v[u].w));
-        else
-          reinterpret_cast<float4*>(static_cast<float*>(dO) + int64_t(rows[j]) * d)[c] =
-              make_float4(g * v[u].x, g * v[u].y, g * v[u].z, g * v[u].w);
-      }
+      if constexpr (BF16)
+        reinterpret_cast<uint2*>(static_cast<uint16_t*>(dO) + int64_t(rows[j]) * d)[c] =
+            make_uint2(pack_bf2(g * v.x, g * v.y), pack_bf2(g * v.z, g * v.w));
+      else
+        reinterpret_cast<float4*>(static_cast<float*>(dO) + int64_t(rows[j]) * d)[c] =
+            make_float4(g * v.x, g * v.y, g * v.z, g * v.w);
     }
   }
 #pragma unroll
-  for (int j = 0; j < BWD_KMAX; ++j) {
+  for (int j = 0; j < KM; ++j) {
     if (j < k) {  // k is uniform over the wave
       const float s = wave_sum(dot[j]);
       if (l == 0) dg[int64_t(t) * k + j] = rows[j] >= 0 ? s : 0.0f;
@@ -360,9 +352,18 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(
 hipError_t launch_combine_bwd(const float* dy, const float* o, const int32_t* ros, const float* gate,
                               int T, int k, int d, bool bf16, void* dO, float* dg, void* dy_x,
                               hipStream_t st) {
-  const unsigned grid = unsigned(cdiv(T, 4));
-  if (bf16) combine_bwd_kernel<true><<<grid, 256, 0, st>>>(dy, o, ros, gate, T, k, d, dO, dg, dy_x);
-  else combine_bwd_kernel<false><<<grid, 256, 0, st>>>(dy, o, ros, gate, T, k, d, dO, dg, dy_x);
+  const dim3 grid(unsigned(cdiv(T, 4))), block(256);
+#define MOE_CBWD(KM)                                                                           \
+  (bf16 ? combine_bwd_kernel<true, KM><<<grid, block, 0, st>>>(dy, o, ros, gate, T, k, d, dO, dg, \
+                                                             dy_x)                           \
+        : combine_bwd_kernel<false, KM><<<grid, block, 0, st>>>(dy, o, ros, gate, T, k, d, dO, dg, \
+                                                              dy_x))
+  if (k <= 1) MOE_CBWD(1);
+  else if (k <= 2) MOE_CBWD(2);
+  else if (k <= 4) MOE_CBWD(4);
+  else if (k <= 8) MOE_CBWD(8);
+  else MOE_CBWD(16);
+#undef MOE_CBWD
   return hipGetLastError();
 }
 
