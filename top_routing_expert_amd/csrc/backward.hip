@@ -295,13 +295,37 @@ hipError_t launch_noise_grad(const float* dz, const float* noise, const float* z
 }
 
 // out[i] = sum over z of P[z][i], z in order.
-__global__ void sum_partials_kernel(const float* __restrict__ P, int nz, int64_t n,
-                                    float* __restrict__ out) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.0f;
-  for (int z = 0; z < nz; ++z) s += P[int64_t(z) * n + i];
-  out[i] = s;
+// Four consecutive elements per thread (16-byte loads when n is a multiple of
+// 4), the loads of four partials in flight; each element still adds its
+// partials in z order.  out may be P itself (each element is read before it
+// is written, by the same thread).
+__global__ void sum_partials_kernel(const float* P, int nz, int64_t n, float* out) {
+  const int64_t i4 = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  if ((n & 3) == 0) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int z = 0;
+    for (; z + 4 <= nz; z += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(P + int64_t(z + u) * n + i4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+      }
+    }
+    for (; z < nz; ++z) {
+      const float4 v = *reinterpret_cast<const float4*>(P + int64_t(z) * n + i4);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    *reinterpret_cast<float4*>(out + i4) = s;
+  } else {
+    for (int64_t i = i4; i < i4 + 4 && i < n; ++i) {
+      float s = 0.0f;
+      for (int z = 0; z < nz; ++z) s += P[int64_t(z) * n + i];
+      out[i] = s;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -389,7 +413,7 @@ hipError_t launch_strided_gemm(const void* A, bool a_bf16, int64_t sam, int64_t 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || out == nullptr) return e;
   const int64_t n = int64_t(M) * N;
-  sum_partials_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(P, nsplit, n, out);
+  sum_partials_kernel<<<unsigned(cdiv(cdiv(n, 4), 256)), 256, 0, st>>>(P, nsplit, n, out);
   return hipGetLastError();
 }
 
@@ -428,7 +452,21 @@ __global__ void dwg_reduce_kernel(const float* __restrict__ P, int nchunks, int 
   if (i >= int64_t(D) * E) return;
   const int dd = int(i / E), e = int(i % E);
   float acc = 0.0f;
-  for (int c = 0; c < nchunks; ++c) {
+  int c = 0;
+  // four chunks' loads in flight; chunks still added in order
+  for (; c + 4 <= nchunks; c += 4) {
+    float v[4][3];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* p = P + (int64_t(c + u) * D + dd) * N3;
+      v[u][0] = p[e];
+      v[u][1] = p[E + e];
+      v[u][2] = p[2 * E + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += (v[u][0] + v[u][1]) + v[u][2];
+  }
+  for (; c < nchunks; ++c) {
     const float* p = P + (int64_t(c) * D + dd) * N3;
     acc += (p[e] + p[E + e]) + p[2 * E + e];
   }
@@ -455,7 +493,7 @@ hipError_t launch_dwg_reduce(const float* P, int nchunks, int D, int N3, int E, 
 }
 
 hipError_t launch_sum_partials(const float* P, int nz, int64_t n, float* out, hipStream_t st) {
-  sum_partials_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(P, nz, n, out);
+  sum_partials_kernel<<<unsigned(cdiv(cdiv(n, 4), 256)), 256, 0, st>>>(P, nz, n, out);
   return hipGetLastError();
 }
 
