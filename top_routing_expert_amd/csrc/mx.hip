@@ -144,21 +144,25 @@ __global__ __launch_bounds__(256) void mx8_quantize_kernel(const void* __restric
                                                            int64_t rows, int K, int64_t stride,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales) {
-  const int per_row = K / 8;
+  // One wave per (8 rows, one 64-element k-block): lane = 8 * (row in the
+  // group) + (8-element slice), so a wave reads 128 contiguous bytes of each
+  // of its rows and writes 512 contiguous bytes of codes (8 rows of the block).
+  const int KB = K / 64;
   const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const bool live = t < rows * per_row;
-  const int64_t r = live ? t / per_row : 0;
-  const int c8 = live ? int(t - r * per_row) : 0;
+  const int64_t wv = t >> 6;
+  const int lane = int(t & 63);
+  const int64_t r = (wv / KB) * 8 + (lane >> 3);
+  const int kb = int(wv % KB), q = lane & 7;
+  const bool live = r < rows;
   float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live) load8(x, r * K + int64_t(c8) * 8, bf16, v);
+  if (live) load8(x, r * K + int64_t(kb) * 64 + q * 8, bf16, v);
   const int sc = scale_code(block_amax<8>(v, live), 8);
   if (!live) return;
   const int k = 127 - sc;
   const uint32_t p[2] = {e4m3_pack4(scale_pow2(v[0], k), scale_pow2(v[1], k), scale_pow2(v[2], k), scale_pow2(v[3], k)),
                          e4m3_pack4(scale_pow2(v[4], k), scale_pow2(v[5], k), scale_pow2(v[6], k), scale_pow2(v[7], k))};
-  *reinterpret_cast<uint2*>(codes + (int64_t(c8 / 8) * stride + r) * 64 + (c8 % 8) * 8) =
-      make_uint2(p[0], p[1]);
-  if ((c8 & 7) == 0) scales[int64_t(c8 / 8) * stride + r] = uint8_t(sc);
+  *reinterpret_cast<uint2*>(codes + (int64_t(kb) * stride + r) * 64 + q * 8) = make_uint2(p[0], p[1]);
+  if (q == 0) scales[int64_t(kb) * stride + r] = uint8_t(sc);
 }
 
 // ---------------------------------------------------------------- grouped GEMM
@@ -443,7 +447,7 @@ hipError_t launch_mx_quantize_weights(const void* w, bool bf16, int64_t rows, in
 
 hipError_t launch_mx_quantize_act(const void* x, bool bf16, int64_t rows, int K, int64_t stride,
                                   uint8_t* codes, uint8_t* scales, hipStream_t st) {
-  const int64_t nt = rows * (K / 8);
+  const int64_t nt = cdiv(rows, 8) * (K / 64) * 64;   // one wave per 8 rows x 64 k
   if (nt == 0) return hipSuccess;
   mx8_quantize_kernel<<<unsigned(cdiv(nt, 256)), 256, 0, st>>>(x, bf16, rows, K, stride, codes,
                                                                scales);
