@@ -180,7 +180,13 @@ def _act_bwd_bound(cA, h, F, act):
     # 1024 routed rows per expert (the c3 and c4 training shapes' row counts)
     # at small widths, one with the shared expert beside them
     ("c3", dict(T=4096, d=256, F=256)),
-    ("c4", dict(T=8192, d=256, F=128, F_shared=128))])
+    ("c4", dict(T=8192, d=256, F=128, F_shared=128)),
+    # long reductions (K >= 10240) whose last, partial round of tiles is cut
+    # into K segments (256 compute units): in the down projection and dXp,
+    # 291 tiles of 128x128 (35 past one whole round, 4 segments each), and
+    # 20 tiles of 128x256 (all split, 4 segments each)
+    ("c3", dict(T=4096, E=64, d=384, F=10240)),
+    ("c3", dict(T=1024, d=256, F=10240))])
 def test_layer_bwd_full_size(name, over):
     """Every expert's dW13 and dW2, every routed row's dH, every token's dx and
     the shared expert's gradients, on the GPU's own routing:

@@ -297,7 +297,12 @@ def test_expert_ffn_parity(name):
     ("c2", dict(T=4096, E=8, d=4096, F=128)),
     # the activation as one bf16 rounding (GELU), and as (hi, lo) pairs (SwiGLU)
     ("c2", dict(T=300, d=128, F=128, act_pair=False)),
-    ("c4", dict(T=200, d=128, F=256, act_pair=True))])
+    ("c4", dict(T=200, d=128, F=256, act_pair=True)),
+    # down projections over K >= 10240 whose last, partial round of tiles is
+    # cut into K segments (256 compute units): 291 tiles of 128x128 (35 split
+    # four ways beside whole ones), and 20 tiles of 128x256 (all split)
+    ("c3", dict(T=4096, E=64, d=384, F=10240)),
+    ("c3", dict(T=1024, d=256, F=10240))])
 def test_expert_ffn_short_k(name, over):
     p, inp, x, w = case(name, **over)
     ref = orc.route(inp["x"], inp["Wg"], p.k, p.score, p.renorm, p.gate_scale, inp["offset"],

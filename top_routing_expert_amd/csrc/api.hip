@@ -131,15 +131,22 @@ PermWs plan_perm(Carver& c, const moe_dims* d, const moe_opts* o) {
   return p;
 }
 
-struct FfnWs { size_t tile_up, tile_down, act; };
+// sk_part, sk_tab: the down projection's split of a partial last round of
+// tiles (bf16 layers; see GemmArgs).
+struct FfnWs { size_t tile_up, tile_down, act, sk_part, sk_tab; };
 // a_cols: columns of the activation buffer (F, or 2F for bf16 pairs)
-FfnWs plan_ffn(Carver& c, int64_t G, int64_t max_rows, int64_t a_cols, int eb, bool need_act) {
+FfnWs plan_ffn(Carver& c, int64_t G, int64_t max_rows, int64_t a_cols, int eb, bool need_act,
+               bool split = true) {
   FfnWs f;
   f.tile_up = c.take(size_t(G + 1) * 4);
   f.tile_down = c.take(size_t(G + 1) * 4);
   f.act = need_act ? c.take(size_t(max_rows) * a_cols * eb) : 0;
+  split = split && eb == 2 && max_rows > 0;
+  f.sk_part = c.take(split ? GB_SK_PART_BYTES : 0);
+  f.sk_tab = c.take(split ? GB_SK_TAB_BYTES : 0);
   return f;
 }
+
 
 struct FwdWs {
   RouteWs route;
@@ -154,7 +161,7 @@ FwdWs plan_fwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   f.route = plan_route(c, d, o);
   f.perm = plan_perm(c, d, o);
   f.ffn = plan_ffn(c, d->E, Tk, d->F, eb, false);
-  f.ffn_shared = plan_ffn(c, 1, d->T, d->F_shared, eb, false);
+  f.ffn_shared = plan_ffn(c, 1, d->T, d->F_shared, eb, false, false);
   f.idx = c.take(size_t(Tk) * 4);
   f.gate = c.take(size_t(Tk) * 4);
   f.counts = c.take(size_t(d->E) * 4);
@@ -174,6 +181,16 @@ FwdWs plan_fwd(Carver& c, const moe_dims* d, const moe_opts* o) {
 
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// The split of a partial last round of tiles into K segments (bf16 GEMMs with
+// an fp32 store), on the workspace regions of `fw`.
+void set_split(GemmArgs& g, void* ws, const FfnWs& fw) {
+  if (fw.sk_part == fw.sk_tab) return;   // no regions carved
+  g.sk_part = at<float>(ws, fw.sk_part);
+  g.sk_tab = at<int32_t>(ws, fw.sk_tab);
+  g.sk_cus = gemm_concurrent_tiles();
+  if (g.sk_cus < 2) g.sk_part = nullptr;
+}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -315,6 +332,7 @@ int do_ffn(const moe_opts* o, int64_t d, int64_t G, int64_t max_rows, int64_t F,
   g2.h_save = nullptr;
   g2.n_b = 0;
   g2.tile_start = at<int32_t>(ws, fw.tile_down);
+  set_split(g2, ws, fw);
   MOE_TRY(bf16 ? launch_grouped_gemm_bf16(g2, st) : launch_grouped_gemm_f32(g2, st));
   return MOE_OK;
 }
@@ -428,7 +446,7 @@ BwdWs plan_bwd(Carver& c, const moe_dims* d, const moe_opts* o) {
   const int64_t R = d->T * d->k, nu = n_up(o, d->F);
   const int64_t Fs = d->F_shared;
   b.ffn = plan_ffn(c, d->E, R, d->F, int(eb), false);
-  b.ffn_s = plan_ffn(c, 1, d->T, Fs, int(eb), false);
+  b.ffn_s = plan_ffn(c, 1, d->T, Fs, int(eb), false, false);
   b.dO = c.take(size_t(R) * d->d * eb);
   b.dg = c.take(size_t(R) * 4);
   b.dH = c.take(size_t(R) * nu * eb);
@@ -824,9 +842,10 @@ int moe_layer_bwd(const moe_dims* d, const moe_opts* o, const moe_weights* w,
                                   swiglu ? EPI_SWIGLU_BWD : EPI_GELU_BWD, dH, sv->h,
                                   nu, swiglu ? F : 0),
                     ts, st));
-    MOE_TRY(gemm_on(o, gemm_dgrad(dH, w->W13, int64_t(nu) * D, sv->offsets, E, R, D,
-                                  nu, EPI_STORE_F32, at<void>(ws, b.dXp), nullptr, 0, 0),
-                    ts, st));
+    GemmArgs gx = gemm_dgrad(dH, w->W13, int64_t(nu) * D, sv->offsets, E, R, D, nu,
+                             EPI_STORE_F32, at<void>(ws, b.dXp), nullptr, 0, 0);
+    set_split(gx, ws, b.ffn);
+    MOE_TRY(gemm_on(o, gx, ts, st));
     // routed experts, weight gradient over each expert's rows: dW13[e] = dH_e^T x_e
     MOE_TRY(gemm_on(o, gemm_wgrad(dH, sv->x_perm, sv->offsets, E, nu, D, grads->dW13),
                     ts, st));

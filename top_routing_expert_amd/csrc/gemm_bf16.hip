@@ -46,6 +46,10 @@
 //    tile (b % 8) * ceil(tiles / 8) + b / 8, so each XCD works through a
 //    contiguous run of tiles (same expert, consecutive n-tiles, m-tiles
 //    fastest) and its L2 holds the shared A rows and weight panels.
+//  * Long reductions with an fp32 store: when the tiles leave a last round
+//    that fills at most half of the compute units, those tiles are cut into
+//    K segments run by extra workgroups after the whole tiles, and a second
+//    kernel adds their partial sums in segment order.
 //  * NP = 2 (SwiGLU forward): the gate rows n0.. and up rows up_off+n0.. of
 //    W13 are two B panels multiplied against one A tile; the epilogue forms
 //    silu(gate) * up directly.
@@ -53,6 +57,8 @@
 //    stores), applies GELU / SwiGLU or their backward with hardware 2^x and
 //    reciprocal and the bf16 conversion instruction, and writes bf16 or fp32
 //    with non-temporal stores.
+#include <atomic>
+
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -190,6 +196,9 @@ void gg_bf16_kernel(GemmArgs g) {
 
   int32_t total;
   int tile;
+  // K segments of a split tile: this block's segment (-1: a whole tile), the
+  // segment count, and the number of whole tiles (split tiles follow them).
+  int seg = -1, nseg = 1, whole = 0;
   if constexpr (MODE == GM_KGROUP) {
     // A tile's work grows with its group's rows, so groups are taken heaviest
     // first (ts[r] = the group of rank r by rows, descending, ties to the
@@ -213,10 +222,35 @@ void gg_bf16_kernel(GemmArgs g) {
     if (tile >= total) return;
   } else {
     total = plan_tiles<BM, BN>(g, ts);
-    const int per = (total + 7) >> 3;
+    whole = total;
+    if (EPI == EPI_STORE_F32 && g.sk_part) {
+      // A last round of at most half the concurrent workgroups would leave
+      // most compute units idle while it runs: its tiles are split along K
+      // into S segments (S * tiles <= sk_cus), all of which run at once.
+      const int tail = total % g.sk_cus;
+      if (tail > 0 && 2 * tail <= g.sk_cus) {
+        nseg = min(4, g.sk_cus / tail);
+        whole = total - tail;
+      }
+      // (every thread of block 0 stores the same two values: no branch on
+      // the thread index, so the tile's values stay wave-uniform)
+      if (blockIdx.x == 0) {
+        g.sk_tab[0] = total - whole;
+        g.sk_tab[1] = nseg;
+      }
+    }
     const int bid = blockIdx.x;
-    tile = (bid & 7) * per + (bid >> 3);
-    if ((bid >> 3) >= per || tile >= total) return;
+    if (!g.sk_part || bid < g.sk_grid0) {
+      const int per = (whole + 7) >> 3;
+      tile = (bid & 7) * per + (bid >> 3);
+      if ((bid >> 3) >= per || tile >= whole) return;
+    } else {
+      // blocks past sk_grid0: segment sidx % S of split tile sidx / S
+      const int sidx = bid - g.sk_grid0;
+      if (sidx >= (total - whole) * nseg) return;
+      tile = whole + sidx / nseg;
+      seg = sidx % nseg;
+    }
   }
   // Row stride of a K-major B: [rows, ldb] in the K-grouped mode, [K, N] otherwise.
   const int64_t ldb = (MODE == GM_KGROUP && g.ldb) ? g.ldb : int64_t(g.N);
@@ -242,6 +276,12 @@ void gg_bf16_kernel(GemmArgs g) {
   } else {
     locate_tile(ts, g.offsets, g.G, tile, BM, BN, tc);
     K = g.K;
+    if (seg == 0) {
+      int32_t* e = g.sk_tab + 2 + 3 * (tile - whole);
+      e[0] = tc.row0 + tc.m0;
+      e[1] = tc.n0;
+      e[2] = min(tc.M - tc.m0, BM);
+    }
     A = static_cast<const uint16_t*>(g.A);
     B = static_cast<const uint16_t*>(g.B) + int64_t(tc.grp) * g.b_group_stride;
   }
@@ -346,7 +386,10 @@ void gg_bf16_kernel(GemmArgs g) {
   const int a_lane = (8 * (gq >> 1) + (jq >> 2)) * (2 * BM) + 8 * (jq & 3);
   const int b_lane = (8 * (gq >> 1) + (jq >> 2)) * (2 * BN) + 8 * (jq & 3);
 
-  const int KT = int(cdiv(K, GB_BK));
+  // K steps [k_lo, k_lo + NK) of this block: all of them, or its segment's.
+  const int KT0 = int(cdiv(K, GB_BK));
+  const int k_lo = seg >= 0 ? seg * KT0 / nseg : 0;
+  const int KT = seg >= 0 ? (seg + 1) * KT0 / nseg - k_lo : KT0;
   // A wave whose half of the tile lies wholly past its group's last row (the
   // last row tile of a group with few rows) skips its fragment reads and
   // MFMAs; it still issues its share of every stage's loads and meets every
@@ -359,7 +402,7 @@ void gg_bf16_kernel(GemmArgs g) {
   const int krot = KT > 0 ? tile % KT : 0;
   auto kcol = [&](int j) {
     const int kn = j + krot;
-    return (kn < KT ? kn : kn - KT) * GB_BK;
+    return (k_lo + (kn < KT ? kn : kn - KT)) * GB_BK;
   };
   // NS-stage ring: the loads of K steps kt+1 .. kt+NS-2 are in flight while
   // step kt multiplies, and step kt+NS-1 is issued into the slot step kt-1
@@ -483,9 +526,15 @@ void gg_bf16_kernel(GemmArgs g) {
         const int64_t row = tc.row0 + mr;
         const float4 v0 = *reinterpret_cast<const float4*>(cw + rl * CST + c4);
         if constexpr (EPI == EPI_STORE_F32) {
-          float* outp = static_cast<float*>(g.out) +
-                        (MODE == GM_KGROUP ? int64_t(tc.grp) * g.M_fixed * g.N : 0);
-          st_f4<NT_OUT>(outp + row * g.N + n, v0);
+          if (seg >= 0) {
+            // partial sum of a K segment: slot (split tile, segment), [BM][BN]
+            float* pp = g.sk_part + (int64_t(tile - whole) * nseg + seg) * (BM * BN);
+            *reinterpret_cast<float4*>(pp + (mr - tc.m0) * BN + (n - tc.n0)) = v0;
+          } else {
+            float* outp = static_cast<float*>(g.out) +
+                          (MODE == GM_KGROUP ? int64_t(tc.grp) * g.M_fixed * g.N : 0);
+            st_f4<NT_OUT>(outp + row * g.N + n, v0);
+          }
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
           // v0 = dA[row, n..n+3]; h_in row = [gate | up]; out row = [dgate | dup]
           const uint16_t* hr = static_cast<const uint16_t*>(g.h_in) + row * g.n_b;
@@ -527,17 +576,70 @@ void gg_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Output rows of the split tiles: the sum of their S segments' partial sums,
+// added in segment order (the result depends only on the shape and the
+// operands).  Work item i is 16 rows (chunk i % (BM / 16)) of split tile
+// i / (BM / 16); the blocks stride over the items, and with no split tile
+// they return at once.  The table written by the GEMM gives each split
+// tile's first output row, first column and number of rows.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void gg_split_sum_kernel(const float* __restrict__ part,
+                                                           const int32_t* __restrict__ tab,
+                                                           float* __restrict__ out, int N) {
+  constexpr int RB = 16, LPR = BN / 4, RPP = 256 / LPR;
+  const int items = tab[0] * (BM / RB), S = tab[1];
+  const int c4 = (threadIdx.x % LPR) * 4;
+  for (int i = blockIdx.x; i < items; i += gridDim.x) {
+    const int ti = i / (BM / RB), rb = i % (BM / RB);
+    const int* e = tab + 2 + 3 * ti;
+    const int64_t row0 = e[0];
+    const int n0 = e[1], rows = e[2];
+    const float* p0 = part + int64_t(ti) * S * (BM * BN);
+#pragma unroll
+    for (int it = 0; it < RB / RPP; ++it) {
+      const int r = rb * RB + it * RPP + threadIdx.x / LPR;
+      if (r < rows) {
+        const float* p = p0 + r * BN + c4;
+        float4 v = *reinterpret_cast<const float4*>(p);
+        for (int s = 1; s < S; ++s) {
+          const float4 u = *reinterpret_cast<const float4*>(p + s * (BM * BN));
+          v.x += u.x;
+          v.y += u.y;
+          v.z += u.z;
+          v.w += u.w;
+        }
+        st_f4<(GB_NT & (GB_NT_FWD_F32 | GB_NT_DGRAD)) != 0>(out + (row0 + r) * N + n0 + c4, v);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int NP, int EPI, int MODE, int WV = GB_WAVES>
-void launch_cfg(const GemmArgs& g, hipStream_t st) {
+void launch_cfg(const GemmArgs& g0, hipStream_t st) {
+  GemmArgs g = g0;
   const int64_t bound = MODE == GM_KGROUP ? int64_t(g.G) * (g.M_fixed / BM) * (g.N / BN)
                                           : (cdiv(g.max_rows, BM) + g.G) * (g.N / BN);
-  const unsigned grid = unsigned(cdiv(bound, 8) * 8);
+  unsigned grid = unsigned(cdiv(bound, 8) * 8);
+  // Only long reductions are split: the split costs a second launch and the
+  // partial sums' traffic (about 10 us), a last round of tiles with K >= 10240
+  // several hundred.
+  const bool split = MODE != GM_KGROUP && EPI == EPI_STORE_F32 && g.sk_part && g.sk_cus >= 2 &&
+                     g.K >= GB_SK_MIN_K;
+  if (split) {
+    g.sk_grid0 = int(grid);
+    grid += unsigned(g.sk_cus);
+  } else {
+    g.sk_part = nullptr;
+  }
   constexpr size_t lds_bytes = size_t(gb_stages(BM, BN, NP)) * (BM + NP * BN) * 128;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&gg_bf16_kernel<BM, BN, NP, EPI, MODE, WV>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
   (void)attr;
   gg_bf16_kernel<BM, BN, NP, EPI, MODE, WV><<<dim3(grid), dim3(64 * WV), lds_bytes, st>>>(g);
+  if (split)
+    gg_split_sum_kernel<BM, BN><<<dim3(unsigned(g.sk_cus)), dim3(256), 0, st>>>(
+        g.sk_part, g.sk_tab, static_cast<float*>(g.out), g.N);
 }
 
 template <int EPI, int MODE>
@@ -557,6 +659,19 @@ static void launch_rows_np1(const GemmArgs& g, bool bm256, bool bn256, hipStream
 // each CU streams twice the weight bytes per stage (32 experts x 245 rows,
 // K = 4096, N = 1024: 85 vs 90 us against 256 x 128; the data gradient 116 vs
 // 119 us).  K-grouped mode: 256 x 256 when the output dimensions allow it.
+int gemm_concurrent_tiles() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    n = n < GB_SK_SLOTS ? n : GB_SK_SLOTS;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.G == 0) return hipSuccess;
   if (g.mode == GM_KGROUP) {

@@ -103,7 +103,26 @@ struct GemmArgs {
   int out_ld;
   int lo_off;
   int b_kwrap;
+  // Split of a partial last round (bf16 row modes with an fp32 store and
+  // K >= GB_SK_MIN_K; nullable sk_part = off).  When the tiles leave a last
+  // round that fills at most half of the sk_cus workgroups that run at once,
+  // those tiles are cut into S <= 4 K segments (S * tiles <= sk_cus) whose
+  // fp32 partial sums go to sk_part and are added in segment order by a
+  // second kernel; the whole tiles run as before.  sk_part holds GB_SK_SLOTS
+  // tiles of BM * BN floats, sk_tab 2 + 3 * GB_SK_SLOTS / 2 ints.  sk_grid0
+  // is set by the launcher.
+  float* sk_part;
+  int32_t* sk_tab;
+  int sk_cus;
+  int sk_grid0;
 };
+constexpr int GB_SK_SLOTS = 256;
+constexpr int GB_SK_MIN_K = 10240;   // shortest reduction that is split
+constexpr size_t GB_SK_PART_BYTES = size_t(GB_SK_SLOTS) * 256 * 256 * 4;
+constexpr size_t GB_SK_TAB_BYTES = size_t(2 + 3 * GB_SK_SLOTS / 2) * 4;
+// Workgroups of the grouped GEMM that run at once on the current device (one
+// per compute unit), at most GB_SK_SLOTS.
+int gemm_concurrent_tiles();
 hipError_t launch_grouped_gemm_bf16(const GemmArgs& g, hipStream_t st);
 hipError_t launch_grouped_gemm_f32(const GemmArgs& g, hipStream_t st);
 
