@@ -90,30 +90,23 @@ int check_router_inputs(const moe_opts* o, const moe_router_inputs* ri) {
 }
 
 // ---- workspace plans -------------------------------------------------------
-// Logits of bf16 tokens for 64 or more (padded) experts run as one grouped-GEMM
-// launch: x . [hi; mid; lo]^T with the three bf16 planes of Wg stacked as the
-// rows of B, into z3 [T, np3] fp32, then a per-token kernel adds the planes and
-// runs the router epilogue.  (With 32 experts the fused logits kernel, which
-// keeps z on chip, is as fast.)
-bool route_gemm(const moe_dims* d, const moe_opts* o, int EP) {
-  return route_mfma(d, o, EP) && EP >= 64 && d->d % 64 == 0 &&
-         o->routing != MOE_ROUTING_NOISY_TOPK;
+// bf16 tokens with 64 or more (padded) experts: the wide kernel (64 tokens per
+// block, logits on chip, one fp32 accumulation over the three planes).
+bool route_wide(const moe_dims* d, const moe_opts* o, int EP) {
+  return route_mfma(d, o, EP) && EP >= 64;
 }
 
 struct RouteWs {
-  size_t wsplit, part_p, part_cnt, part_lse2, part_nf, zn, z3, off1;
-  int nblk, EP, np3;
-  bool gemm;
+  size_t wsplit, part_p, part_cnt, part_lse2, part_nf, zn;
+  int nblk, EP;
+  bool wide;
 };
 RouteWs plan_route(Carver& c, const moe_dims* d, const moe_opts* o) {
   RouteWs r;
   r.EP = route_pad_experts(int(d->E));
-  r.nblk = int(cdiv(d->T, ROUTE_BT));
-  r.gemm = route_gemm(d, o, r.EP);
-  r.np3 = int(cdiv(3 * r.EP, 128) * 128);
-  r.wsplit = c.take(size_t(r.gemm ? r.np3 : 3 * r.EP) * d->d * 2);
-  r.z3 = c.take(r.gemm ? size_t(d->T) * r.np3 * 4 : 0);
-  r.off1 = c.take(r.gemm ? 2 * 4 : 0);
+  r.wide = route_wide(d, o, r.EP);
+  r.nblk = int(cdiv(d->T, r.wide ? ROUTE_WIDE_BT : ROUTE_BT));
+  r.wsplit = c.take(size_t(3 * r.EP) * d->d * 2);
   r.part_p = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_cnt = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_lse2 = c.take(size_t(r.nblk) * 4);
@@ -217,6 +210,7 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
   a.x_bf16 = o->dtype == MOE_DTYPE_BF16;
   a.Wg = Wg;
   a.wsplit = at<uint16_t>(ws, rw.wsplit);
+  a.wfrag = at<float>(ws, rw.wsplit);
   a.offset = offset;
   a.bias = bias;
   a.T = int(d->T);
@@ -237,6 +231,19 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
   a.part_lse2 = at<float>(ws, rw.part_lse2);
   a.part_nf = at<int32_t>(ws, rw.part_nf);
   const bool mfma = route_mfma(d, o, rw.EP);
+  uint16_t* planes = at<uint16_t>(ws, rw.wsplit);
+  // the Wg planes in the layout the logits kernel reads, then the logits
+  auto logits_pass = [&](const float* W, const RouteArgs& ra) -> hipError_t {
+    if (rw.wide) {
+      hipError_t e = launch_wg_frag(W, ra.d, ra.E, ra.EP, reinterpret_cast<float*>(planes), st);
+      return e != hipSuccess ? e : launch_route_wide(ra, st);
+    }
+    if (mfma) {
+      hipError_t e = launch_wg_split(W, ra.d, ra.E, ra.EP, planes, st);
+      if (e != hipSuccess) return e;
+    }
+    return launch_route(ra, mfma, st);
+  };
   if (o->routing == MOE_ROUTING_NOISY_TOPK) {
     // first pass: zn = x . W_noise (raw logits of the noise projection)
     float* zn = zn_out ? zn_out : at<float>(ws, rw.zn);
@@ -245,30 +252,13 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
     an.offset = nullptr;
     an.logits = zn;
     an.logits_only = 1;
-    if (mfma)
-      MOE_TRY(launch_wg_split(ri->W_noise, a.d, a.E, a.EP, 0, at<uint16_t>(ws, rw.wsplit), nullptr,
-                              a.T, st));
-    MOE_TRY(launch_route(an, mfma, st));
+    MOE_TRY(logits_pass(ri->W_noise, an));
     a.noise = ri->noise;
     a.noise_logit = zn;
   }
   if (o->routing == MOE_ROUTING_RANDOM_SECOND) a.uniform = ri->uniform;
   if (o->routing == MOE_ROUTING_HASH) a.token_ids = ri->token_ids;
-  if (rw.gemm) {
-    int32_t* off1 = at<int32_t>(ws, rw.off1);
-    float* z3 = at<float>(ws, rw.z3);
-    MOE_TRY(launch_wg_split(Wg, a.d, a.E, a.EP, rw.np3 - 3 * a.EP, at<uint16_t>(ws, rw.wsplit),
-                            off1, a.T, st));
-    GemmArgs g{};
-    g.A = x; g.B = a.wsplit; g.offsets = off1; g.G = 1; g.max_rows = a.T; g.N = rw.np3; g.K = a.d;
-    g.epi = EPI_STORE_F32; g.out = z3; g.mode = GM_NT;
-    MOE_TRY(launch_grouped_gemm_bf16(g, st));
-    MOE_TRY(launch_route_from_partials(a, z3, rw.np3, st));
-  } else {
-    if (mfma)
-      MOE_TRY(launch_wg_split(Wg, a.d, a.E, a.EP, 0, at<uint16_t>(ws, rw.wsplit), nullptr, a.T, st));
-    MOE_TRY(launch_route(a, mfma, st));
-  }
+  MOE_TRY(logits_pass(Wg, a));
   if (counts || losses || n_nonfinite)
     MOE_TRY(launch_route_reduce(a, rw.nblk, o->aux_coef, o->z_coef, counts, losses, n_nonfinite, st));
   return MOE_OK;

@@ -127,18 +127,6 @@ __host__ __device__ constexpr int gb_stages(int BM, int BN, int NP) {
   return (BM + NP * BN) * 128 <= 32768 ? 4 : ((BM + NP * BN) * 128 <= 49152 ? 3 : 2);
 }
 
-// Wait until at most N of this wave's vector-memory loads are outstanding
-// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which would
-// wait for every outstanding load); LDS accesses are not moved across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
 // Segment swizzle of K-major rows: distinct in the low two bits and in bits
 // 1..2 over any four consecutive rows.
 __device__ __forceinline__ int kswz(int r) { return (r & 3) ^ ((r & 3) << 1); }

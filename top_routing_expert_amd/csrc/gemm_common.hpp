@@ -122,4 +122,16 @@ __device__ __forceinline__ void lds_load4(rsrc_t r, uint32_t voff, uint32_t soff
       r, (__attribute__((address_space(3))) void*)(lds_wave_base), 4, voff, soff, 0, 0);
 }
 
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding load); LDS accesses are not moved across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace moe

@@ -11,7 +11,8 @@ struct RouteArgs {
   const void* x;            // [T, d] bf16 or fp32
   int x_bf16;
   const float* Wg;          // [d, E]
-  const uint16_t* wsplit;   // [3][EP][d] bf16 planes of Wg (MFMA path)
+  const uint16_t* wsplit;   // [3][EP][d] bf16 planes of Wg (32-expert MFMA kernel)
+  const float* wfrag;       // Wg in the wide kernel's fp32 fragment layout
   const float* offset;      // nullable [E]
   const float* bias;        // nullable [E]
   int T, d, E, k, EP;
@@ -35,12 +36,15 @@ struct RouteArgs {
 constexpr int ROUTE_BT = 32;   // tokens per route block
 
 int route_pad_experts(int E);  // 32, 64, 128 or 256
-hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, int pad_rows, uint16_t* out,
-                           int32_t* off1, int T, hipStream_t st);
-// Route from z3 [T, ldz] fp32 = x . [planes of Wg]^T (columns p*EP + e).
-hipError_t launch_route_from_partials(const RouteArgs& a, const float* z3, int ldz,
-                                      hipStream_t st);
+// Wg [d, E] -> three bf16 planes [3][EP][d] (32-expert kernel), or Wg in the
+// wide kernel's fp32 fragment layout (d % 64 == 0, EP % 32 == 0).
+hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, uint16_t* out, hipStream_t st);
+hipError_t launch_wg_frag(const float* Wg, int d, int E, int EP, float* out, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, bool mfma, hipStream_t st);
+// bf16 tokens, EP >= 64: 64 tokens per block (partial-sum rows per 64 tokens),
+// logits kept on chip, Wg planes in the fragment layout; d % (64 * 256 / EP) == 0.
+constexpr int ROUTE_WIDE_BT = 64;
+hipError_t launch_route_wide(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, float z_coef,
                                int32_t* counts, float* losses, int32_t* n_nonfinite,
                                hipStream_t st);
