@@ -250,11 +250,10 @@ int moe_permute(const moe_dims* dims, const moe_opts* opts, const void* x,
  * memory or pass scratch (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, results and errors as
  * moe_permute minus ws/ws_bytes.  Its scratch (the dispatch's per-block
- * histogram and base tables, 2 x ceil(T*k/1024) x E int32, each rounded up to
- * 256 bytes) lives in a 1 MiB device array inside the library, one per GPU,
- * held until the process ends; larger problems (for instance E = 256 with
- * T*k above 524288 slots) return MOE_ERR_UNSUPPORTED before anything is
- * enqueued.  The array keeps the last call's contents and needs no clearing.
+ * histogram table, ceil(T*k/1024) x E int32 rounded up to 256 bytes) lives in
+ * a 1 MiB device array inside the library, one per GPU, held until the
+ * process ends; larger problems (for instance E = 256 with T*k above 1048576
+ * slots) return MOE_ERR_UNSUPPORTED before anything is enqueued.  The array keeps the last call's contents and needs no clearing.
  * Calls that overlap on one GPU (concurrent streams, host threads) share the
  * array and race: serialise them.  Allocates nothing and calls no allocating
  * routine. */

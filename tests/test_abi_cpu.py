@@ -163,8 +163,8 @@ def test_mx_entry_points_reject_bad_arguments(L):
 
 def test_noalloc_permute_limit(L):
     """moe_permute_noalloc refuses, before touching any pointer or the device,
-    problems whose dispatch tables exceed its 1 MiB scratch: with 256 experts
-    that is above 512 blocks of 1024 slots (T*k > 524288)."""
+    problems whose dispatch table exceeds its 1 MiB scratch: with 256 experts
+    that is above 1024 blocks of 1024 slots (T*k > 1048576)."""
     dummy = C.c_void_p(256)
 
     def call(T, x):
@@ -172,8 +172,8 @@ def test_noalloc_permute_limit(L):
         return L.moe_permute_noalloc(C.byref(B.dims_of(p)), C.byref(B.opts_of(p)), x, dummy,
                                      dummy, dummy, dummy, dummy, dummy, None)
 
-    assert call(65536, None) == B.MOE_ERR_INVALID_ARG    # T*k = 524288 fits: a null x is refused
-    assert call(65537, dummy) == B.MOE_ERR_UNSUPPORTED   # one block of slots too many
+    assert call(131072, None) == B.MOE_ERR_INVALID_ARG   # T*k = 1048576 fits: a null x is refused
+    assert call(131073, dummy) == B.MOE_ERR_UNSUPPORTED  # one block of slots too many
     assert call(1 << 20, dummy) == B.MOE_ERR_UNSUPPORTED
 
 

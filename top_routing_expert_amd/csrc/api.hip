@@ -115,12 +115,11 @@ RouteWs plan_route(Carver& c, const moe_dims* d, const moe_opts* o) {
   return r;
 }
 
-struct PermWs { size_t blockcnt, blockbase; int nblk; };
+struct PermWs { size_t blockcnt; int nblk; };
 PermWs plan_perm(Carver& c, const moe_dims* d, const moe_opts* o) {
   PermWs p;
   p.nblk = dispatch_blocks(int(d->T), int(d->k), o->priority == MOE_PRIORITY_SLOT);
   p.blockcnt = c.take(size_t(p.nblk) * d->E * 4);
-  p.blockbase = c.take(size_t(p.nblk) * d->E * 4);
   return p;
 }
 
@@ -270,11 +269,10 @@ int do_permute(const moe_dims* d, const moe_opts* o, const void* x, const int32_
   const int T = int(d->T), k = int(d->k), E = int(d->E);
   const int64_t C = capacity_of(d, o);
   int32_t* bc = at<int32_t>(ws, pw.blockcnt);
-  int32_t* bb = at<int32_t>(ws, pw.blockbase);
   const bool slot_major = o->priority == MOE_PRIORITY_SLOT;
   MOE_TRY(launch_dispatch_hist(idx, T, k, E, slot_major, bc, st));
-  MOE_TRY(launch_dispatch_scan(bc, pw.nblk, E, C, bb, counts, offsets, n_dropped, st));
-  MOE_TRY(launch_dispatch_permute(idx, T, k, E, C, slot_major, bb, offsets, x, int(d->d),
+  MOE_TRY(launch_dispatch_permute(idx, T, k, E, C, slot_major, bc, counts, offsets, n_dropped,
+                                  x, int(d->d),
                                   elem_bytes(o), ros, tor, xperm, st));
   return MOE_OK;
 }

@@ -36,95 +36,89 @@ __global__ __launch_bounds__(1024) void dispatch_hist_kernel(const int32_t* __re
   for (int e = threadIdx.x; e < E; e += blockDim.x) blockcnt[int64_t(blockIdx.x) * E + e] = hist[e];
 }
 
-// One block of 1024 threads: expert e's per-block counts are split into four
-// quarters of the blocks (thread e + 256 q takes quarter q, 16 loads in flight
-// per step), the quarters' sums give each quarter's base, and a second pass
-// writes the exclusive scan over the blocks.  Then the totals, the kept counts
-// min(total, C) and an exclusive scan over experts -> offsets.  C < 0: no
-// capacity.
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ blockcnt,
-                                                             int nblk, int E, int64_t C,
-                                                             int32_t* __restrict__ blockbase,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ n_dropped) {
-  __shared__ int32_t qsum[4][256];
-  __shared__ int32_t sk[256];
-  __shared__ int32_t sd[256];
-  const int tid = threadIdx.x, e = tid & 255, q = tid >> 8;
-  const int nq = (nblk + 3) / 4;
-  const int b0 = q * nq, b1 = min(nblk, b0 + nq);
-  int32_t part = 0;
-  if (e < E) {
-    for (int b = b0; b < b1; b += 16) {
-      int32_t c[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = b + i < b1 ? blockcnt[int64_t(b + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) part += c[i];
-    }
-  }
-  qsum[q][e] = part;
-  __syncthreads();
-  int32_t run = 0, total = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    run += i < q ? qsum[i][e] : 0;
-    total += qsum[i][e];
-  }
-  if (e < E) {
-    for (int b = b0; b < b1; b += 16) {
-      int32_t c[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = b + i < b1 ? blockcnt[int64_t(b + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (b + i < b1) blockbase[int64_t(b + i) * E + e] = run;
-        run += c[i];
-      }
-    }
-    if (q == 0 && counts) counts[e] = total;
-  }
-  const int32_t kept = (e < E) ? ((C >= 0 && int64_t(total) > C) ? int32_t(C) : total) : 0;
-  if (q == 0) {
-    sk[e] = kept;
-    sd[e] = (e < E) ? total - kept : 0;
-  }
-  __syncthreads();
-  // Hillis-Steele inclusive scan of kept counts and drop counts (threads 0..255).
-  for (int st = 1; st < 256; st <<= 1) {
-    const int32_t vk = (q == 0 && e >= st) ? sk[e - st] : 0;
-    const int32_t vd = (q == 0 && e >= st) ? sd[e - st] : 0;
-    __syncthreads();
-    if (q == 0) {
-      sk[e] += vk;
-      sd[e] += vd;
-    }
-    __syncthreads();
-  }
-  if (q == 0 && e < E) offsets[e] = sk[e] - kept;
-  if (tid == 0) {
-    offsets[E] = sk[255];
-    if (n_dropped) n_dropped[0] = sd[255];
-  }
-}
-
 // Stable ranks.  Block b covers the NT slots from b*NT in the order's sequence,
 // wave w the 64 from b*NT + 64w, one per lane.
+//   0. bases: from the per-block counts every block computes, for each expert,
+//      the count in the blocks before it (its base) and in all blocks (the
+//      total), then kept = min(total, C) and an exclusive scan over experts
+//      (the rows' offsets).  Expert e's blocks are split into four quarters
+//      (thread e + 256 q takes quarter q, 16 loads in flight per step) summed
+//      in a fixed order.  Block 0 also writes the counts, offsets and drops.
 //   1. peel: repeatedly take the expert of the first lane still pending,
 //      ballot the lanes holding that expert, rank = popcount of lower lanes;
 //      the leader records the wave's count for the expert;
-//   2. rank in expert = blockbase[b][e] + counts of lower waves + rank in wave;
+//   2. rank in expert = base[e] + counts of lower waves + rank in wave;
 //      kept iff rank < C; row = offsets[e] + rank.
 // The row copy is a separate, token-parallel kernel (permute_copy_kernel).
 template <int ORDER, int NT>
 __global__ __launch_bounds__(NT) void dispatch_rank_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int E, int64_t C,
-    const int32_t* __restrict__ blockbase, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ idx, int T, int k, int E, int64_t C, int nblk,
+    const int32_t* __restrict__ blockcnt, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped,
     int32_t* __restrict__ row_of_slot, int32_t* __restrict__ token_of_row) {
+  static_assert(NT == 1024, "four quarters of 256 expert lanes");
   __shared__ int32_t wavecnt[NT / 64][256];
+  __shared__ int32_t qsum[2][4][256];
+  __shared__ int32_t sbase[256], soff[256], sk[256], sd[256];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   for (int i = tid; i < (NT / 64) * 256; i += NT) (&wavecnt[0][0])[i] = 0;
+  {
+    const int e = tid & 255, q = tid >> 8;
+    const int nq = (nblk + 3) / 4;
+    const int b0 = q * nq, b1 = min(nblk, b0 + nq), bl = min(b1, int(blockIdx.x));
+    int32_t before = 0, part = 0;
+    if (e < E) {
+      for (int b = b0; b < b1; b += 16) {
+        int32_t c[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = b + i < b1 ? blockcnt[int64_t(b + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          part += c[i];
+          before += b + i < bl ? c[i] : 0;
+        }
+      }
+    }
+    qsum[0][q][e] = before;
+    qsum[1][q][e] = part;
+    __syncthreads();
+    if (q == 0) {
+      int32_t base = 0, total = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        base += qsum[0][i][e];
+        total += qsum[1][i][e];
+      }
+      const int32_t kept = (e < E) ? ((C >= 0 && int64_t(total) > C) ? int32_t(C) : total) : 0;
+      sbase[e] = base;
+      sk[e] = kept;
+      sd[e] = (e < E) ? total - kept : 0;
+      if (blockIdx.x == 0 && e < E && counts) counts[e] = total;
+      soff[e] = kept;
+    }
+    __syncthreads();
+    // Hillis-Steele inclusive scan of kept counts and drop counts
+    for (int st = 1; st < 256; st <<= 1) {
+      const int32_t vk = (q == 0 && e >= st) ? sk[e - st] : 0;
+      const int32_t vd = (q == 0 && e >= st) ? sd[e - st] : 0;
+      __syncthreads();
+      if (q == 0) {
+        sk[e] += vk;
+        sd[e] += vd;
+      }
+      __syncthreads();
+    }
+    if (q == 0) {
+      soff[e] = sk[e] - soff[e];   // exclusive: the rows of the experts before e
+      if (blockIdx.x == 0 && e < E) offsets[e] = soff[e];
+    }
+    if (blockIdx.x == 0) {
+      if (tid == 0) {
+        offsets[E] = sk[255];
+        if (n_dropped) n_dropped[0] = sd[255];
+      }
+    }
+  }
   const int v = blockIdx.x * NT + tid;
   const bool valid = int64_t(v) < int64_t(T) * k;
   const int t = !valid ? 0 : (ORDER == DISP_SLOT ? v % T : v / k);      // token of this slot
@@ -154,10 +148,10 @@ __global__ __launch_bounds__(NT) void dispatch_rank_kernel(
   __syncthreads();
   int row = -1;
   if (ex >= 0) {
-    int32_t rank = blockbase[int64_t(blockIdx.x) * E + ex] + rk;
+    int32_t rank = sbase[ex] + rk;
     for (int ww = 0; ww < w; ++ww) rank += wavecnt[ww][ex];
     if (C < 0 || rank < C) {
-      row = offsets[ex] + rank;
+      row = soff[ex] + rank;
       token_of_row[row] = t;
     }
   }
@@ -208,8 +202,8 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const int32_t* __rest
 
 int dispatch_order(bool slot_major) { return slot_major ? DISP_SLOT : DISP_FLAT; }
 
-// Slots per dispatch block (16 waves; fewer blocks keep the single-workgroup
-// scan over the blocks short).
+// Slots per dispatch block (16 waves; fewer blocks keep each block's scan over
+// the per-block counts short).
 constexpr int DISP_NT = 1024;
 
 int dispatch_blocks(int T, int k, bool) { return int(cdiv(int64_t(T) * k, DISP_NT)); }
@@ -222,19 +216,11 @@ hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, bool sl
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_scan(const int32_t* blockcnt, int nblk, int E, int64_t C,
-                                int32_t* blockbase, int32_t* counts, int32_t* offsets,
-                                int32_t* n_dropped, hipStream_t st) {
-  dispatch_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(blockcnt, nblk, E, C, blockbase, counts,
-                                                       offsets, n_dropped);
-  return hipGetLastError();
-}
-
 hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int64_t C,
-                                   bool slot_major, const int32_t* blockbase,
-                                   const int32_t* offsets, const void* x, int d, int elem_bytes,
-                                   int32_t* row_of_slot, int32_t* token_of_row, void* x_perm,
-                                   hipStream_t st) {
+                                   bool slot_major, const int32_t* blockcnt, int32_t* counts,
+                                   int32_t* offsets, int32_t* n_dropped, const void* x, int d,
+                                   int elem_bytes, int32_t* row_of_slot, int32_t* token_of_row,
+                                   void* x_perm, hipStream_t st) {
   const unsigned nblk = unsigned(dispatch_blocks(T, k, slot_major));
   const unsigned ncopy = unsigned(cdiv(T, 4));
   const int row_bytes = d * elem_bytes;
@@ -242,10 +228,12 @@ hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int6
   auto* xp = static_cast<uint8_t*>(x_perm);
   if (slot_major)
     dispatch_rank_kernel<DISP_SLOT, DISP_NT><<<dim3(nblk), dim3(DISP_NT), 0, st>>>(
-        idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);
+        idx, T, k, E, C, int(nblk), blockcnt, counts, offsets, n_dropped, row_of_slot,
+        token_of_row);
   else
     dispatch_rank_kernel<DISP_FLAT, DISP_NT><<<dim3(nblk), dim3(DISP_NT), 0, st>>>(
-        idx, T, k, E, C, blockbase, offsets, row_of_slot, token_of_row);
+        idx, T, k, E, C, int(nblk), blockcnt, counts, offsets, n_dropped, row_of_slot,
+        token_of_row);
   if (k <= 1) permute_copy_kernel<1><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
   else if (k <= 2) permute_copy_kernel<2><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);
   else if (k <= 4) permute_copy_kernel<4><<<dim3(ncopy), dim3(256), 0, st>>>(row_of_slot, T, k, xs, row_bytes, xp);

@@ -59,14 +59,11 @@ int dispatch_order(bool slot_major);
 int dispatch_blocks(int T, int k, bool slot_major);
 hipError_t launch_dispatch_hist(const int32_t* idx, int T, int k, int E, bool slot_major,
                                 int32_t* blockcnt, hipStream_t st);
-hipError_t launch_dispatch_scan(const int32_t* blockcnt, int nblk, int E, int64_t C,
-                                int32_t* blockbase, int32_t* counts, int32_t* offsets,
-                                int32_t* n_dropped, hipStream_t st);
 hipError_t launch_dispatch_permute(const int32_t* idx, int T, int k, int E, int64_t C,
-                                   bool slot_major, const int32_t* blockbase,
-                                   const int32_t* offsets, const void* x, int d, int elem_bytes,
-                                   int32_t* row_of_slot, int32_t* token_of_row, void* x_perm,
-                                   hipStream_t st);
+                                   bool slot_major, const int32_t* blockcnt, int32_t* counts,
+                                   int32_t* offsets, int32_t* n_dropped, const void* x, int d,
+                                   int elem_bytes, int32_t* row_of_slot, int32_t* token_of_row,
+                                   void* x_perm, hipStream_t st);
 
 // ------------------------------------------------------------------ grouped GEMM
 // Epilogues: fp32 store; forward activations (GELU, SwiGLU of two panels);

@@ -2,15 +2,14 @@
 // allocate device memory or pass a workspace (code under HIP graph capture,
 // tight serving loops, harnesses that forbid allocation).
 //
-// The dispatch kernels' only scratch is two per-block tables, the expert
-// histogram of each block of 1024 slots and each block's exclusive base per
-// expert (ceil(T*k/1024) * E int32 each).  Here they live in one file-scope
-// device array of NOALLOC_SCRATCH_BYTES bytes.  Every GPU holds its own copy at
-// its own address; the address is fetched once per device with
-// hipGetSymbolAddress and only that address is handed to kernels.  Both tables
-// are written in full before they are read, so nothing needs clearing between
-// calls.  Calls that overlap on one GPU (on different streams) share the array
-// and race.
+// The dispatch kernels' only scratch is one per-block table, the expert
+// histogram of each block of 1024 slots (ceil(T*k/1024) * E int32).  Here it
+// lives in one file-scope device array of NOALLOC_SCRATCH_BYTES bytes.  Every
+// GPU holds its own copy at its own address; the address is fetched once per
+// device with hipGetSymbolAddress and only that address is handed to kernels.
+// The table is written in full before it is read, so nothing needs clearing
+// between calls.  Calls that overlap on one GPU (on different streams) share
+// the array and race.
 #include <mutex>
 
 #include "../../include/moe.h"
@@ -65,7 +64,7 @@ extern "C" int moe_permute_noalloc(const moe_dims* d, const moe_opts* o, const v
   const int T = int(d->T), k = int(d->k), E = int(d->E);
   const int nblk = dispatch_blocks(T, k, slot_major);
   const size_t table = round256(size_t(nblk) * size_t(E) * 4);
-  if (2 * table > NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  if (table > NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
   int64_t C = -1;
   if ((s = moe_capacity(d, o, &C))) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -73,13 +72,10 @@ extern "C" int moe_permute_noalloc(const moe_dims* d, const moe_opts* o, const v
   void* base = nullptr;
   if (scratch_address(&base) != hipSuccess) return MOE_ERR_HIP;
   int32_t* blockcnt = static_cast<int32_t*>(base);
-  int32_t* blockbase = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(base) + table);
   if (launch_dispatch_hist(topk_idx, T, k, E, slot_major, blockcnt, st) != hipSuccess ||
-      launch_dispatch_scan(blockcnt, nblk, E, C, blockbase, counts, offsets, nullptr, st) !=
-          hipSuccess ||
-      launch_dispatch_permute(topk_idx, T, k, E, C, slot_major, blockbase, offsets, x,
-                              int(d->d), o->dtype == MOE_DTYPE_BF16 ? 2 : 4, row_of_slot,
-                              token_of_row, x_perm, st) != hipSuccess)
+      launch_dispatch_permute(topk_idx, T, k, E, C, slot_major, blockcnt, counts, offsets,
+                              nullptr, x, int(d->d), o->dtype == MOE_DTYPE_BF16 ? 2 : 4,
+                              row_of_slot, token_of_row, x_perm, st) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
