@@ -69,10 +69,11 @@ int64_t capacity_of(const moe_dims* d, const moe_opts* o) {
   return int64_t(ceil(cf * double(d->T) * double(d->k) / double(d->E)));
 }
 
-// d-split of the MFMA router (8 waves over EP/32 output blocks).
-int route_ks(int EP) { return 256 / EP; }
-bool route_mfma(const moe_dims* d, const moe_opts* o, int EP) {
-  return o->dtype == MOE_DTYPE_BF16 && d->d % (64 * route_ks(EP)) == 0;
+// bf16 tokens: the wide router kernel (64 tokens per block, logits on chip,
+// one fp32 accumulation over the three planes of Wg).  Its 8 waves split d
+// into 256 / EP ranges of whole 64-k chunks.
+bool route_wide(const moe_dims* d, const moe_opts* o, int EP) {
+  return o->dtype == MOE_DTYPE_BF16 && d->d % (64 * (256 / EP)) == 0;
 }
 
 // The variant routers' inputs that opts->routing needs must be present.
@@ -90,14 +91,9 @@ int check_router_inputs(const moe_opts* o, const moe_router_inputs* ri) {
 }
 
 // ---- workspace plans -------------------------------------------------------
-// bf16 tokens with 64 or more (padded) experts: the wide kernel (64 tokens per
-// block, logits on chip, one fp32 accumulation over the three planes).
-bool route_wide(const moe_dims* d, const moe_opts* o, int EP) {
-  return route_mfma(d, o, EP) && EP >= 64;
-}
 
 struct RouteWs {
-  size_t wsplit, part_p, part_cnt, part_lse2, part_nf, zn;
+  size_t wfrag, part_p, part_cnt, part_lse2, part_nf, zn;
   int nblk, EP;
   bool wide;
 };
@@ -106,7 +102,7 @@ RouteWs plan_route(Carver& c, const moe_dims* d, const moe_opts* o) {
   r.EP = route_pad_experts(int(d->E));
   r.wide = route_wide(d, o, r.EP);
   r.nblk = int(cdiv(d->T, r.wide ? ROUTE_WIDE_BT : ROUTE_BT));
-  r.wsplit = c.take(size_t(3 * r.EP) * d->d * 2);
+  r.wfrag = c.take(r.wide ? size_t(r.EP) * d->d * 4 : 0);
   r.part_p = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_cnt = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_lse2 = c.take(size_t(r.nblk) * 4);
@@ -208,8 +204,7 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
   a.x = x;
   a.x_bf16 = o->dtype == MOE_DTYPE_BF16;
   a.Wg = Wg;
-  a.wsplit = at<uint16_t>(ws, rw.wsplit);
-  a.wfrag = at<float>(ws, rw.wsplit);
+  a.wfrag = at<float>(ws, rw.wfrag);
   a.offset = offset;
   a.bias = bias;
   a.T = int(d->T);
@@ -229,19 +224,14 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
   a.part_cnt = at<int32_t>(ws, rw.part_cnt);
   a.part_lse2 = at<float>(ws, rw.part_lse2);
   a.part_nf = at<int32_t>(ws, rw.part_nf);
-  const bool mfma = route_mfma(d, o, rw.EP);
-  uint16_t* planes = at<uint16_t>(ws, rw.wsplit);
-  // the Wg planes in the layout the logits kernel reads, then the logits
+  float* wfrag = at<float>(ws, rw.wfrag);
+  // Wg in the layout the logits kernel reads, then the logits
   auto logits_pass = [&](const float* W, const RouteArgs& ra) -> hipError_t {
     if (rw.wide) {
-      hipError_t e = launch_wg_frag(W, ra.d, ra.E, ra.EP, reinterpret_cast<float*>(planes), st);
+      hipError_t e = launch_wg_frag(W, ra.d, ra.E, ra.EP, wfrag, st);
       return e != hipSuccess ? e : launch_route_wide(ra, st);
     }
-    if (mfma) {
-      hipError_t e = launch_wg_split(W, ra.d, ra.E, ra.EP, planes, st);
-      if (e != hipSuccess) return e;
-    }
-    return launch_route(ra, mfma, st);
+    return launch_route(ra, st);
   };
   if (o->routing == MOE_ROUTING_NOISY_TOPK) {
     // first pass: zn = x . W_noise (raw logits of the noise projection)

@@ -11,7 +11,6 @@ struct RouteArgs {
   const void* x;            // [T, d] bf16 or fp32
   int x_bf16;
   const float* Wg;          // [d, E]
-  const uint16_t* wsplit;   // [3][EP][d] bf16 planes of Wg (32-expert MFMA kernel)
   const float* wfrag;       // Wg in the wide kernel's fp32 fragment layout
   const float* offset;      // nullable [E]
   const float* bias;        // nullable [E]
@@ -36,13 +35,11 @@ struct RouteArgs {
 constexpr int ROUTE_BT = 32;   // tokens per route block
 
 int route_pad_experts(int E);  // 32, 64, 128 or 256
-// Wg [d, E] -> three bf16 planes [3][EP][d] (32-expert kernel), or Wg in the
-// wide kernel's fp32 fragment layout (d % 64 == 0, EP % 32 == 0).
-hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, uint16_t* out, hipStream_t st);
+// Wg in the wide kernel's fp32 fragment layout (d % 64 == 0, EP % 32 == 0).
 hipError_t launch_wg_frag(const float* Wg, int d, int E, int EP, float* out, hipStream_t st);
-hipError_t launch_route(const RouteArgs& a, bool mfma, hipStream_t st);
-// bf16 tokens, EP >= 64: 64 tokens per block (partial-sum rows per 64 tokens),
-// logits kept on chip, Wg planes in the fragment layout; d % (64 * 256 / EP) == 0.
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);   // fp32 FMA logits
+// bf16 tokens: 64 tokens per block (partial-sum rows per 64 tokens), logits
+// kept on chip, Wg in the fragment layout; d % (64 * 256 / EP) == 0.
 constexpr int ROUTE_WIDE_BT = 64;
 hipError_t launch_route_wide(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, float z_coef,

@@ -21,31 +21,6 @@ namespace moe {
 int route_pad_experts(int E) { return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256; }
 
 // ---------------------------------------------------------------------------
-// Wg [d, E] fp32 -> three bf16 planes.  hi = rne(w), mid = rne(w - hi),
-// lo = rne(w - hi - mid); each residual is exact in fp32 and the last has at
-// most 8 significant bits, so hi + mid + lo == w for every normal w.  Experts
-// e >= E are zero.
-__device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
-  hi = f2bf(w);
-  const float r1 = w - bf2f(hi);
-  mid = f2bf(r1);
-  lo = f2bf(r1 - bf2f(mid));
-}
-
-// Row layout [3][EP][d] (expert-major, K-contiguous), for the 32-expert kernel.
-__global__ void wg_split_kernel(const float* __restrict__ Wg, int d, int E, int EP,
-                                uint16_t* __restrict__ out) {
-  const int64_t n = int64_t(EP) * d;
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int e = int(i / d), kk = int(i % d);
-  uint16_t hi, mid, lo;
-  split3(e < E ? Wg[int64_t(kk) * E + e] : 0.0f, hi, mid, lo);
-  out[i] = hi;
-  out[n + i] = mid;
-  out[2 * n + i] = lo;
-}
-
 // Fragment layout for the wide kernel (fp32, split into planes on chip): the
 // 16-byte pieces out[((eb * (d / 64) + c) * 8 + i) * 64 + l] hold Wg of expert
 // e = 32 eb + l % 32 at k = 64 c + 32 (l / 32) + 8 (i / 2) + 4 (i % 2) .. + 3,
@@ -311,85 +286,7 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[B
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tokens: logits on MFMA 32x32x16.  A block of 8 waves covers 32 tokens
-// and all EP experts: wave w computes output block (w % NB) (32 experts) over
-// the d-range (w / NB) of KS = 8 / NB parts, summed in order afterwards.
-// Within a 64-wide K chunk a lane loads 32 contiguous k of its token row and
-// of its expert row in each Wg plane; MFMA step s uses elements 8s..8s+7 of
-// them, the same permutation of k for both operands.  All loads of a chunk
-// are issued together and the next chunk is prefetched during the MFMAs.
-template <int EP>
-__global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
-  constexpr int NW = 8;
-  constexpr int NB = EP / 32;
-  constexpr int KS = NW / NB;
-  __shared__ float zs[KS][ROUTE_BT][EP + 1];
-  __shared__ float red_p[NW * EP];
-  __shared__ int32_t red_c[EP];
-  __shared__ float red_s[2 * NW];
-  __shared__ float ob[2 * EP];
-
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int t0 = blockIdx.x * ROUTE_BT;
-  const int eb = w % NB, kp = w / NB;
-  const int dpart = a.d / KS;
-  const int row = l & 31, g = l >> 5;
-  const int trow = min(t0 + row, a.T - 1);
-  const uint16_t* xr = static_cast<const uint16_t*>(a.x) + int64_t(trow) * a.d + kp * dpart + 32 * g;
-  const int64_t plane = int64_t(EP) * a.d;
-  const uint16_t* wr = a.wsplit + int64_t(eb * 32 + row) * a.d + kp * dpart + 32 * g;
-
-  floatx16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-
-  // Rows of padding experts (eb*32 + row >= E) are zero in every plane: their
-  // lanes load nothing and multiply zeros.
-  const bool wlive = eb * 32 + row < a.E;
-  uint4 xa[4], wv[3][4], xb[4], wb[3][4];
-  auto load = [&](int kc, uint4 (&xo)[4], uint4 (&wo)[3][4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xo[q] = ld16(xr + kc + 8 * q);
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        wo[p][q] = wlive ? ld16(wr + p * plane + kc + 8 * q) : make_uint4(0, 0, 0, 0);
-  };
-  // Two chunks in flight: chunk c+2 is loaded while chunk c multiplies.
-  load(0, xa, wv);
-  if (64 < dpart) load(64, xb, wb);
-  for (int kc = 0; kc < dpart; kc += 64) {
-    uint4 xc[4], wc[3][4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      xc[q] = xa[q];
-      xa[q] = xb[q];
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        wc[p][q] = wv[p][q];
-        wv[p][q] = wb[p][q];
-      }
-    }
-    if (kc + 128 < dpart) load(kc + 128, xb, wb);
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xc[s]),
-                                                      __builtin_bit_cast(bf16x8, wc[p][s]), acc,
-                                                      0, 0, 0);
-  }
-  // D[i][j] of a 32x32 block: lane l holds column j = l%32 and rows
-  // i = 8*(r/4) + 4*(l/32) + r%4 in accumulator register r.
-#pragma unroll
-  for (int r = 0; r < 16; ++r) zs[kp][8 * (r >> 2) + 4 * g + (r & 3)][eb * 32 + row] = acc[r];
-  __syncthreads();
-  route_epilogue<EP, KS, NW>(a, zs, t0, red_p, red_c, red_s, ob);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 tokens, 64 or more (padded) experts: a block of 8 waves covers
+// bf16 tokens: a block of 8 waves covers
 // ROUTE_WIDE_BT = 64 tokens and all EP experts, and the logits never leave the
 // chip.  The waves split the work into NB = EP / 32 expert blocks times
 // KS = 8 / NB d-ranges: wave w computes expert block eb = w % NB over d-range
@@ -420,8 +317,9 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
   constexpr int XL = KS;                           // token-row loads per wave and chunk
   constexpr int XSLOT = KS * ROUTE_WIDE_BT * 64;   // bf16 elements of one chunk's token rows
   // register sets of plane pieces in rotation (and LDS slots of token rows):
-  // three (loads two chunks ahead), two with four d-ranges (register budget)
-  constexpr int P = KS == 4 ? 2 : 3;
+  // three (loads two chunks ahead), two with four or eight d-ranges (register
+  // and LDS budget)
+  constexpr int P = KS >= 4 ? 2 : 3;
   constexpr int D = P - 1;                         // chunks ahead
   constexpr int RING = P * XSLOT * 2;
   constexpr int ZSB = KS * ROUTE_WIDE_BT * (EP + 1) * 4;
@@ -480,10 +378,12 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
 #pragma unroll
     for (int q = 0; q < XL; ++q) slot[q * ROUTE_WIDE_BT * 8 + xdst] = xn[q];
   };
+  // lanes of padding experts (zero weights) load nothing
+  const bool wlive = 32 * eb + (l & 31) < a.E;
   auto load_w = [&](int j, uint4 (&wr)[8]) {
     const uint4* src = wf + int64_t(chunk(j)) * 8 * 64;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wr[i] = src[64 * i];
+    for (int i = 0; i < 8; ++i) wr[i] = wlive ? src[64 * i] : make_uint4(0u, 0u, 0u, 0u);
   };
   // the three bf16 planes of eight fp32 weights (pieces u0, u1)
   auto split8 = [](const uint4& u0, const uint4& u1, bf16x8& ph, bf16x8& pm, bf16x8& pl) {
@@ -573,7 +473,7 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Plain FMA logits (fp32 tokens, or shapes the MFMA tiling does not cover).
+// Plain FMA logits (fp32 tokens, or d not a multiple of the wide kernel's d-ranges).
 template <int EP>
 __global__ __launch_bounds__(256) void route_simt_kernel(RouteArgs a) {
   constexpr int NW = 4;
@@ -704,13 +604,6 @@ __global__ __launch_bounds__(1024) void route_reduce_kernel(RouteArgs a, int nbl
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_wg_split(const float* Wg, int d, int E, int EP, uint16_t* out,
-                           hipStream_t st) {
-  const int64_t n = int64_t(EP) * d;
-  wg_split_kernel<<<dim3(unsigned(cdiv(n, 256))), dim3(256), 0, st>>>(Wg, d, E, EP, out);
-  return hipGetLastError();
-}
-
 hipError_t launch_wg_frag(const float* Wg, int d, int E, int EP, float* out, hipStream_t st) {
   if (d % 64 || EP % 32) return hipErrorInvalidValue;
   wg_frag_kernel<<<dim3(unsigned(d / 64), unsigned(EP / 32)), dim3(256), 0, st>>>(
@@ -718,22 +611,10 @@ hipError_t launch_wg_frag(const float* Wg, int d, int E, int EP, float* out, hip
   return hipGetLastError();
 }
 
-template <int EP>
-static hipError_t launch_route_ep(const RouteArgs& a, bool mfma, hipStream_t st) {
-  const unsigned nblk = unsigned(cdiv(a.T, ROUTE_BT));
-  if (mfma) {
-    // 64 or more padded experts take the wide kernel
-    if constexpr (EP == 32) route_mfma_kernel<EP><<<dim3(nblk), dim3(512), 0, st>>>(a);
-    else return hipErrorInvalidValue;
-  } else {
-    route_simt_kernel<EP><<<dim3(nblk), dim3(256), 0, st>>>(a);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_route_wide(const RouteArgs& a, hipStream_t st) {
   const unsigned nblk = unsigned(cdiv(a.T, ROUTE_WIDE_BT));
   switch (a.EP) {
+    case 32: route_wide_kernel<32><<<nblk, 512, 0, st>>>(a); break;
     case 64: route_wide_kernel<64><<<nblk, 512, 0, st>>>(a); break;
     case 128: route_wide_kernel<128><<<nblk, 512, 0, st>>>(a); break;
     case 256: route_wide_kernel<256><<<nblk, 512, 0, st>>>(a); break;
@@ -742,14 +623,16 @@ hipError_t launch_route_wide(const RouteArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_route(const RouteArgs& a, bool mfma, hipStream_t st) {
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+  const unsigned nblk = unsigned(cdiv(a.T, ROUTE_BT));
   switch (a.EP) {
-    case 32: return launch_route_ep<32>(a, mfma, st);
-    case 64: return launch_route_ep<64>(a, mfma, st);
-    case 128: return launch_route_ep<128>(a, mfma, st);
-    case 256: return launch_route_ep<256>(a, mfma, st);
+    case 32: route_simt_kernel<32><<<dim3(nblk), dim3(256), 0, st>>>(a); break;
+    case 64: route_simt_kernel<64><<<dim3(nblk), dim3(256), 0, st>>>(a); break;
+    case 128: route_simt_kernel<128><<<dim3(nblk), dim3(256), 0, st>>>(a); break;
+    case 256: route_simt_kernel<256><<<dim3(nblk), dim3(256), 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, float z_coef,
