@@ -101,7 +101,7 @@ RouteWs plan_route(Carver& c, const moe_dims* d, const moe_opts* o) {
   RouteWs r;
   r.EP = route_pad_experts(int(d->E));
   r.wide = route_wide(d, o, r.EP);
-  r.nblk = int(cdiv(d->T, r.wide ? ROUTE_WIDE_BT : ROUTE_BT));
+  r.nblk = int(cdiv(d->T, r.wide ? route_wide_bt(d->T, r.EP) : ROUTE_BT));
   r.wfrag = c.take(r.wide ? size_t(r.EP) * d->d * 4 : 0);
   r.part_p = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_cnt = c.take(size_t(r.nblk) * r.EP * 4);

@@ -38,9 +38,10 @@ int route_pad_experts(int E);  // 32, 64, 128 or 256
 // Wg in the wide kernel's fp32 fragment layout (d % 64 == 0, EP % 32 == 0).
 hipError_t launch_wg_frag(const float* Wg, int d, int E, int EP, float* out, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);   // fp32 FMA logits
-// bf16 tokens: 64 tokens per block (partial-sum rows per 64 tokens), logits
-// kept on chip, Wg in the fragment layout; d % (64 * 256 / EP) == 0.
-constexpr int ROUTE_WIDE_BT = 64;
+// bf16 tokens: route_wide_bt(T, EP) tokens per block (64, or 32 for small
+// batches; one partial-sum row per block), logits kept on chip, Wg in the
+// fragment layout; d % (64 * 256 / EP) == 0.
+int route_wide_bt(int64_t T, int EP);
 hipError_t launch_route_wide(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_reduce(const RouteArgs& a, int nblk, float aux_coef, float z_coef,
                                int32_t* counts, float* losses, int32_t* n_nonfinite,

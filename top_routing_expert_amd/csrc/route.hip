@@ -286,9 +286,9 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[B
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tokens: a block of 8 waves covers
-// ROUTE_WIDE_BT = 64 tokens and all EP experts, and the logits never leave the
-// chip.  The waves split the work into NB = EP / 32 expert blocks times
+// bf16 tokens: a block of 8 waves covers 64 tokens (two 32-token halves,
+// H = 2; 32 tokens, H = 1, for small batches) and all EP experts, and the
+// logits never leave the chip.  The waves split the work into NB = EP / 32 expert blocks times
 // KS = 8 / NB d-ranges: wave w computes expert block eb = w % NB over d-range
 // kp = w / NB for both 32-token halves, so each plane piece of Wg is loaded
 // once per block, by one wave, straight into registers from the fragment
@@ -309,20 +309,22 @@ __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[B
 // different parts of Wg, spreading their requests over the L2 channels (the
 // sum order depends only on the block).  The LDS slots hold the logits after
 // the loop.
-template <int EP>
+template <int EP, int H>
 __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
   constexpr int NW = 8;
   constexpr int NB = EP / 32;
   constexpr int KS = NW / NB;
-  constexpr int XL = KS;                           // token-row loads per wave and chunk
-  constexpr int XSLOT = KS * ROUTE_WIDE_BT * 64;   // bf16 elements of one chunk's token rows
+  constexpr int BT = 32 * H;                       // tokens per block (H 32-token halves)
+  constexpr int XL = KS * H / 2;                   // token-row loads per wave and chunk
+  static_assert(KS * H % 2 == 0, "whole 1 KB row groups per wave");
+  constexpr int XSLOT = KS * BT * 64;              // bf16 elements of one chunk's token rows
   // register sets of plane pieces in rotation (and LDS slots of token rows):
   // three (loads two chunks ahead), two with four or eight d-ranges (register
   // and LDS budget)
   constexpr int P = KS >= 4 ? 2 : 3;
   constexpr int D = P - 1;                         // chunks ahead
   constexpr int RING = P * XSLOT * 2;
-  constexpr int ZSB = KS * ROUTE_WIDE_BT * (EP + 1) * 4;
+  constexpr int ZSB = KS * BT * (EP + 1) * 4;
   __shared__ __attribute__((aligned(16))) char smem[RING > ZSB ? RING : ZSB];
   __shared__ float red_p[NW * EP];
   __shared__ int32_t red_c[EP];
@@ -331,27 +333,31 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
   uint4* const xs = reinterpret_cast<uint4*>(smem);
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int t0 = blockIdx.x * ROUTE_WIDE_BT;
+  const int t0 = blockIdx.x * BT;
   const int eb = w % NB, kp = w / NB;
   const int dpart = a.d / KS;
   const int C = a.d / 64, CK = C / KS;   // 64-k chunks in all, per d-range
   const int rot = blockIdx.x % CK;
   const int fr = l & 31, fg = l >> 5;
 
-  // Token rows: load q of a wave covers rows 8w + l/8 of d-range q; lane l
-  // holds physical piece l%8 of its row, i.e. logical piece
-  // (l%8) ^ ((row >> 1) & 7).  Rows past T repeat row T-1 (their tokens are
-  // never stored).
-  const int xrow = 8 * w + (l >> 3);
-  const uint16_t* xsrc = static_cast<const uint16_t*>(a.x) +
-                         int64_t(min(t0 + xrow, a.T - 1)) * a.d +
-                         8 * ((l & 7) ^ ((xrow >> 1) & 7));
-  const int xdst = xrow * 8 + (l & 7);
+  // Token rows: load i of wave w is 1 KB row group n = w + 8i, i.e. rows
+  // 8 (n % 4H) + l/8 of d-range n / 4H; lane l holds physical piece l%8 of
+  // its row, i.e. logical piece (l%8) ^ ((row >> 1) & 7).  Rows past T repeat
+  // row T-1 (their tokens are never stored).
+  const uint16_t* xsrc[XL];
+  int xdst[XL];
+#pragma unroll
+  for (int i = 0; i < XL; ++i) {
+    const int n = w + 8 * i, q = n / (4 * H), row = 8 * (n % (4 * H)) + (l >> 3);
+    xsrc[i] = static_cast<const uint16_t*>(a.x) + int64_t(min(t0 + row, a.T - 1)) * a.d +
+              q * dpart + 8 * ((l & 7) ^ ((row >> 1) & 7));
+    xdst[i] = (q * BT + row) * 8 + (l & 7);
+  }
   const uint4* wf = reinterpret_cast<const uint4*>(a.wfrag) +
                     (int64_t(eb) * C + int64_t(kp) * CK) * 8 * 64 + l;
-  // fragment pieces of this lane (uint4 units): rows fr and 32 + fr, logical
-  // piece 4 fg + s
-  const int xo0 = (kp * ROUTE_WIDE_BT + fr) * 8;
+  // fragment pieces of this lane (uint4 units): rows fr (and 32 + fr),
+  // logical piece 4 fg + s
+  const int xo0 = (kp * BT + fr) * 8;
   const int xo1 = xo0 + 32 * 8;
   const int xsw = (fr >> 1) & 7;   // same for rows fr and 32 + fr
 
@@ -372,11 +378,11 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
   auto load_x = [&](int j) {
     const int c = chunk(j);
 #pragma unroll
-    for (int q = 0; q < XL; ++q) xn[q] = ld16(xsrc + q * dpart + 64 * c);
+    for (int i = 0; i < XL; ++i) xn[i] = ld16(xsrc[i] + 64 * c);
   };
   auto store_x = [&](uint4* slot) {
 #pragma unroll
-    for (int q = 0; q < XL; ++q) slot[q * ROUTE_WIDE_BT * 8 + xdst] = xn[q];
+    for (int i = 0; i < XL; ++i) slot[xdst[i]] = xn[i];
   };
   // lanes of padding experts (zero weights) load nothing
   const bool wlive = 32 * eb + (l & 31) < a.E;
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       xa[s] = rslot[xo0 + ((4 * fg + s) ^ xsw)];
-      xb[s] = rslot[xo1 + ((4 * fg + s) ^ xsw)];
+      if constexpr (H == 2) xb[s] = rslot[xo1 + ((4 * fg + s) ^ xsw)];
     }
     if (FULL || j + 1 < CK) {
       store_x(xslot);
@@ -431,8 +437,9 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
       for (int p = 0; p < 3; ++p) {
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[s]), b[p],
                                                        acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xb[s]), b[p],
-                                                       acc1, 0, 0, 0);
+        if constexpr (H == 2)
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xb[s]), b[p],
+                                                         acc1, 0, 0, 0);
       }
     }
   };
@@ -459,17 +466,17 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
       step(tail, j + u, xs + (u % P) * (XSLOT / 8), r[u % P], xs + ((u + 1) % P) * (XSLOT / 8),
            r[(u + D) % P]);
   __syncthreads();   // every wave has read its last token rows; the slots become zs
-  auto zs = reinterpret_cast<float (*)[ROUTE_WIDE_BT][EP + 1]>(smem);
+  auto zs = reinterpret_cast<float (*)[BT][EP + 1]>(smem);
   // D[i][j] of a 32x32 block: lane l holds column j = l%32 and rows
   // i = 8*(r/4) + 4*(l/32) + r%4 in accumulator register r.
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int i = 8 * (r >> 2) + 4 * fg + (r & 3);
     zs[kp][i][eb * 32 + fr] = acc0[r];
-    zs[kp][ROUTE_BT + i][eb * 32 + fr] = acc1[r];
+    if constexpr (H == 2) zs[kp][32 + i][eb * 32 + fr] = acc1[r];
   }
   __syncthreads();
-  route_epilogue<EP, KS, NW, ROUTE_WIDE_BT>(a, zs, t0, red_p, red_c, red_s, ob);
+  route_epilogue<EP, KS, NW, BT>(a, zs, t0, red_p, red_c, red_s, ob);
 }
 
 // ---------------------------------------------------------------------------
@@ -611,13 +618,28 @@ hipError_t launch_wg_frag(const float* Wg, int d, int E, int EP, float* out, hip
   return hipGetLastError();
 }
 
+// Tokens per wide-kernel block: 64, or 32 when 64-token blocks would leave
+// compute units idle (fewer than 256 of them) and the experts' d-ranges allow
+// it (not with 256 padded experts: one d-range needs whole 64-row groups).
+int route_wide_bt(int64_t T, int EP) { return EP < 256 && cdiv(T, 64) < 256 ? 32 : 64; }
+
 hipError_t launch_route_wide(const RouteArgs& a, hipStream_t st) {
-  const unsigned nblk = unsigned(cdiv(a.T, ROUTE_WIDE_BT));
+  const bool small = route_wide_bt(a.T, a.EP) == 32;
+  const unsigned nblk = unsigned(cdiv(a.T, small ? 32 : 64));
   switch (a.EP) {
-    case 32: route_wide_kernel<32><<<nblk, 512, 0, st>>>(a); break;
-    case 64: route_wide_kernel<64><<<nblk, 512, 0, st>>>(a); break;
-    case 128: route_wide_kernel<128><<<nblk, 512, 0, st>>>(a); break;
-    case 256: route_wide_kernel<256><<<nblk, 512, 0, st>>>(a); break;
+    case 32:
+      if (small) route_wide_kernel<32, 1><<<nblk, 512, 0, st>>>(a);
+      else route_wide_kernel<32, 2><<<nblk, 512, 0, st>>>(a);
+      break;
+    case 64:
+      if (small) route_wide_kernel<64, 1><<<nblk, 512, 0, st>>>(a);
+      else route_wide_kernel<64, 2><<<nblk, 512, 0, st>>>(a);
+      break;
+    case 128:
+      if (small) route_wide_kernel<128, 1><<<nblk, 512, 0, st>>>(a);
+      else route_wide_kernel<128, 2><<<nblk, 512, 0, st>>>(a);
+      break;
+    case 256: route_wide_kernel<256, 2><<<nblk, 512, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
