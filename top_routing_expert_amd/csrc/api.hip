@@ -91,6 +91,8 @@ int check_router_inputs(const moe_opts* o, const moe_router_inputs* ri) {
 }
 
 // ---- workspace plans -------------------------------------------------------
+// 17 to 32 experts: the wide kernel reads Wg [d, E] as stored (no layout pass).
+bool route_wg_direct(int E) { return E > 16 && E <= 32; }
 
 struct RouteWs {
   size_t wfrag, part_p, part_cnt, part_lse2, part_nf, zn;
@@ -102,7 +104,7 @@ RouteWs plan_route(Carver& c, const moe_dims* d, const moe_opts* o) {
   r.EP = route_pad_experts(int(d->E));
   r.wide = route_wide(d, o, r.EP);
   r.nblk = int(cdiv(d->T, r.wide ? route_wide_bt(d->T, r.EP) : ROUTE_BT));
-  r.wfrag = c.take(r.wide ? size_t(r.EP) * d->d * 4 : 0);
+  r.wfrag = c.take(r.wide && !route_wg_direct(int(d->E)) ? size_t(r.EP) * d->d * 4 : 0);
   r.part_p = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_cnt = c.take(size_t(r.nblk) * r.EP * 4);
   r.part_lse2 = c.take(size_t(r.nblk) * 4);
@@ -228,6 +230,11 @@ int do_route(const moe_dims* d, const moe_opts* o, const void* x, const float* W
   // Wg in the layout the logits kernel reads, then the logits
   auto logits_pass = [&](const float* W, const RouteArgs& ra) -> hipError_t {
     if (rw.wide) {
+      if (route_wg_direct(ra.E)) {   // the kernel reads Wg as stored
+        RouteArgs rd = ra;
+        rd.wfrag = nullptr;
+        return launch_route_wide(rd, st);
+      }
       hipError_t e = launch_wg_frag(W, ra.d, ra.E, ra.EP, wfrag, st);
       return e != hipSuccess ? e : launch_route_wide(ra, st);
     }

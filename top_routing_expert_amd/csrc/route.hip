@@ -386,10 +386,28 @@ __global__ __launch_bounds__(512) void route_wide_kernel(RouteArgs a) {
   };
   // lanes of padding experts (zero weights) load nothing
   const bool wlive = 32 * eb + (l & 31) < a.E;
+  // With 17 to 32 experts (no fragment layout given) Wg is small and is read
+  // as stored, [d, E]: lane l takes the 32 k of its expert column that the
+  // fragment layout would hold (the lanes of one k row read adjacent experts,
+  // at least 68 contiguous bytes), so no layout pass runs.  Fewer experts
+  // leave too few live lanes per load instruction for this to pay.
+  const bool wdirect = EP == 32 && a.wfrag == nullptr;
+  const float* wcol = a.Wg + (int64_t(kp) * dpart + 32 * fg) * a.E + 32 * eb + (l & 31);
   auto load_w = [&](int j, uint4 (&wr)[8]) {
-    const uint4* src = wf + int64_t(chunk(j)) * 8 * 64;
+    if (wdirect) {
+      const float* src = wcol + int64_t(64 * chunk(j)) * a.E;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wr[i] = wlive ? src[64 * i] : make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < 8; ++i) {
+        uint32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = wlive ? __float_as_uint(src[(4 * i + u) * a.E]) : 0u;
+        wr[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+      const uint4* src = wf + int64_t(chunk(j)) * 8 * 64;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wr[i] = wlive ? src[64 * i] : make_uint4(0u, 0u, 0u, 0u);
+    }
   };
   // the three bf16 planes of eight fp32 weights (pieces u0, u1)
   auto split8 = [](const uint4& u0, const uint4& u1, bf16x8& ph, bf16x8& pm, bf16x8& pl) {
