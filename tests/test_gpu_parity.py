@@ -93,11 +93,13 @@ def test_route_parity(name):
 
 @pytest.mark.parametrize("name,over", [("c4", dict(T=333)), ("c5", dict(T=1)), ("c5", dict(T=97)),
                                        ("c3", dict(T=33)), ("c4", dict(T=130, E=100, k=6)),
-                                       ("c5", dict(T=70, E=65, k=3)), ("c4", dict(T=64, d=256))])
+                                       ("c5", dict(T=70, E=65, k=3)), ("c4", dict(T=64, d=256)),
+                                       ("c2", dict(T=77, E=20, k=2)), ("c3", dict(T=100, E=5))])
 def test_route_parity_ragged(name, over):
-    """Ragged token counts through the wide kernel (64 or more padded experts,
-    64-token blocks; 64, 128 and 256 padded experts) and the 32-expert kernel
-    (32-token blocks): row tails of the blocks and padding experts."""
+    """Ragged token counts through the wide router kernel: 32-token blocks
+    (small batches) and 64-token blocks, 32, 64, 128 and 256 padded experts,
+    Wg read as stored (17 to 32 experts) or through the fragment pass: row
+    tails of the blocks and padding experts."""
     p, inp, x, w = case(name, **over)
     out = B.route(p, x, w.Wg, w.offset, w.sel_bias)
     torch.cuda.synchronize()
