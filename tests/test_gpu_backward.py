@@ -173,7 +173,7 @@ def _act_bwd_bound(cA, h, F, act):
 @pytest.mark.parametrize("name,over", [
     ("c2", {}), ("c5", {}),
     # ragged token counts through the bf16 router-gradient GEMMs (chunk tails,
-    # one-tile grids) and the logits GEMM (E >= 64)
+    # one-tile grids) and the router's 32- and 64-token blocks
     ("c5", dict(T=300, d=256, F=256, F_shared=256)),
     ("c4", dict(T=333, d=256, F=256, F_shared=0)),
     ("c2", dict(T=257, d=256, F=512)),
