@@ -7,9 +7,9 @@
 // news digest, "confirmed" bullets on sigmoid / sqrt(softplus) scoring).
 //
 // The logits are an [T, d] x [d, E] contraction.  With bf16 tokens it runs on
-// bf16 MFMA: Wg is split once per call into three bf16 planes whose sum is
-// exactly Wg, so every product x*w is formed exactly and accumulated in FP32.
-// fp32 tokens use a plain FMA loop.
+// bf16 MFMA: Wg is split on chip, per MFMA step, into three bf16 planes whose
+// sum is exactly Wg, so every product x*w is formed exactly and accumulated in
+// FP32.  fp32 tokens use a plain FMA loop.
 #include <type_traits>
 
 #include "common.hpp"
@@ -79,7 +79,8 @@ __device__ __forceinline__ float softplus_fast(float z) {
 // a time), each owning VPL experts e = lane_in_group + LG * v; all per-token
 // reductions stay inside the row.  LDS scratch: red_p [NW * EP], red_c [EP]
 // (the block's routed-slot counts, integer LDS atomics: exact in any order),
-// red_s [2 * NW].
+// red_s [2 * NW], ob [2 * EP] (the experts' logit offsets and selection
+// biases, read once per block).
 template <int EP, int KS, int NW, int BT = ROUTE_BT>
 __device__ __forceinline__ void route_epilogue(const RouteArgs& a, float (*zs)[BT][EP + 1],
                                                int t0, float* red_p, int32_t* red_c,
